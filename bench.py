@@ -1,0 +1,221 @@
+"""Benchmark: one step = forward + backward of the latent-attention block on
+one query shard (synthetic seeded inputs, resident in HBM before timing).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line. `value` is the step's algorithmic TFLOP/s: visible
+(query, key) pairs times 2*n_h*(d_qk+d_v) forward and 2*n_h*(3*d_qk+2*d_v)
+backward, plus the latent up-projection of the keys the shard needs (once
+forward, twice backward); masked work and the backward's K/V recomputation
+earn nothing. `roofline` is for the kernel with the largest share of the
+step's time, timed live with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 oracle on a few heads of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA attn-block fwd/bwd TFLOP/s + % bf16 MFMA peak, n_h=128 S=16384 shard"
+PEAK_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(cfg, pairs, kn, backward):
+    d_qk = cfg.d_nope + cfg.d_rope
+    up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
+    if not backward:
+        return 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs + up
+    return 2 * cfg.n_h * (3 * d_qk + 2 * cfg.d_v) * pairs + 2 * up
+
+
+def kernel_flops(name, cfg, pairs, kn):
+    """Algorithmic FLOPs one launch of `name` does (None: not a contraction)."""
+    d_qk = cfg.d_nope + cfg.d_rope
+    up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
+    table = {
+        "upproj": up, "plain_upproj": up,
+        "attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
+        "plain_attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
+        # dK/dV pass: S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+        "attn_bwd_dkdv": 2 * cfg.n_h * (2 * d_qk + 2 * cfg.d_v) * pairs,
+        "plain_attn_bwd_dkdv": 2 * cfg.n_h * (2 * d_qk + 2 * cfg.d_v) * pairs,
+        # dQ pass: S = Q K^T, dP = dO V^T, dQ = dS K
+        "attn_bwd_dq": 2 * cfg.n_h * (2 * d_qk + cfg.d_v) * pairs,
+        "plain_attn_bwd_dq": 2 * cfg.n_h * (2 * d_qk + cfg.d_v) * pairs,
+        # dc_kv = [dK_nope | dV] W^T and dW = c_kv^T [dK_nope | dV]: one up-projection each
+        "grad_latent": up, "plain_grad_latent": up,
+        "grad_w": up, "plain_grad_w": up,
+    }
+    return table.get(name)
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc", rec["source"])
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if sha != rec["sha"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
+    """The fp64 oracle, as it stands, on whole heads of the workload (all rows,
+    forward and backward) until about `budget_s` seconds have been spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    args = [x[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < min(max_heads, cfg.n_h) and time.perf_counter() - t0 < budget_s:
+        h = [heads]
+        oracle.mla_forward(*args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h)
+        oracle.mla_backward(x["dout"], *args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h)
+        heads += 1
+    dt = time.perf_counter() - t0
+    F = (flops(cfg, pairs, kn, False) + flops(cfg, pairs, kn, True)) * heads / cfg.n_h
+    return {"value": round(F / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of heads 0..{heads - 1} of {cfg.n_h} "
+                      f"(all {cfg.S_loc} rows), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h128_s16k_shard")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's query shard: the library has no multi-GPU path "
+              "(the latent all-gather is not part of it); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import head_latent_attention_kv_amd as hla
+    import workloads
+
+    cfg = workloads.config(args.workload)
+    x = workloads.make_inputs(cfg, with_dout=True)
+    cu = cfg.cu_seqlens()
+    dev = {}
+    for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV", "dout"):
+        if cfg.dtype == "bf16":
+            dev[k] = torch.from_numpy(x[k + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            dev[k] = torch.from_numpy(x[k]).cuda()
+    a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True)
+    pairs, k_lo, k_hi = hla.mla_laga_count(call.desc, call.cu)
+    kn = k_hi - k_lo
+    F_fwd, F_bwd = flops(cfg, pairs, kn, False), flops(cfg, pairs, kn, True)
+    out, lse = call.fwd(*a)
+    grads = call.bwd(dev["dout"], *a, out, lse)
+
+    def step():
+        call.fwd(*a, out=out, lse=lse)
+        call.bwd(dev["dout"], *a, out, lse, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    hla.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        call.fwd(*a, out=out, lse=lse)
+        e1.record(stream)
+        call.bwd(dev["dout"], *a, out, lse, grads=grads)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    step_ms = wall * 1e3 / args.steps
+    kern = {}
+    for name in hla.timing_names():
+        tot, n = hla.timing_read(name)
+        kern[name] = {"ms_per_launch": tot / max(n, 1), "launches_per_step": n / args.steps,
+                      "ms_per_step": tot / args.steps}
+    hla.timing_enable(False)
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"]) if kern else None
+    roofline = None
+    if dom:
+        kf = kernel_flops(dom, cfg, pairs, kn)
+        per_launch_s = kern[dom]["ms_per_launch"] / 1e3
+        traffic = recorded_traffic(dom, cfg.name)
+        if kf is not None:
+            ach = kf / per_launch_s / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4),
+                        "traffic": traffic, "ms_per_launch": round(kern[dom]["ms_per_launch"], 4)}
+    for name, k in kern.items():
+        kf = kernel_flops(name, cfg, pairs, kn)
+        if kf is not None:
+            k["tflops"] = round(kf / (k["ms_per_launch"] / 1e3) / 1e12, 2)
+        for f in ("ms_per_launch", "ms_per_step"):
+            k[f] = round(k[f], 4)
+
+    med = lambda v: float(np.median(v))  # noqa: E731
+    value = (F_fwd + F_bwd) / (step_ms / 1e3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_h": cfg.n_h, "d_c": cfg.d_c, "d_rope": cfg.d_rope,
+                   "d_nope": cfg.d_nope, "d_v": cfg.d_v, "S": cfg.S, "S_loc": cfg.S_loc,
+                   "q_offset": cfg.q_offset, "packed_samples": None if cu is None else len(cu) - 1,
+                   "step": "forward+backward", "fast_path": call.fast,
+                   "visible_pairs_per_head": pairs, "keys_needed": kn,
+                   "flop_fwd": F_fwd, "flop_bwd": F_bwd},
+        "frac_peak": round(value / PEAK_TFLOPS, 4),
+        "fwd": {"ms_median": round(med(fwd_ms), 4), "ms_min": round(min(fwd_ms), 4),
+                "tflops": round(F_fwd / (med(fwd_ms) / 1e3) / 1e12, 2),
+                "frac_peak": round(F_fwd / (med(fwd_ms) / 1e3) / 1e12 / PEAK_TFLOPS, 4)},
+        "bwd": {"ms_median": round(med(bwd_ms), 4), "ms_min": round(min(bwd_ms), 4),
+                "tflops": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12, 2),
+                "frac_peak": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12 / PEAK_TFLOPS, 4)},
+        "roofline": roofline,
+        "kernels": kern,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, cu, pairs, kn, budget_s=args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

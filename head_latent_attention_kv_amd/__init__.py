@@ -1,0 +1,284 @@
+"""Python binding of libmla_laga.so, the MI355X latent-attention block.
+
+The names follow the C ABI in include/mla_laga.h. This layer only marshals
+arguments: it reads shapes off torch tensors, allocates outputs and the
+workspace with torch (device memory and the current stream are all torch is
+used for) and calls the library. Every step of the computation runs in the
+library's HIP kernels; if the library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+__all__ = [
+    "MLAError", "MLADesc", "load_library", "library_path", "mla_laga_fwd", "mla_laga_bwd",
+    "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
+    "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC",
+]
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
+MLA_F32, MLA_BF16 = 0, 1
+MLA_FLAG_GENERIC = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmla_laga.so")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+class MLADesc(ctypes.Structure):
+    _fields_ = [
+        ("n_h", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+        ("S", ctypes.c_int64), ("S_loc", ctypes.c_int64), ("q_offset", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_DESCP = ctypes.POINTER(MLADesc)
+
+EXPORTED = {
+    "mla_laga_fwd_workspace_size": (ctypes.c_int, [_DESCP, _I32P, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_laga_bwd_workspace_size": (ctypes.c_int, [_DESCP, _I32P, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_laga_fwd": (ctypes.c_int, [_DESCP, _P, _P, _P, _P, _P, _I32P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
+    "mla_laga_bwd": (ctypes.c_int, [_DESCP, _P, _P, _P, _P, _P, _P, _I32P, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_laga_count": (ctypes.c_int, [_DESCP, _I32P, _I64P, _I64P, _I64P]),
+    "mla_laga_uses_fast_path": (ctypes.c_int, [_DESCP]),
+    "mla_laga_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "mla_laga_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), _I64P]),
+    "mla_laga_timing_names": (ctypes.c_char_p, []),
+    "mla_laga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_laga_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load_library():
+    """Load libmla_laga.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m head_latent_attention_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTED.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return load_library().mla_laga_status_string(s).decode()
+    except ImportError:
+        return str(s)
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MLAError(status, load_library().mla_laga_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _in_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _host_cu(cu_seqlens) -> Optional[np.ndarray]:
+    if cu_seqlens is None:
+        return None
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+
+
+def _cu_ptr(cu: Optional[np.ndarray]):
+    return None if cu is None else cu.ctypes.data_as(_I32P)
+
+
+def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: torch.Tensor,
+              q_offset: int = 0, cu_seqlens=None, softmax_scale: Optional[float] = None,
+              generic: bool = False) -> Tuple[MLADesc, Optional[np.ndarray]]:
+    S_loc, n_h, d_qk = q.shape
+    S, d_c = c_kv.shape
+    d_rope = k_rope.shape[1]
+    cu = _host_cu(cu_seqlens)
+    d = MLADesc()
+    d.n_h, d.d_c, d.d_rope = n_h, d_c, d_rope
+    d.d_nope, d.d_v = d_qk - d_rope, W_UV.shape[1] // n_h
+    d.n_seqs = 0 if cu is None else len(cu) - 1
+    d.S, d.S_loc, d.q_offset = S, S_loc, int(q_offset)
+    d.in_dtype = _in_dtype(q)
+    d.flags = MLA_FLAG_GENERIC if generic else 0
+    d.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    return d, cu
+
+
+def _check_inputs(d: MLADesc, tensors):
+    dt = None
+    for name, t, shape in tensors:
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        dt = t.dtype if dt is None else dt
+        if t.dtype != dt:
+            raise ValueError(f"{name} is {t.dtype}; all inputs must share one dtype ({dt})")
+
+
+def _input_specs(d: MLADesc, q, c_kv, k_rope, W_UK, W_UV):
+    d_qk = d.d_nope + d.d_rope
+    return [("q", q, (d.S_loc, d.n_h, d_qk)), ("c_kv", c_kv, (d.S, d.d_c)),
+            ("k_rope", k_rope, (d.S, d.d_rope)), ("W_UK", W_UK, (d.d_c, d.n_h * d.d_nope)),
+            ("W_UV", W_UV, (d.d_c, d.n_h * d.d_v))]
+
+
+def mla_laga_fwd_workspace_size(desc: MLADesc, cu: Optional[np.ndarray] = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mla_laga_fwd_workspace_size(ctypes.byref(desc), _cu_ptr(cu), ctypes.byref(n)))
+    return n.value
+
+
+def mla_laga_bwd_workspace_size(desc: MLADesc, cu: Optional[np.ndarray] = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mla_laga_bwd_workspace_size(ctypes.byref(desc), _cu_ptr(cu), ctypes.byref(n)))
+    return n.value
+
+
+def mla_laga_count(desc: MLADesc, cu: Optional[np.ndarray] = None) -> Tuple[int, int, int]:
+    """(visible pairs per head, key_lo, key_hi) from the library's host plan."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().mla_laga_count(ctypes.byref(desc), _cu_ptr(cu), ctypes.byref(a),
+                                         ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def mla_laga_uses_fast_path(desc: MLADesc) -> bool:
+    return bool(load_library().mla_laga_uses_fast_path(ctypes.byref(desc)))
+
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel with HIP events on its stream (and forget
+    earlier records)."""
+    _check(load_library().mla_laga_timing_enable(1 if on else 0))
+
+
+def timing_read(kernel: str) -> Tuple[float, int]:
+    """(summed ms, launches) of the recorded kernels named `kernel`; waits for them."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load_library().mla_laga_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def timing_names():
+    return [n for n in load_library().mla_laga_timing_names().decode().split(";") if n]
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # the caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+class MLACall:
+    """One shard's shapes, prepared once: descriptor, host and device
+    cu_seqlens and workspaces, for repeated forward/backward calls."""
+
+    def __init__(self, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
+                 softmax_scale: Optional[float] = None, generic: bool = False,
+                 backward: bool = False):
+        self.desc, self.cu = make_desc(q, c_kv, k_rope, W_UV, q_offset, cu_seqlens,
+                                       softmax_scale, generic)
+        _check_inputs(self.desc, _input_specs(self.desc, q, c_kv, k_rope, W_UK, W_UV))
+        self.device = q.device
+        self.cu_dev = None if self.cu is None else torch.from_numpy(self.cu).to(self.device)
+        self.ws_fwd = _workspace(mla_laga_fwd_workspace_size(self.desc, self.cu), self.device)
+        self.ws_bwd = (_workspace(mla_laga_bwd_workspace_size(self.desc, self.cu), self.device)
+                       if backward else None)
+
+    @property
+    def fast(self) -> bool:
+        return mla_laga_uses_fast_path(self.desc)
+
+    def fwd(self, q, c_kv, k_rope, W_UK, W_UV, out=None, lse=None):
+        d = self.desc
+        if out is None:
+            out = torch.empty((d.S_loc, d.n_h, d.d_v), dtype=torch.float32, device=self.device)
+        if lse is None:
+            lse = torch.empty((d.S_loc, d.n_h), dtype=torch.float32, device=self.device)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(load_library().mla_laga_fwd(
+            ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK), _ptr(W_UV),
+            _cu_ptr(self.cu), _ptr(self.cu_dev), _ptr(out), _ptr(lse), _ptr(self.ws_fwd),
+            self.ws_fwd.numel(), ctypes.c_void_p(stream)))
+        return out, lse
+
+    def bwd(self, dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, grads=None):
+        d = self.desc
+        if self.ws_bwd is None:
+            self.ws_bwd = _workspace(mla_laga_bwd_workspace_size(d, self.cu), self.device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        if grads is None:
+            grads = (torch.empty((d.S_loc, d.n_h, d.d_nope + d.d_rope), **f32),
+                     torch.empty((d.S, d.d_c), **f32), torch.empty((d.S, d.d_rope), **f32),
+                     torch.empty((d.d_c, d.n_h * d.d_nope), **f32),
+                     torch.empty((d.d_c, d.n_h * d.d_v), **f32))
+        dq, dc_kv, dk_rope, dW_UK, dW_UV = grads
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(load_library().mla_laga_bwd(
+            ctypes.byref(d), _ptr(dout), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK),
+            _ptr(W_UV), _cu_ptr(self.cu), _ptr(self.cu_dev), _ptr(out), _ptr(lse), _ptr(dq),
+            _ptr(dc_kv), _ptr(dk_rope), _ptr(dW_UK), _ptr(dW_UV), _ptr(self.ws_bwd),
+            self.ws_bwd.numel(), ctypes.c_void_p(stream)))
+        return grads
+
+
+def mla_laga_fwd(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
+                 softmax_scale: Optional[float] = None, generic: bool = False):
+    """out [S_loc,n_h,d_v] fp32 and lse [S_loc,n_h] fp32 for one query shard."""
+    call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic)
+    return call.fwd(q, c_kv, k_rope, W_UK, W_UV)
+
+
+def mla_laga_bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, q_offset: int = 0,
+                 cu_seqlens=None, softmax_scale: Optional[float] = None, generic: bool = False):
+    """(dq, dc_kv, dk_rope, dW_UK, dW_UV), all fp32, gradients of sum(out*dout)."""
+    call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic,
+                   backward=True)
+    d = call.desc
+    _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))] +
+                  _input_specs(d, q, c_kv, k_rope, W_UK, W_UV)[:1])
+    return call.bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse)

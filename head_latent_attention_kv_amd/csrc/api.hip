@@ -1,0 +1,354 @@
+// C ABI: argument validation, the call plan, workspace layout and dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace mla {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+// ---------------------------------------------------------------- timing
+namespace {
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_event_pool;
+std::string g_names;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void release_records() {
+  for (auto& r : g_launches) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_launches.clear();
+}
+}  // namespace
+
+KernelTimer::KernelTimer(const char* name, hipStream_t st) : st_(st) {
+  if (!g_timing) return;
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return;
+  if (hipEventRecord(a, st) != hipSuccess) {
+    g_event_pool.push_back(a);
+    g_event_pool.push_back(b);
+    return;
+  }
+  g_launches.push_back({name, a, b});
+  slot_ = static_cast<int>(g_launches.size()) - 1;
+}
+
+KernelTimer::~KernelTimer() {
+  // a start event without its stop makes the record unreadable: drop it
+  if (slot_ >= 0 && hipEventRecord(g_launches[slot_].stop, st_) != hipSuccess)
+    g_launches[slot_].name = "";
+}
+
+FwdLayout fwd_layout(const Plan& p) {
+  FwdLayout L{};
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += align_up(bytes, kAlign);
+    return o;
+  };
+  if (p.fast) {
+    L.K = L.V = -1;
+    L.WT = take(static_cast<int64_t>(p.n_h) * (p.d_nope + p.d_v) * p.d_c * 2);  // bf16
+    L.Knope = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 2);       // fp16
+    L.Vt = take(static_cast<int64_t>(p.n_h) * p.d_v * p.Kpad * 2);             // fp16
+    L.Krope = take(p.Kpad * p.d_rope * 2);                                    // fp16
+  } else {
+    L.WT = L.Knope = L.Vt = L.Krope = -1;
+    L.K = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_qk * 4);
+    L.V = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_v * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+BwdLayout bwd_layout(const Plan& p) {
+  BwdLayout L{};
+  L.f = fwd_layout(p);
+  int64_t off = L.f.total;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += align_up(bytes, kAlign);
+    return o;
+  };
+  L.D = take(p.S_loc * p.n_h * 4);
+  if (p.fast) {
+    // dK_nope and dV in fp32 rows [n_h][Kpad][128]; per-head rope-key
+    // gradient partials [n_h][Kpad][64]
+    L.dK = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 4);
+    L.dV = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_v * 4);
+    L.dKrope = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_rope * 4);
+  } else {
+    L.dK = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_qk * 4);
+    L.dV = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_v * 4);
+    L.dKrope = -1;
+  }
+  L.total = off;
+  return L;
+}
+
+static constexpr bool kFastBuilt = false;
+
+static bool fast_shape(const mla_laga_desc* d) {
+  if (!kFastBuilt) return false;
+  return d->in_dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) && d->d_nope == kFastDNope &&
+         d->d_v == kFastDV && d->d_rope == kFastDRope && d->d_c % 64 == 0 && d->d_c >= 64 &&
+         d->d_c <= 4096;
+}
+
+// Validate the descriptor (and host cu_seqlens) and fill the plan.
+static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_h < 1 || d->d_c < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 0)
+    return fail(MLA_ERR_INVALID_ARG, "dims must be positive (n_h=%d d_c=%d d_nope=%d d_v=%d d_rope=%d)",
+                d->n_h, d->d_c, d->d_nope, d->d_v, d->d_rope);
+  if (d->S < 1) return fail(MLA_ERR_INVALID_ARG, "S must be >= 1 (got %lld)", (long long)d->S);
+  if (d->S_loc < 0) return fail(MLA_ERR_INVALID_ARG, "S_loc must be >= 0");
+  if (d->q_offset < 0 || d->q_offset + d->S_loc > d->S)
+    return fail(MLA_ERR_INVALID_ARG, "need 0 <= q_offset and q_offset + S_loc <= S (q_offset=%lld S_loc=%lld S=%lld)",
+                (long long)d->q_offset, (long long)d->S_loc, (long long)d->S);
+  if (d->S > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "S above 2^31-1");
+  if (d->in_dtype != MLA_F32 && d->in_dtype != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "in_dtype must be MLA_F32 or MLA_BF16");
+  if (d->n_seqs < 0) return fail(MLA_ERR_INVALID_ARG, "n_seqs must be >= 0");
+  if (d->n_seqs > 0) {
+    if (!cu) return fail(MLA_ERR_INVALID_ARG, "n_seqs > 0 needs cu_seqlens_host");
+    if (cu[0] != 0 || cu[d->n_seqs] != d->S)
+      return fail(MLA_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at S (got %d .. %d)",
+                  cu[0], cu[d->n_seqs]);
+    for (int k = 0; k < d->n_seqs; ++k)
+      if (cu[k + 1] < cu[k])
+        return fail(MLA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", k);
+  }
+  Plan& P = *p;
+  P.n_h = d->n_h; P.d_c = d->d_c; P.d_rope = d->d_rope; P.d_nope = d->d_nope; P.d_v = d->d_v;
+  P.d_qk = d->d_nope + d->d_rope; P.n_seqs = d->n_seqs;
+  P.S = d->S; P.S_loc = d->S_loc; P.q_offset = d->q_offset;
+  P.bf16 = d->in_dtype == MLA_BF16;
+  P.fast = fast_shape(d);
+  if (!P.fast && (P.d_qk > 256 || P.d_v > 256))
+    return fail(MLA_ERR_UNSUPPORTED, "plain path takes d_nope+d_rope <= 256 and d_v <= 256");
+  P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(P.d_qk));
+  if (!(P.scale < INFINITY)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (P.S_loc > 0) {
+    P.key_lo = seg_lo_host(cu, P.n_seqs, P.q_offset);
+    P.key_hi = P.q_offset + P.S_loc;
+  } else {
+    P.key_lo = P.key_hi = 0;
+  }
+  P.Kn = P.key_hi - P.key_lo;
+  P.Kpad = align_up(P.Kn, kKeyTile);
+  int64_t pairs = 0;
+  for (int64_t i = 0; i < P.S_loc; ++i) {
+    const int64_t pos = P.q_offset + i;
+    pairs += pos - seg_lo_host(cu, P.n_seqs, pos) + 1;
+  }
+  P.visible_pairs = pairs;
+  return MLA_OK;
+}
+
+static bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+mla_status mla_laga_fwd_workspace_size(const mla_laga_desc* desc, const int32_t* cu_host,
+                                        size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  *bytes = static_cast<size_t>(fwd_layout(p).total);
+  return MLA_OK;
+}
+
+mla_status mla_laga_bwd_workspace_size(const mla_laga_desc* desc, const int32_t* cu_host,
+                                        size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  *bytes = static_cast<size_t>(bwd_layout(p).total);
+  return MLA_OK;
+}
+
+mla_status mla_laga_count(const mla_laga_desc* desc, const int32_t* cu_host,
+                          int64_t* visible_pairs, int64_t* key_lo, int64_t* key_hi) {
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (visible_pairs) *visible_pairs = p.visible_pairs;
+  if (key_lo) *key_lo = p.key_lo;
+  if (key_hi) *key_hi = p.key_hi;
+  return MLA_OK;
+}
+
+int mla_laga_uses_fast_path(const mla_laga_desc* desc) {
+  return desc && fast_shape(desc) ? 1 : 0;
+}
+
+static mla_status check_common(const Plan& p, const mla_laga_desc* d, const void* q,
+                               const void* c_kv, const void* k_rope, const void* W_UK,
+                               const void* W_UV, const int32_t* cu_dev, const void* ws,
+                               size_t ws_bytes, int64_t need) {
+  const void* ptrs[] = {q, c_kv, W_UK, W_UV};
+  const char* names[] = {"q", "c_kv", "W_UK", "W_UV"};
+  for (int k = 0; k < 4; ++k) {
+    if (!ptrs[k]) return fail(MLA_ERR_INVALID_ARG, "%s is NULL", names[k]);
+    if (misaligned(ptrs[k])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[k]);
+  }
+  if (p.d_rope > 0 && (!k_rope || misaligned(k_rope)))
+    return fail(MLA_ERR_INVALID_ARG, "k_rope is NULL or not 16-byte aligned");
+  if (d->n_seqs > 0 && !cu_dev) return fail(MLA_ERR_INVALID_ARG, "n_seqs > 0 needs cu_seqlens_dev");
+  if (need > 0 && (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))))
+    return fail(MLA_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (static_cast<int64_t>(ws_bytes) < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %lld", ws_bytes, (long long)need);
+  return MLA_OK;
+}
+
+mla_status mla_laga_fwd(const mla_laga_desc* desc, const void* q, const void* c_kv,
+                        const void* k_rope, const void* W_UK, const void* W_UV,
+                        const int32_t* cu_host, const int32_t* cu_dev, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (p.S_loc == 0) return MLA_OK;
+  const FwdLayout L = fwd_layout(p);
+  if (mla_status s = check_common(p, desc, q, c_kv, k_rope, W_UK, W_UV, cu_dev, workspace,
+                                  workspace_bytes, L.total);
+      s != MLA_OK)
+    return s;
+  if (!out || !lse || misaligned(out) || misaligned(lse))
+    return fail(MLA_ERR_INVALID_ARG, "out/lse NULL or not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (p.fast) return fast_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+  return generic_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+}
+
+mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void* q,
+                        const void* c_kv, const void* k_rope, const void* W_UK, const void* W_UV,
+                        const int32_t* cu_host, const int32_t* cu_dev, const float* out,
+                        const float* lse, float* dq, float* dc_kv, float* dk_rope, float* dW_UK,
+                        float* dW_UV, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (!dc_kv || !dW_UK || !dW_UV || (p.d_rope > 0 && !dk_rope))
+    return fail(MLA_ERR_INVALID_ARG, "a gradient output is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.S_loc == 0) {
+    // no local query: nothing is visible and every gradient is zero
+    mla_status s = zero_fill(dc_kv, p.S * p.d_c, st);
+    if (s == MLA_OK) s = zero_fill(dk_rope, p.S * p.d_rope, st);
+    if (s == MLA_OK) s = zero_fill(dW_UK, static_cast<int64_t>(p.d_c) * p.n_h * p.d_nope, st);
+    if (s == MLA_OK) s = zero_fill(dW_UV, static_cast<int64_t>(p.d_c) * p.n_h * p.d_v, st);
+    return s;
+  }
+  const BwdLayout L = bwd_layout(p);
+  if (mla_status s = check_common(p, desc, q, c_kv, k_rope, W_UK, W_UV, cu_dev, workspace,
+                                  workspace_bytes, L.total);
+      s != MLA_OK)
+    return s;
+  if (!dout || !out || !lse || !dq) return fail(MLA_ERR_INVALID_ARG, "dout/out/lse/dq is NULL");
+  const void* al[] = {dout, out, lse, dq, dc_kv, dk_rope, dW_UK, dW_UV};
+  for (const void* a : al)
+    if (a && misaligned(a)) return fail(MLA_ERR_INVALID_ARG, "a gradient argument is not 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  if (p.fast)
+    return fast_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
+                    dW_UK, dW_UV, ws, st);
+  return generic_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
+                     dW_UK, dW_UV, ws, st);
+}
+
+const char* mla_laga_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "unknown mla_status";
+}
+
+const char* mla_laga_last_error(void) { return g_last_error; }
+
+mla_status mla_laga_timing_enable(int on) {
+  for (auto& r : g_launches)
+    if (!r.name.empty()) (void)hipEventSynchronize(r.stop);
+  release_records();
+  g_timing = on != 0;
+  return MLA_OK;
+}
+
+mla_status mla_laga_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(MLA_ERR_INVALID_ARG, "NULL argument");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_launches) {
+    if (r.name.empty() || r.name != kernel) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess)
+      return fail(MLA_ERR_HIP, "event wait failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      return fail(MLA_ERR_HIP, "event elapsed time failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return MLA_OK;
+}
+
+const char* mla_laga_timing_names(void) {
+  g_names.clear();
+  for (auto& r : g_launches) {
+    const std::string key = r.name + ";";
+    if (g_names.find(key) == std::string::npos) g_names += key;
+  }
+  return g_names.c_str();
+}
+
+}  // extern "C"

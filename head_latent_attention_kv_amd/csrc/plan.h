@@ -1,0 +1,99 @@
+// Host-side call plan shared by the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla_laga.h"
+
+namespace mla {
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Fast-path tile sizes (MFMA kernels).
+constexpr int kFastDNope = 128;
+constexpr int kFastDV = 128;
+constexpr int kFastDRope = 64;
+constexpr int kKeyTile = 128;  // up-projection key tile; rebuilt-K/V rows are padded to it
+
+struct Plan {
+  int n_h, d_c, d_rope, d_nope, d_v, d_qk, n_seqs;
+  int64_t S, S_loc, q_offset;
+  bool bf16;
+  bool fast;
+  float scale;
+  // latent rows the shard needs: [key_lo, key_hi), Kn of them
+  int64_t key_lo, key_hi, Kn, Kpad;
+  int64_t visible_pairs;
+};
+
+// Byte offsets of the workspace regions for one call.
+struct FwdLayout {
+  // plain fp32 path
+  int64_t K, V;
+  // fast path
+  int64_t WT, Knope, Vt, Krope;
+  int64_t total;
+};
+struct BwdLayout {
+  FwdLayout f;
+  int64_t D, dK, dV, dKrope;
+  int64_t total;
+};
+
+FwdLayout fwd_layout(const Plan& p);
+BwdLayout bwd_layout(const Plan& p);
+
+// Set the thread's last-error message and return `s`.
+mla_status fail(mla_status s, const char* fmt, ...);
+mla_status check_launch(const char* what);
+
+// Brackets one kernel launch with HIP events on `st` while timing is on.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t st);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  int slot_ = -1;
+  hipStream_t st_;
+};
+
+// Segment start of global position p (host version; device twin in kernels).
+inline int64_t seg_lo_host(const int32_t* cu, int n_seqs, int64_t p) {
+  if (n_seqs == 0 || cu == nullptr) return 0;
+  // last k with cu[k] <= p  (upper_bound - 1); skips empty samples
+  int lo = 0, hi = n_seqs + 1;  // search in cu[0..n_seqs]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (cu[mid] <= p) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+
+// ---- plain fp32 path (generic.hip)
+mla_status generic_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
+                       const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
+                       float* lse, char* ws, hipStream_t st);
+mla_status generic_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
+                       const void* k_rope, const void* W_UK, const void* W_UV,
+                       const int32_t* cu_dev, const float* out, const float* lse, float* dq,
+                       float* dc_kv, float* dk_rope, float* dW_UK, float* dW_UV, char* ws,
+                       hipStream_t st);
+mla_status zero_fill(float* p, int64_t n, hipStream_t st);
+
+// ---- fast path (fast_*.hip)
+mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
+                    const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
+                    float* lse, char* ws, hipStream_t st);
+mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
+                    const void* k_rope, const void* W_UK, const void* W_UV,
+                    const int32_t* cu_dev, const float* out, const float* lse, float* dq,
+                    float* dc_kv, float* dk_rope, float* dW_UK, float* dW_UV, char* ws,
+                    hipStream_t st);
+
+}  // namespace mla

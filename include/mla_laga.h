@@ -1,0 +1,170 @@
+/*
+ * mla_laga.h - C ABI of the MI355X (gfx950) latent-attention block library.
+ *
+ * The operation (LAGA abstract, "A Training-Memory Regression in MLA Sequence
+ * Parallelism: Why Megatron-Core Forbids Absorption, and LAGA -- a
+ * Communication-Efficient Fix", weekinpapers.com / OpenAlex pages, Abstract):
+ * every sequence-parallel rank holds the gathered compressed KV latent of the
+ * whole sequence and a contiguous block of query rows. It rebuilds each
+ * head's keys and values locally from the latent instead of absorbing the
+ * up-projection into the query, then runs causal attention for its rows.
+ * The result is the explicit MLA form. One call computes one rank's share:
+ *
+ *   K_nope[t,h,:] = c_kv[t,:] @ W_UK[:, h*d_nope : (h+1)*d_nope]
+ *   V[t,h,:]      = c_kv[t,:] @ W_UV[:, h*d_v    : (h+1)*d_v]
+ *   K[t,h,:]      = [ K_nope[t,h,:] | k_rope[t,:] ]          (rope key shared by heads)
+ *   s[i,j,h]      = scale * q[i,h,:] . K[j,h,:]              (q row = [nope | rope])
+ *   lse[i,h]      = ln sum_{j visible} exp(s[i,j,h])
+ *   out[i,h,:]    = sum_{j visible} exp(s[i,j,h] - lse[i,h]) V[j,h,:]
+ *
+ * Row i sits at global position p = q_offset + i and sees keys j with
+ * seg_lo(p) <= j <= p: seg_lo(p) = 0 for one causal sequence, else the start
+ * of the packed sample holding p (block-diagonal causal mask of fixed-token
+ * packing, Libra review page, "Axiom ledger"). q's rope part and k_rope come
+ * already rotated. The backward computes the gradients of sum(out * dout).
+ *
+ * Conventions for every entry point
+ *   - All tensors are dense, row-major, in the shapes given. "Device" means
+ *     memory of the current HIP device; "host" means ordinary host memory.
+ *   - The caller owns all memory, including the workspace. The library does
+ *     not allocate, free, or keep any pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     with no host synchronisation. Outputs are valid once the stream has
+ *     reached the call. Calls that share a workspace must be ordered.
+ *   - Validation happens on the host before anything is enqueued. On error
+ *     nothing is enqueued, the status is returned and a message is kept for
+ *     mla_laga_last_error() (per thread). A failed launch returns MLA_ERR_HIP.
+ *   - Gradients overwrite their outputs (no accumulation). dc_kv and dk_rope
+ *     cover all S latent rows; rows no local query sees are written as 0.
+ *   - Precisions: in_dtype MLA_BF16 (the fast path) or MLA_F32 for q, c_kv,
+ *     k_rope, W_UK, W_UV and dout; out, lse and all gradients are float32.
+ *     The fast path takes d_nope = d_v = 128, d_rope = 64, d_c a multiple of
+ *     64 (512 in DeepSeek-V3), any n_h; it keeps the rebuilt K/V and the
+ *     softmax weights in fp16 with fp32 accumulation. Every other shape (and
+ *     MLA_F32) runs a plain fp32 path of simple kernels.
+ */
+#ifndef MLA_LAGA_H
+#define MLA_LAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* bad shape, offset, pointer or cu_seqlens    */
+  MLA_ERR_UNSUPPORTED = -2, /* valid, but outside what any path handles     */
+  MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  MLA_ERR_HIP = -4          /* a HIP runtime call or a launch failed        */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Force the plain fp32 path even where the fast path applies. */
+#define MLA_FLAG_GENERIC 1
+
+typedef struct {
+  int32_t n_h;      /* heads                                                  */
+  int32_t d_c;      /* latent width                                           */
+  int32_t d_rope;   /* shared rope-key width (also the rope part of q)        */
+  int32_t d_nope;   /* per-head no-position key width                         */
+  int32_t d_v;      /* per-head value width                                   */
+  int32_t n_seqs;   /* 0: one causal sequence over [0,S); else packed samples */
+  int64_t S;        /* latent (key) length                                    */
+  int64_t S_loc;    /* local query rows (0 is a valid empty call)             */
+  int64_t q_offset; /* global position of local row 0                         */
+  int32_t in_dtype; /* mla_dtype of the inputs                                */
+  int32_t flags;    /* MLA_FLAG_* bits                                        */
+  float softmax_scale; /* <= 0: 1/sqrt(d_nope + d_rope)                       */
+} mla_laga_desc;
+
+/*
+ * Workspace bytes mla_laga_fwd / mla_laga_bwd need for `desc` (written to
+ * *bytes). cu_seqlens_host: n_seqs+1 int32 sample starts in host memory
+ * (cu[0] = 0, cu[n_seqs] = S, non-decreasing), or NULL when n_seqs = 0; it
+ * sets how many latent rows the shard needs. Grows linearly in S_loc + q_offset
+ * and in n_h.
+ */
+mla_status mla_laga_fwd_workspace_size(const mla_laga_desc* desc,
+                                        const int32_t* cu_seqlens_host,
+                                        size_t* bytes);
+mla_status mla_laga_bwd_workspace_size(const mla_laga_desc* desc,
+                                        const int32_t* cu_seqlens_host,
+                                        size_t* bytes);
+
+/*
+ * Forward for one query shard (the local computation of LAGA: rebuild K/V
+ * from the gathered latent, then attention; LAGA abstract).
+ *   q        device [S_loc, n_h, d_nope + d_rope]   in_dtype
+ *   c_kv     device [S, d_c]                        in_dtype
+ *   k_rope   device [S, d_rope]                     in_dtype
+ *   W_UK     device [d_c, n_h * d_nope]             in_dtype (head-major columns)
+ *   W_UV     device [d_c, n_h * d_v]                in_dtype (head-major columns)
+ *   cu_seqlens_host / cu_seqlens_dev: the same n_seqs+1 int32 values in host
+ *            and device memory; both NULL when n_seqs = 0.
+ *   out      device [S_loc, n_h, d_v] float32 (written)
+ *   lse      device [S_loc, n_h] float32, natural log (written)
+ *   workspace device, >= mla_laga_fwd_workspace_size bytes, 256-byte aligned.
+ * Device pointers must be 16-byte aligned.
+ */
+mla_status mla_laga_fwd(const mla_laga_desc* desc, const void* q, const void* c_kv,
+                        const void* k_rope, const void* W_UK, const void* W_UV,
+                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        float* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Backward: gradients of sum(out * dout) (training path; LAGA abstract).
+ *   dout     device [S_loc, n_h, d_v] in_dtype
+ *   out, lse device, as written by mla_laga_fwd for the same inputs.
+ *   dq       device [S_loc, n_h, d_nope + d_rope] float32 (written)
+ *   dc_kv    device [S, d_c] float32 (written)
+ *   dk_rope  device [S, d_rope] float32 (written)
+ *   dW_UK    device [d_c, n_h * d_nope] float32 (written)
+ *   dW_UV    device [d_c, n_h * d_v] float32 (written)
+ *   workspace device, >= mla_laga_bwd_workspace_size bytes, 256-byte aligned.
+ * Other arguments as for mla_laga_fwd.
+ */
+mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void* q,
+                        const void* c_kv, const void* k_rope, const void* W_UK,
+                        const void* W_UV, const int32_t* cu_seqlens_host,
+                        const int32_t* cu_seqlens_dev, const float* out, const float* lse,
+                        float* dq, float* dc_kv, float* dk_rope, float* dW_UK, float* dW_UV,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side counts used for FLOP accounting: visible (query, key) pairs per
+ * head, and the half-open latent row range [key_lo, key_hi) the shard needs.
+ * Attention cost grows with the visible pairs, i.e. with the sum of squared
+ * sample lengths for packed data (Libra review page, Eq. 2).
+ */
+mla_status mla_laga_count(const mla_laga_desc* desc, const int32_t* cu_seqlens_host,
+                          int64_t* visible_pairs, int64_t* key_lo, int64_t* key_hi);
+
+/*
+ * Kernel timing, for measurement. While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on the stream it runs
+ * on. mla_laga_timing_enable(1) also forgets earlier records.
+ * mla_laga_timing_read waits for the recorded events and returns the summed
+ * duration (ms) and launch count of the kernels named `kernel` (the names
+ * are listed by mla_laga_timing_names, separated by ';'). Not thread-safe:
+ * enable, run and read from one host thread.
+ */
+mla_status mla_laga_timing_enable(int on);
+mla_status mla_laga_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+const char* mla_laga_timing_names(void);
+
+/* 1 if `desc` runs the fast (MFMA) path, 0 if the plain fp32 path. */
+int mla_laga_uses_fast_path(const mla_laga_desc* desc);
+
+const char* mla_laga_status_string(mla_status status);
+const char* mla_laga_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LAGA_H */

@@ -1,0 +1,132 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, validates arguments on the host before touching
+the device, and its host-side counts agree with the oracle's mask."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+hla = pytest.importorskip("head_latent_attention_kv_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hla.load_library()
+
+
+def header_symbols(root):
+    src = open(os.path.join(root, "include", "mla_laga.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_laga_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib, root_dir):
+    names = header_symbols(root_dir)
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in hla.EXPORTED, f"binding does not wrap {n}"
+
+
+def desc_for(cfg, **kw):
+    d = hla.MLADesc()
+    d.n_h, d.d_c, d.d_rope, d.d_nope, d.d_v = cfg.n_h, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v
+    cu = cfg.cu_seqlens()
+    d.n_seqs = 0 if cu is None else len(cu) - 1
+    d.S, d.S_loc, d.q_offset = cfg.S, cfg.S_loc, cfg.q_offset
+    d.in_dtype = hla.MLA_BF16 if cfg.dtype == "bf16" else hla.MLA_F32
+    d.flags, d.softmax_scale = 0, 0.0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d, cu
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_counts_match_oracle(name):
+    cfg = workloads.config(name)
+    d, cu = desc_for(cfg)
+    pairs, lo, hi = hla.mla_laga_count(d, cu)
+    assert pairs == oracle.visible_pairs(cfg.S_loc, cfg.q_offset, cu)
+    assert (lo, hi) == oracle.key_range(cfg.S_loc, cfg.q_offset, cu)
+
+
+@pytest.mark.parametrize("S,S_loc,q_off,cu", [
+    (12, 12, 0, [0, 3, 3, 4, 9, 12]), (12, 7, 5, [0, 3, 3, 4, 9, 12]),
+    (40, 9, 31, [0, 31, 31, 31, 40]), (5, 1, 4, None), (33, 0, 33, None)])
+def test_counts_edge_cases(S, S_loc, q_off, cu):
+    cfg = workloads.config("tiny_f32").with_(S=S, S_loc=S_loc, q_offset=q_off)
+    d, _ = desc_for(cfg)
+    cu_a = None if cu is None else np.array(cu, np.int32)
+    d.n_seqs = 0 if cu is None else len(cu) - 1
+    pairs, lo, hi = hla.mla_laga_count(d, cu_a)
+    assert pairs == oracle.visible_pairs(S_loc, q_off, cu_a)
+    if S_loc:
+        assert (lo, hi) == oracle.key_range(S_loc, q_off, cu_a)
+
+
+def test_workspace_linear_in_rows_and_heads():
+    # the rebuilt K/V dominate the workspace: affine in the key count and in n_h
+    base = workloads.config("h128_s16k_shard")
+    def ws(**kw):
+        d, cu = desc_for(base.with_(**kw))
+        return hla.mla_laga_fwd_workspace_size(d, cu)
+    a, b, c = ws(S=4096, S_loc=1024, q_offset=3072), ws(S=8192, S_loc=1024, q_offset=7168), \
+        ws(S=12288, S_loc=1024, q_offset=11264)
+    assert b - a == c - b and b > a
+    h1, h2, h3 = ws(n_h=8), ws(n_h=16), ws(n_h=24)
+    assert h2 - h1 == h3 - h2 and h2 > h1
+
+
+def bad(status, fn, *args):
+    with pytest.raises(hla.MLAError) as e:
+        fn(*args)
+    assert e.value.status == status
+    return str(e.value)
+
+
+def test_invalid_arguments_rejected_on_host():
+    cfg = workloads.config("h16_s4k")
+    E = hla.MLA_ERR_INVALID_ARG
+    d, _ = desc_for(cfg, q_offset=1)                       # q_offset + S_loc > S
+    assert "q_offset" in bad(E, hla.mla_laga_fwd_workspace_size, d, None)
+    d, _ = desc_for(cfg, n_h=0)
+    bad(E, hla.mla_laga_fwd_workspace_size, d, None)
+    d, _ = desc_for(cfg, in_dtype=7)
+    bad(E, hla.mla_laga_fwd_workspace_size, d, None)
+    d, _ = desc_for(cfg, n_seqs=2)                         # cu missing
+    bad(E, hla.mla_laga_fwd_workspace_size, d, None)
+    d, _ = desc_for(cfg, n_seqs=2)
+    bad(E, hla.mla_laga_fwd_workspace_size, d, np.array([0, 5, 4000], np.int32))  # end != S
+    bad(E, hla.mla_laga_fwd_workspace_size, d, np.array([0, 5000, 4096], np.int32))  # decreasing
+    d, _ = desc_for(cfg, d_nope=300, in_dtype=hla.MLA_F32)
+    bad(hla.MLA_ERR_UNSUPPORTED, hla.mla_laga_fwd_workspace_size, d, None)
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch(lib):
+    cfg = workloads.config("h16_s4k")
+    d, _ = desc_for(cfg)
+    ws = hla.mla_laga_fwd_workspace_size(d, None)
+    good = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    args = [good] * 5
+    st = lib.mla_laga_fwd(ctypes.byref(d), None, *args[1:], None, None, good, good, good, ws, None)
+    assert st == hla.MLA_ERR_INVALID_ARG and b"q" in lib.mla_laga_last_error()
+    st = lib.mla_laga_fwd(ctypes.byref(d), odd, *args[1:], None, None, good, good, good, ws, None)
+    assert st == hla.MLA_ERR_INVALID_ARG and b"aligned" in lib.mla_laga_last_error()
+    st = lib.mla_laga_fwd(ctypes.byref(d), *args, None, None, good, good, good, ws - 1, None)
+    assert st == hla.MLA_ERR_WORKSPACE
+    st = lib.mla_laga_fwd(ctypes.byref(d), *args, None, None, good, good, None, ws, None)
+    assert st == hla.MLA_ERR_WORKSPACE
+    st = lib.mla_laga_fwd(ctypes.byref(d), *args, None, None, None, good, good, ws, None)
+    assert st == hla.MLA_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert lib.mla_laga_status_string(s).startswith(b"MLA_")

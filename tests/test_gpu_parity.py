@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Small shapes (several tiles and a ragged tail) are compared element by
+element. The full-size workloads run in the same launch configuration the
+benchmark uses and are compared on sampled heads: every output of a head
+depends only on that head's inputs, except the latent and rope-key gradients,
+which sum over heads and are checked with dout zero outside the sampled heads.
+The mask is checked exactly with q = 0, where every visible score is 0, so
+exp(lse) is the number of visible keys of the row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_kv_amd as hla
+import oracle
+import workloads
+from tests.gpu_helpers import announce, check, to_device
+
+pytestmark = pytest.mark.gpu
+
+DSV3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
+GRADS = ("dq", "dc_kv", "dk_rope", "dW_UK", "dW_UV")
+
+
+def small(name, n_h, S, S_loc, q_offset, cu=None, backward=True, seed=3):
+    cfg = workloads.MLAConfig(name, n_h=n_h, S=S, S_loc=S_loc, q_offset=q_offset, dtype="bf16",
+                              backward=backward, seed=seed, **DSV3)
+    return cfg, (None if cu is None else np.array(cu, np.int32))
+
+
+SMALL = [
+    small("causal_ragged", 2, 300, 300, 0),
+    small("shard_ragged", 3, 700, 333, 367),
+    small("varlen_shard", 2, 600, 450, 150, cu=[0, 1, 1, 130, 131, 400, 600]),
+    small("one_token", 1, 1, 1, 0),
+    small("last_row_only", 2, 257, 1, 256),
+    small("varlen_len1_and_empty", 2, 520, 520, 0, cu=[0, 1, 1, 2, 258, 258, 259, 520]),
+]
+
+
+def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None):
+    dev = to_device(x, cfg)
+    if dout_override is not None:
+        dev["dout"] = dout_override
+    call = hla.MLACall(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                       q_offset=cfg.q_offset, cu_seqlens=cu, generic=generic, backward=backward)
+    out, lse = call.fwd(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
+    res = {"out": out, "lse": lse, "fast": call.fast}
+    if backward:
+        g = call.bwd(dev["dout"], dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                     out, lse)
+        res.update(dict(zip(GRADS, g)))
+    torch.cuda.synchronize()
+    return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in res.items()}
+
+
+def oracle_args(x):
+    return [x[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["default", "plain"])
+@pytest.mark.parametrize("cfg,cu", SMALL, ids=[c.name for c, _ in SMALL])
+def test_small_fwd_bwd_elementwise(cfg, cu, generic):
+    announce(f"small {cfg.name} generic={generic} n_h={cfg.n_h} S={cfg.S} S_loc={cfg.S_loc} q_off={cfg.q_offset}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    g = run(cfg, x, cu, generic=generic, backward=True)
+    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu)
+    check("out", g["out"], ro)
+    check("lse", g["lse"], rl)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu)
+    for name, ref in zip(GRADS, rg):
+        check(name, g[name], ref)
+
+
+def test_tiny_f32_config():
+    cfg = workloads.config("tiny_f32")
+    announce("tiny_f32 fwd+bwd")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    g = run(cfg, x, backward=True)
+    ro, rl = oracle.mla_forward(*oracle_args(x))
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x))
+    # fp32 inputs on the plain fp32 path: far inside the bf16 bar
+    for name, got, ref in [("out", g["out"], ro), ("lse", g["lse"], rl)] + \
+            [(n, g[n], r) for n, r in zip(GRADS, rg)]:
+        ma, mr = check(name, got, ref)
+        assert ma < 1e-4 and mr < 1e-5, name
+
+
+def test_h16_s4k_full_forward():
+    cfg = workloads.config("h16_s4k")
+    announce("h16_s4k fwd full")
+    x = workloads.make_inputs(cfg)
+    g = run(cfg, x)
+    ro, rl = oracle.mla_forward(*oracle_args(x))
+    check("out", g["out"], ro)
+    check("lse", g["lse"], rl)
+
+
+@pytest.mark.parametrize("heads", [[0, 37, 64, 127]])
+def test_h128_s16k_shard_forward_sampled_heads(heads):
+    cfg = workloads.config("h128_s16k_shard")
+    announce(f"h128_s16k_shard fwd, heads {heads}")
+    x = workloads.make_inputs(cfg)
+    g = run(cfg, x)
+    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset, heads=heads)
+    check("out", g["out"][:, heads], ro)
+    check("lse", g["lse"][:, heads], rl)
+
+
+@pytest.mark.parametrize("name", ["h128_s8k_bwd", "h128_varlen64k"])
+def test_full_size_backward_sampled_heads(name):
+    cfg = workloads.config(name)
+    cu = cfg.cu_seqlens()
+    heads = [5, 122]
+    announce(f"{name} fwd+bwd, dout only on heads {heads}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    dz = np.zeros_like(x["dout"])
+    dz[:, heads] = x["dout"][:, heads]
+    x0 = dict(x, dout=dz, dout_bits=workloads.f32_to_bf16_bits(dz))
+    g = run(cfg, x0, cu, backward=True)
+    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu, heads=heads)
+    check("out", g["out"][:, heads], ro)
+    check("lse", g["lse"][:, heads], rl)
+    rg = oracle.mla_backward(dz, *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu, heads=heads)
+    for nm, ref in zip(GRADS, rg):
+        check(nm, g[nm], ref)
+
+    announce(f"{name} fwd+bwd, full dout; dq and weight blocks of heads {heads}")
+    g = run(cfg, x, cu, backward=True)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu,
+                             heads=heads)
+    check("dq", g["dq"][:, heads], rg[0][:, heads])
+    cols_k = np.concatenate([np.arange(h * 128, (h + 1) * 128) for h in heads])
+    check("dW_UK", g["dW_UK"][:, cols_k], rg[3][:, cols_k])
+    check("dW_UV", g["dW_UV"][:, cols_k], rg[4][:, cols_k])
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_mask_probe_exact_counts(name):
+    """q = 0: every visible score is exactly 0, so exp(lse) counts the visible
+    keys of each row; it must equal the oracle's integer count exactly."""
+    cfg = workloads.config(name)
+    cu = cfg.cu_seqlens()
+    announce(f"mask probe {name}")
+    x = workloads.make_inputs(cfg)
+    dev = to_device(x, cfg)
+    q0 = torch.zeros_like(dev["q"])
+    call = hla.MLACall(q0, dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                       q_offset=cfg.q_offset, cu_seqlens=cu)
+    _, lse = call.fwd(q0, dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
+    counts = np.rint(np.exp(lse.double().cpu().numpy())).astype(np.int64)
+    lo, hi = oracle.visible_range(cfg.S_loc, cfg.q_offset, cu)
+    expect = (hi - lo + 1)[:, None]
+    bad = np.argwhere(counts != expect)
+    assert bad.size == 0, f"{len(bad)} rows with wrong visible-key count, first {bad[:3]}"
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["default", "plain"])
+def test_shard_concatenation_identity(generic):
+    """Eight contiguous query shards reproduce the single-rank call (LAGA
+    abstract: equivalence across sequence-parallel degrees)."""
+    cfg = workloads.MLAConfig("sp", n_h=4, S=2048, S_loc=2048, q_offset=0, dtype="bf16", **DSV3)
+    announce(f"shard identity generic={generic}")
+    x = workloads.make_inputs(cfg)
+    full = run(cfg, x, generic=generic)
+    n = 256
+    outs, lses = [], []
+    for r in range(8):
+        c = cfg.with_(S_loc=n, q_offset=r * n)
+        xr = dict(x, q=x["q"][r * n:(r + 1) * n], q_bits=x["q_bits"][r * n:(r + 1) * n])
+        g = run(c, xr, generic=generic)
+        outs.append(g["out"]); lses.append(g["lse"])
+    o, l = np.concatenate(outs), np.concatenate(lses)
+    assert np.array_equal(o, full["out"]) and np.array_equal(l, full["lse"])
+
+
+def test_forward_backward_deterministic():
+    cfg = workloads.MLAConfig("det", n_h=8, S=1500, S_loc=1000, q_offset=500, dtype="bf16",
+                              backward=True, **DSV3)
+    announce("determinism")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    a = run(cfg, x, backward=True)
+    b = run(cfg, x, backward=True)
+    for k in ("out", "lse") + GRADS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_empty_shard():
+    cfg = workloads.MLAConfig("empty", n_h=2, S=64, S_loc=0, q_offset=64, dtype="bf16",
+                              backward=True, **DSV3)
+    announce("empty shard")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    dev = to_device(x, cfg)
+    call = hla.MLACall(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                       q_offset=64, backward=True)
+    out, lse = call.fwd(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
+    assert out.numel() == 0 and lse.numel() == 0
+    grads = [torch.full_like(t, 7.0) for t in call.bwd(dev["dout"], dev["q"], dev["c_kv"],
+                                                      dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                                                      out, lse)]
+    grads = call.bwd(dev["dout"], dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
+                     out, lse, grads=grads)
+    torch.cuda.synchronize()
+    for t in grads[1:]:
+        assert torch.count_nonzero(t).item() == 0
