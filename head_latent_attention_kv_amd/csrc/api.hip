@@ -79,7 +79,7 @@ KernelTimer::~KernelTimer() {
     g_launches[slot_].name = "";
 }
 
-FwdLayout fwd_layout(const Plan& p) {
+FwdLayout fwd_layout(const Plan& p, bool fast) {
   FwdLayout L{};
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -87,7 +87,7 @@ FwdLayout fwd_layout(const Plan& p) {
     off += align_up(bytes, kAlign);
     return o;
   };
-  if (p.fast) {
+  if (fast) {
     L.K = L.V = -1;
     L.WT = take(static_cast<int64_t>(p.n_h) * (p.d_nope + p.d_v) * p.d_c * 2);  // bf16
     L.Knope = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 2);       // fp16
@@ -104,7 +104,7 @@ FwdLayout fwd_layout(const Plan& p) {
 
 BwdLayout bwd_layout(const Plan& p) {
   BwdLayout L{};
-  L.f = fwd_layout(p);
+  L.f = fwd_layout(p, p.fast_bwd);
   int64_t off = L.f.total;
   auto take = [&](int64_t bytes) {
     const int64_t o = off;
@@ -112,7 +112,7 @@ BwdLayout bwd_layout(const Plan& p) {
     return o;
   };
   L.D = take(p.S_loc * p.n_h * 4);
-  if (p.fast) {
+  if (p.fast_bwd) {
     // dK_nope and dV in fp32 rows [n_h][Kpad][128]; per-head rope-key
     // gradient partials [n_h][Kpad][64]
     L.dK = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 4);
@@ -127,7 +127,8 @@ BwdLayout bwd_layout(const Plan& p) {
   return L;
 }
 
-static constexpr bool kFastBuilt = false;
+static constexpr bool kFastBuilt = true;
+static constexpr bool kFastBwdBuilt = false;
 
 static bool fast_shape(const mla_laga_desc* d) {
   if (!kFastBuilt) return false;
@@ -166,7 +167,8 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   P.S = d->S; P.S_loc = d->S_loc; P.q_offset = d->q_offset;
   P.bf16 = d->in_dtype == MLA_BF16;
   P.fast = fast_shape(d);
-  if (!P.fast && (P.d_qk > 256 || P.d_v > 256))
+  P.fast_bwd = P.fast && kFastBwdBuilt;
+  if (!P.fast_bwd && (P.d_qk > 256 || P.d_v > 256))
     return fail(MLA_ERR_UNSUPPORTED, "plain path takes d_nope+d_rope <= 256 and d_v <= 256");
   P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(P.d_qk));
   if (!(P.scale < INFINITY)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
@@ -295,7 +297,7 @@ mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void*
   for (const void* a : al)
     if (a && misaligned(a)) return fail(MLA_ERR_INVALID_ARG, "a gradient argument is not 16-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  if (p.fast)
+  if (p.fast_bwd)
     return fast_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
                     dW_UK, dW_UV, ws, st);
   return generic_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,

@@ -1,0 +1,36 @@
+// Launchers shared by the fast-path forward and backward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace mla {
+
+enum class Elem { BF16, F16, F32 };
+
+// out[c][r] = conv(in[r][c]) for r < rows_valid (0 for rows_valid <= r < rows),
+// c < cols; `batch` independent copies, in/out advanced by in_batch/out_batch
+// elements. in is bf16; out is bf16 or fp16.
+mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
+                            int64_t rows, int64_t cols, void* out, int64_t ld_out,
+                            int64_t out_batch, Elem out_t, int batch, hipStream_t st,
+                            const char* name);
+
+// out[r][c] = conv(in[r][c]) with the same conventions (no transpose).
+mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
+                          int64_t rows, int64_t cols, void* out, int64_t ld_out, int64_t out_batch,
+                          Elem out_t, int batch, hipStream_t st, const char* name);
+
+// Out[r][c] = sum_k X[r][k] * Y[c][k] on MFMA, 128x128 tiles, K % 64 == 0.
+// X rows >= R and Y rows >= C read as 0. Element (r, c) is stored at
+//   out + (c / 128) * ct_stride + r * ldo + c % 128
+// for r < R_store and c < C_store (C_store a multiple of 8).
+// in_t: BF16 or F16 (both operands); out_t: F16 or F32.
+mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
+                          int64_t C, int64_t K, void* out, int64_t ldo, int64_t ct_stride,
+                          int64_t R_store, int64_t C_store, Elem in_t, Elem out_t, hipStream_t st,
+                          const char* name);
+
+}  // namespace mla

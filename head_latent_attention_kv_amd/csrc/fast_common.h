@@ -1,0 +1,67 @@
+// Types and helpers shared by the MFMA (gfx950) kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace mla {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_{f16,bf16}: D[32x32] += A[32x16] * B[16x32], one wave.
+// Lane l supplies A row (l % 32), k-slots 8*(l/32)..+7, and B column (l % 32),
+// the same k-slots. D element (m, n) sits in lane n + 32*((m/4) % 2), register
+// 4*(m/8) + m%4.
+__device__ __forceinline__ f32x16 mfma_f16(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <typename T> struct MfmaOp;
+template <> struct MfmaOp<_Float16> {
+  typedef half8 vec;
+  static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) { return mfma_f16(a, b, c); }
+};
+template <> struct MfmaOp<__bf16> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) { return mfma_bf16(a, b, c); }
+};
+
+// Row (within a 32-row MFMA tile) of the D element held by register r of a
+// lane in half `lh` (lh = lane / 32).
+__device__ __forceinline__ int d_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
+
+// Row order for an operand whose D output is fed straight back in as the
+// k-operand of the next product: loading A (or B) row m from source row
+// swap23(m) (bits 2 and 3 of m exchanged) makes D registers 8s..8s+7 of half
+// lh cover source rows 16s + 8lh .. 16s + 8lh + 7 in order, which is exactly
+// the k-slot layout of the next MFMA. The map is its own inverse.
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ half8 bf16x8_to_half8(u32x4 v) {
+  half8 h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = v[k];
+    h[2 * k] = static_cast<_Float16>(__uint_as_float(w << 16));
+    h[2 * k + 1] = static_cast<_Float16>(__uint_as_float(w & 0xffff0000u));
+  }
+  return h;
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // lanes l and l ^ 32 hold the same MFMA column
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+}  // namespace mla

@@ -22,7 +22,8 @@ struct Plan {
   int n_h, d_c, d_rope, d_nope, d_v, d_qk, n_seqs;
   int64_t S, S_loc, q_offset;
   bool bf16;
-  bool fast;
+  bool fast;      // forward runs the MFMA path
+  bool fast_bwd;  // backward runs the MFMA path
   float scale;
   // latent rows the shard needs: [key_lo, key_hi), Kn of them
   int64_t key_lo, key_hi, Kn, Kpad;
@@ -43,7 +44,8 @@ struct BwdLayout {
   int64_t total;
 };
 
-FwdLayout fwd_layout(const Plan& p);
+FwdLayout fwd_layout(const Plan& p, bool fast);
+inline FwdLayout fwd_layout(const Plan& p) { return fwd_layout(p, p.fast); }
 BwdLayout bwd_layout(const Plan& p);
 
 // Set the thread's last-error message and return `s`.
@@ -90,6 +92,10 @@ mla_status zero_fill(float* p, int64_t n, hipStream_t st);
 mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st);
+mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
+                           const void* W_UV, uint16_t* WT, _Float16* Knope, _Float16* Vt,
+                           _Float16* Vkm, _Float16* Krope, _Float16* KnopeT, _Float16* KropeT,
+                           hipStream_t st);
 mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
                     const void* k_rope, const void* W_UK, const void* W_UV,
                     const int32_t* cu_dev, const float* out, const float* lse, float* dq,

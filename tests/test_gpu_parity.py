@@ -30,6 +30,12 @@ def small(name, n_h, S, S_loc, q_offset, cu=None, backward=True, seed=3):
     return cfg, (None if cu is None else np.array(cu, np.int32))
 
 
+# With one visible key a row's softmax weight is exactly 1, so dS = P (dP - D)
+# is zero and dq, dK (hence dk_rope and dW_UK) vanish analytically: the
+# oracle's values are rounding noise, and a ratio of sums against them means
+# nothing. Such tensors get an absolute bound instead.
+VANISHING = {"one_token": {"dq", "dk_rope", "dW_UK"}}
+
 SMALL = [
     small("causal_ragged", 2, 300, 300, 0),
     small("shard_ragged", 3, 700, 333, 367),
@@ -71,7 +77,11 @@ def test_small_fwd_bwd_elementwise(cfg, cu, generic):
     check("lse", g["lse"], rl)
     rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu)
     for name, ref in zip(GRADS, rg):
-        check(name, g[name], ref)
+        if name in VANISHING.get(cfg.name, ()):
+            assert np.abs(ref).max() < 1e-12
+            check(name, g[name], ref, max_abs=2e-3, mean_rel=np.inf)
+        else:
+            check(name, g[name], ref)
 
 
 def test_tiny_f32_config():
