@@ -42,7 +42,8 @@ def kernel_flops(name, cfg, pairs, kn):
     d_qk = cfg.d_nope + cfg.d_rope
     up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
     table = {
-        "upproj": up, "plain_upproj": up,
+        # the fast path rebuilds K_nope and V in separate launches (half each)
+        "upproj": up // 2, "plain_upproj": up,
         "attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
         "plain_attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
         # dK/dV pass: S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
@@ -53,7 +54,8 @@ def kernel_flops(name, cfg, pairs, kn):
         "plain_attn_bwd_dq": 2 * cfg.n_h * (2 * d_qk + cfg.d_v) * pairs,
         # dc_kv = [dK_nope | dV] W^T and dW = c_kv^T [dK_nope | dV]: one up-projection each
         "grad_latent": up, "plain_grad_latent": up,
-        "grad_w": up, "plain_grad_w": up,
+        # dW_UK and dW_UV are separate launches on the fast path
+        "grad_w": up // 2, "plain_grad_w": up,
     }
     return table.get(name)
 

@@ -104,21 +104,38 @@ FwdLayout fwd_layout(const Plan& p, bool fast) {
 
 BwdLayout bwd_layout(const Plan& p) {
   BwdLayout L{};
-  L.f = fwd_layout(p, p.fast_bwd);
-  int64_t off = L.f.total;
+  int64_t off = 0;
   auto take = [&](int64_t bytes) {
     const int64_t o = off;
     off += align_up(bytes, kAlign);
     return o;
   };
-  L.D = take(p.S_loc * p.n_h * 4);
+  L.KnopeT = L.KropeT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = -1;
   if (p.fast_bwd) {
-    // dK_nope and dV in fp32 rows [n_h][Kpad][128]; per-head rope-key
-    // gradient partials [n_h][Kpad][64]
-    L.dK = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 4);
-    L.dV = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_v * 4);
-    L.dKrope = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_rope * 4);
+    const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
+    const int64_t S_pad = align_up(p.S_loc, 64);
+    L.f.K = L.f.V = L.f.Vt = -1;
+    L.f.WT = take(2 * nk * p.d_c * 2);
+    L.f.Knope = take(nk * p.Kpad * 2);
+    L.f.Krope = take(p.Kpad * 64 * 2);
+    L.KnopeT = take(nk * p.Kpad * 2);
+    L.KropeT = take(64 * p.Kpad * 2);
+    L.Vkm = take(nk * p.Kpad * 2);
+    L.W16 = take(static_cast<int64_t>(p.d_c) * 2 * nk * 2);
+    L.ckvT = take(static_cast<int64_t>(p.d_c) * p.Kpad * 2);
+    L.Qn = take(p.n_h * S_pad * 192 * 2);
+    L.Qt = take(p.n_h * S_pad * 192 * 2);
+    L.dOn = take(p.n_h * S_pad * 128 * 2);
+    L.dOt = take(p.n_h * S_pad * 128 * 2);
+    L.D = take(p.n_h * S_pad * 4);
+    L.dK = take(p.Kpad * 2 * nk * 2);
+    L.dV = take(p.Kpad * 2 * nk * 2);
+    L.dKrope = take(p.n_h * p.Kpad * 64 * 4);
+    L.f.total = -1;
   } else {
+    L.f = fwd_layout(p, false);
+    off = L.f.total;
+    L.D = take(p.S_loc * p.n_h * 4);
     L.dK = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_qk * 4);
     L.dV = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_v * 4);
     L.dKrope = -1;
@@ -128,7 +145,7 @@ BwdLayout bwd_layout(const Plan& p) {
 }
 
 static constexpr bool kFastBuilt = true;
-static constexpr bool kFastBwdBuilt = false;
+static constexpr bool kFastBwdBuilt = true;
 
 static bool fast_shape(const mla_laga_desc* d) {
   if (!kFastBuilt) return false;

@@ -39,8 +39,15 @@ struct FwdLayout {
   int64_t total;
 };
 struct BwdLayout {
-  FwdLayout f;
+  FwdLayout f;  // plain path: K, V; fast path: WT, Knope, Krope (Vt unused)
+  // plain path: D [S_loc][n_h], dK/dV fp32 [n_h][Kn][.]
+  // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128],
+  //             dV = its transpose [2*n_h*128][Kpad], dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
+  // fast path only (fp16): K_nope^T [n_h][128][Kpad], k_rope^T [64][Kpad],
+  // V key-major [n_h][Kpad][128], [W_UK | W_UV] [d_c][2*n_h*128],
+  // c_kv^T [d_c][Kpad], q and dout per head: [n_h][S_pad][.] and [n_h][.][S_pad]
+  int64_t KnopeT, KropeT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
   int64_t total;
 };
 
