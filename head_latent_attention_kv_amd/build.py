@@ -42,9 +42,18 @@ COMMON = [
 ]
 
 
+# Per-source device flags. The backward kernels keep their large gradient
+# accumulators next to score tiles that the softmax reads on the VALU; the
+# backend otherwise picks the AGPR form for every MFMA of such a kernel and
+# then copies each score tile back to VGPRs, so ask for the VGPR form there.
+DEVICE_FLAGS = {
+    "fast_bwd.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: harmless
     noise = ("packed-fp32-ops' is not a recognized feature",)

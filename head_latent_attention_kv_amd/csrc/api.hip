@@ -90,11 +90,10 @@ FwdLayout fwd_layout(const Plan& p, bool fast) {
   if (fast) {
     L.K = L.V = -1;
     L.WT = take(static_cast<int64_t>(p.n_h) * (p.d_nope + p.d_v) * p.d_c * 2);  // bf16
-    L.Knope = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_nope * 2);       // fp16
+    L.Kfull = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_qk * 2);         // fp16
     L.Vt = take(static_cast<int64_t>(p.n_h) * p.d_v * p.Kpad * 2);             // fp16
-    L.Krope = take(p.Kpad * p.d_rope * 2);                                    // fp16
   } else {
-    L.WT = L.Knope = L.Vt = L.Krope = -1;
+    L.WT = L.Kfull = L.Vt = -1;
     L.K = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_qk * 4);
     L.V = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_v * 4);
   }
@@ -110,16 +109,14 @@ BwdLayout bwd_layout(const Plan& p) {
     off += align_up(bytes, kAlign);
     return o;
   };
-  L.KnopeT = L.KropeT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = -1;
+  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
     const int64_t S_pad = align_up(p.S_loc, 64);
     L.f.K = L.f.V = L.f.Vt = -1;
     L.f.WT = take(2 * nk * p.d_c * 2);
-    L.f.Knope = take(nk * p.Kpad * 2);
-    L.f.Krope = take(p.Kpad * 64 * 2);
-    L.KnopeT = take(nk * p.Kpad * 2);
-    L.KropeT = take(64 * p.Kpad * 2);
+    L.f.Kfull = take(p.n_h * p.Kpad * 192 * 2);
+    L.KfullT = take(p.n_h * p.Kpad * 192 * 2);
     L.Vkm = take(nk * p.Kpad * 2);
     L.W16 = take(static_cast<int64_t>(p.d_c) * 2 * nk * 2);
     L.ckvT = take(static_cast<int64_t>(p.d_c) * p.Kpad * 2);
@@ -131,6 +128,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.dK = take(p.Kpad * 2 * nk * 2);
     L.dV = take(p.Kpad * 2 * nk * 2);
     L.dKrope = take(p.n_h * p.Kpad * 64 * 4);
+    L.info = take(p.n_h * S_pad * 16);
     L.f.total = -1;
   } else {
     L.f = fwd_layout(p, false);

@@ -23,14 +23,22 @@ mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, i
                           int64_t rows, int64_t cols, void* out, int64_t ld_out, int64_t out_batch,
                           Elem out_t, int batch, hipStream_t st, const char* name);
 
+// out[b][r][0..cols) = fp16(in[r][..]) (bf16 in), rows_valid <= r < rows
+// zero-filled, for b < batch copies advanced by out_batch; 16 B per thread.
+mla_status launch_broadcast_rows_f16(const uint16_t* in, int64_t ld_in, int64_t rows_valid,
+                                     int64_t rows, int cols, _Float16* out, int64_t ld_out,
+                                     int64_t out_batch, int batch, hipStream_t st,
+                                     const char* name);
+
 // Out[r][c] = sum_k X[r][k] * Y[c][k] on MFMA, 128x128 tiles, K % 64 == 0.
 // X rows >= R and Y rows >= C read as 0. Element (r, c) is stored at
-//   out + (c / 128) * ct_stride + r * ldo + c % 128
-// for r < R_store and c < C_store (C_store a multiple of 8).
+//   out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride + c % 128
+// for r < R_store and c < C_store (C_store a multiple of 8). A plain row-major
+// matrix has rt_stride = 128 * ldo and ct_stride = 128.
 // in_t: BF16 or F16 (both operands); out_t: F16 or F32.
 mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
-                          int64_t C, int64_t K, void* out, int64_t ldo, int64_t ct_stride,
-                          int64_t R_store, int64_t C_store, Elem in_t, Elem out_t, hipStream_t st,
-                          const char* name);
+                          int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
+                          int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
+                          Elem out_t, hipStream_t st, const char* name);
 
 }  // namespace mla

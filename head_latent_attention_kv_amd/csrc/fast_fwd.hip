@@ -17,6 +17,7 @@
 //      The running max is only moved when a block's max exceeds it by more
 //      than 2^8 (so P <= 256), which skips almost every rescale of O.
 #include <math.h>
+#include <stdlib.h>
 
 #include "fast.h"
 #include "fast_common.h"
@@ -27,23 +28,18 @@ namespace {
 constexpr int FQ = 256;             // query rows per workgroup
 constexpr int FK = 64;              // keys per step
 constexpr int DQK = 192;
-constexpr int K_ROW_B = DQK * 2;    // bytes per key row in LDS: nope 256 + rope 128
-constexpr int K_TILE_B = FK * K_ROW_B;   // 24 KiB
-constexpr int V_TILE_B = 128 * FK * 2;   // 16 KiB: V^T, 128 rows of 64 keys
+// LDS tiles carry a 16-byte pad per row: a wave's 16-lane groups then hit 16
+// different 16-byte slots of the 64 banks for every read pattern used here
+// (row stride 25 or 9 slots, both odd), and each fragment address is a
+// per-lane base plus a compile-time offset.
+constexpr int K_ROW_B = DQK * 2 + 16;    // 400 B
+constexpr int V_ROW_B = FK * 2 + 16;     // 144 B
+constexpr int K_TILE_B = FK * K_ROW_B;   // 25 KiB: 64 keys x 192 dims
+constexpr int V_TILE_B = 128 * V_ROW_B;  // 18 KiB: V^T, 128 dims x 64 keys
 constexpr int STAGE_B = K_TILE_B + V_TILE_B;
+constexpr int STAGE_PIECES = STAGE_B / 1024;  // 43 DMA wave instructions
 constexpr float kTau = 8.f;         // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
-
-// LDS tiles are unpadded and XOR-swizzled in 16-byte pieces so that they can
-// be filled by global_load_lds (each wave instruction writes 1 KiB
-// contiguously, lane l at +16*l) and read back conflict-free: the 8 lanes
-// served together read 8 different key rows at the same logical piece, and
-// the swizzle spreads those over all 32 banks.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int k_off(int row, int c) {
-  return row * K_ROW_B + (((c & ~7) | ((c & 7) ^ kswz(row))) << 4);
-}
-__device__ __forceinline__ int v_off(int d, int c) { return d * (FK * 2) + ((c ^ (d & 7)) << 4); }
 
 __device__ __forceinline__ void work_item(int bid, int n_h, int n_qt, int* h, int* qt) {
   // consecutive workgroups land on different XCDs (round robin over 8); with
@@ -63,78 +59,86 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Knope,
-                const _Float16* __restrict__ Krope, const _Float16* __restrict__ Vt,
-                const int32_t* __restrict__ cu, float* __restrict__ out, float* __restrict__ lse,
-                int n_h, int n_seqs, int64_t S_loc, int64_t q_offset, int64_t key_lo, int64_t Kpad,
-                int n_qt, float scale_log2) {
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// NT: 32-row query tiles per wave; NW: waves per workgroup (NT*NW*32 = 256).
+// NT = 2 keeps 64 rows per wave (half the LDS reads per MFMA, one wave per
+// SIMD); NT = 1 fits two waves per SIMD, which lets one wave's softmax run
+// while the other's MFMAs do.
+template <int NT, int NW>
+__global__ void __launch_bounds__(NW * 64)
+attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfull,
+                const _Float16* __restrict__ Vt, const int32_t* __restrict__ cu,
+                float* __restrict__ out, float* __restrict__ lse, int n_h, int n_seqs,
+                int S_loc, int q_offset, int key_lo, int Kpad, int n_qt, float scale_log2) {
+  static_assert(NT * NW * 32 == FQ, "workgroup covers 256 query rows");
+  constexpr int NP = (STAGE_PIECES + NW - 1) / NW;  // DMA pieces per wave and stage
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_B];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
   int h, qt;
   work_item(blockIdx.x, n_h, n_qt, &h, &qt);
-  const int64_t q0 = static_cast<int64_t>(qt) * FQ;
-  const int64_t wq0 = q0 + 64 * w;
+  const int q0 = qt * FQ;
+  const int wq0 = q0 + NT * 32 * w;
 
-  // this lane's two query columns (nt = 0, 1); rows past S_loc see nothing
-  int64_t p[2], lo[2];
+  // this lane's query columns; rows past S_loc see nothing
+  int p[NT], lo[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t i = wq0 + 32 * nt + lr;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int i = wq0 + 32 * nt + lr;
     p[nt] = i < S_loc ? q_offset + i : -1;
-    lo[nt] = i < S_loc ? seg_lo_dev(cu, n_seqs, q_offset + i) : 0;
+    lo[nt] = i < S_loc ? static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + i)) : 0;
   }
   const bool wave_live = wq0 < S_loc;
-  const int64_t wi_last = min(S_loc - 1, wq0 + 63);
-  const int64_t wp_min = q_offset + wq0, wp_max = q_offset + wi_last;
-  const int64_t wlo_min = wave_live ? seg_lo_dev(cu, n_seqs, wp_min) : 0;
-  const int64_t wlo_max = wave_live ? seg_lo_dev(cu, n_seqs, wp_max) : 0;
+  const int wi_last = min(S_loc - 1, wq0 + NT * 32 - 1);
+  const int wp_min = q_offset + wq0, wp_max = q_offset + wi_last;
+  const int wlo_min = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_min)) : 0;
+  const int wlo_max = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_max)) : 0;
 
   // key blocks (workspace rows) the workgroup's rows can see
-  const int64_t i_last = min(S_loc - 1, q0 + FQ - 1);
-  const int64_t kb_begin = ((seg_lo_dev(cu, n_seqs, q_offset + q0) - key_lo) / FK) * FK;
-  const int64_t kb_end = q_offset + i_last + 1 - key_lo;
-  const int nblk = static_cast<int>((kb_end - kb_begin + FK - 1) / FK);
+  const int i_last = min(S_loc - 1, q0 + FQ - 1);
+  const int kb_begin = ((static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + q0)) - key_lo) / FK) * FK;
+  const int kb_end = q_offset + i_last + 1 - key_lo;
+  const int nblk = (kb_end - kb_begin + FK - 1) / FK;
 
-  // per-lane sources of this wave's DMA pieces: 6 of the 24 K-tile KiB and
-  // 4 of the 16 V-tile KiB (offsets in elements relative to key block kb)
-  int k_src[6];
-  bool k_rope[6];
+  // DMA: piece I (wave instruction) fills stage bytes [1024 I, 1024 I + 1024),
+  // lane l the 16 bytes at +16 l. Per-lane source offsets (elements) relative
+  // to the block's first key row; the 16-byte pad slot of a row reloads that
+  // row's last piece (never read back).
+  int dsrc[NP];
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int o = (w * 6 + j) * 1024 + lane * 16;
-    const int row = o / K_ROW_B, pos = (o % K_ROW_B) >> 4;
-    const int c = (pos & ~7) | ((pos & 7) ^ kswz(row));
-    k_rope[j] = c >= 16;
-    k_src[j] = c < 16 ? row * 128 + c * 8 : row * 64 + (c - 16) * 8;
+  for (int j = 0; j < NP; ++j) {
+    const int o = (w * NP + j) * 1024 + lane * 16;
+    int off = 0;
+    if (o < K_TILE_B) {
+      const int row = o / K_ROW_B, pc = min((o % K_ROW_B) >> 4, DQK / 8 - 1);
+      off = row * DQK + pc * 8;
+    } else if (o < STAGE_B) {
+      const int oo = o - K_TILE_B, d = oo / V_ROW_B, pc = min((oo % V_ROW_B) >> 4, FK / 8 - 1);
+      off = d * Kpad + pc * 8;
+    }
+    dsrc[j] = off;
   }
-  int v_src[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int o = (w * 4 + j) * 1024 + lane * 16;
-    const int d = o >> 7, pos = (o & 127) >> 4;
-    v_src[j] = d * static_cast<int>(Kpad) + ((pos ^ (d & 7)) << 3);
-  }
-  const _Float16* Kh = Knope + static_cast<int64_t>(h) * Kpad * 128;
+  const _Float16* Kh = Kfull + static_cast<int64_t>(h) * Kpad * DQK;
   const _Float16* Vh = Vt + static_cast<int64_t>(h) * 128 * Kpad;
-  auto issue = [&](int64_t kb, int st) {
-    char* kdst = smem + st * STAGE_B;
-    const _Float16* kn = Kh + kb * 128;
-    const _Float16* kr = Krope + kb * 64;
+  auto issue = [&](int kb, int st) {
+    char* dst = smem + st * STAGE_B;
+    const _Float16* kbase = Kh + static_cast<int64_t>(kb) * DQK;
+    const _Float16* vbase = Vh + kb;
 #pragma unroll
-    for (int j = 0; j < 6; ++j)
-      lds_dma16((k_rope[j] ? kr : kn) + k_src[j], kdst + (w * 6 + j) * 1024);
-    const _Float16* vb = Vh + kb;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(vb + v_src[j], kdst + K_TILE_B + (w * 4 + j) * 1024);
+    for (int j = 0; j < NP; ++j) {
+      const int I = w * NP + j;   // wave-uniform
+      if (I < STAGE_PIECES)
+        lds_dma16((I * 1024 < K_TILE_B ? kbase : vbase) + dsrc[j], dst + I * 1024);
+    }
   };
 
-  half8 qf[2][12];
+  half8 qf[NT][12];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t i = wq0 + 32 * nt + lr;
-    const uint16_t* src = q + (i * n_h + h) * DQK + 8 * lh;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int i = wq0 + 32 * nt + lr;
+    const uint16_t* src = q + (static_cast<int64_t>(i) * n_h + h) * DQK + 8 * lh;
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) {
       if (i < S_loc) {
@@ -146,61 +150,68 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kno
     }
   }
 
-  f32x16 o[2][4];
+  f32x16 o[NT][4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[nt][dt][e] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  float m[NT], l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+  }
+  const half2v ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  // per-lane fragment bases: K rows swap23(lr) (+32 per key tile), V^T rows lr
+  const int k_lane = swap23(lr) * K_ROW_B + lh * 16;
+  const int v_lane = lr * V_ROW_B + lh * 16;
 
   if (nblk > 0) issue(kb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int b = 0; b < nblk; ++b) {
     const int st = b & 1;
-    const int64_t kb = kb_begin + static_cast<int64_t>(b) * FK;
+    const int kb = kb_begin + b * FK;
     if (b + 1 < nblk) issue(kb + FK, st ^ 1);
-    const int64_t g0 = key_lo + kb;  // global position of the block's first key
+    const int g0 = key_lo + kb;  // global position of the block's first key
     const bool skip = !wave_live || g0 > wp_max || g0 + FK - 1 < wlo_min;
     if (!skip) {
       const bool need_mask = !(g0 >= wlo_max && g0 + FK - 1 <= wp_min);
-      const char* sk = smem + st * STAGE_B;
-      const char* sv = sk + K_TILE_B;
+      const char* sk = smem + st * STAGE_B + k_lane;
+      const char* sv = smem + st * STAGE_B + K_TILE_B + v_lane;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         // S^T rows: keys 32mt + swap23(lr) of the block
-        const int krow = 32 * mt + swap23(lr);
-        f32x16 s[2];
+        f32x16 s[NT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[nt][e] = 0.f;
+        const char* skm = sk + mt * 32 * K_ROW_B;
         half8 fa[3];
-        fa[0] = *reinterpret_cast<const half8*>(sk + k_off(krow, lh));
-        fa[1] = *reinterpret_cast<const half8*>(sk + k_off(krow, 2 + lh));
+        fa[0] = *reinterpret_cast<const half8*>(skm);
+        fa[1] = *reinterpret_cast<const half8*>(skm + 32);
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) {
-          if (kk + 2 < 12)
-            fa[(kk + 2) % 3] = *reinterpret_cast<const half8*>(sk + k_off(krow, 2 * (kk + 2) + lh));
-          s[0] = mfma_f16(fa[kk % 3], qf[0][kk], s[0]);
-          s[1] = mfma_f16(fa[kk % 3], qf[1][kk], s[1]);
+          if (kk + 2 < 12) fa[(kk + 2) % 3] = *reinterpret_cast<const half8*>(skm + 32 * (kk + 2));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma_f16(fa[kk % 3], qf[nt][kk], s[nt]);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (need_mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t key = g0 + 32 * mt + swap23(d_row(r, lh));
+            const int key = g0 + 32 * mt + swap23(d_row(r, lh));
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
               if (key < lo[nt] || key > p[nt]) s[nt][r] = -INFINITY;
           }
         }
-        half8 pb[2][2];
+        half8 pb[NT][2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           float mx = s[nt][0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
@@ -217,23 +228,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kno
               for (int e = 0; e < 16; ++e) o[nt][dt][e] *= alpha;
           }
           const float mu = m[nt] == -INFINITY ? 0.f : m[nt];
-          float sum = 0.f;
+          float sum = l[nt];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[nt][r], scale_log2, -mu));
-            sum += pv;
-            pb[nt][r >> 3][r & 7] = static_cast<_Float16>(pv);
+          for (int r = 0; r < 16; r += 2) {
+            half2v pr;
+            pr[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[nt][r], scale_log2, -mu)));
+            pr[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[nt][r + 1], scale_log2, -mu)));
+            pb[nt][r >> 3][r & 7] = pr[0];
+            pb[nt][r >> 3][(r & 7) + 1] = pr[1];
+            sum = __builtin_amdgcn_fdot2(pr, ones, sum, false);   // sum of the fp16 weights
           }
-          l[nt] += sum;
+          l[nt] = sum;
         }
 #pragma unroll
         for (int ksl = 0; ksl < 2; ++ksl) {
           const int ks = 2 * mt + ksl;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const half8 a = *reinterpret_cast<const half8*>(sv + v_off(32 * dt + lr, 2 * ks + lh));
-            o[0][dt] = mfma_f16(a, pb[0][ksl], o[0][dt]);
-            o[1][dt] = mfma_f16(a, pb[1][ksl], o[1][dt]);
+            const half8 a = *reinterpret_cast<const half8*>(sv + dt * 32 * V_ROW_B + ks * 32);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma_f16(a, pb[nt][ksl], o[nt][dt]);
           }
         }
       }
@@ -243,12 +257,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kno
   }
 
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const float lt = l[nt] + __shfl_xor(l[nt], 32, 64);
-    const int64_t i = wq0 + 32 * nt + lr;
+    const int i = wq0 + 32 * nt + lr;
     if (i < S_loc) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* dst = out + (i * n_h + h) * 128;
+      float* dst = out + (static_cast<int64_t>(i) * n_h + h) * 128;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -257,56 +271,70 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kno
                            o[nt][dt][4 * g + 2] * inv, o[nt][dt][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * g + 4 * lh) = v;
         }
-      if (lh == 0) lse[i * n_h + h] = lt > 0.f ? (m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+      if (lh == 0)
+        lse[static_cast<int64_t>(i) * n_h + h] = lt > 0.f ? (m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
 
+// Which attention tiling to launch: 1 = 32 rows per wave, two waves per SIMD
+// (default), 2 = 64 rows per wave, one wave per SIMD. MLA_LAGA_ATTN_VARIANT
+// overrides it.
+int attn_fwd_variant() {
+  static const int v = [] {
+    const char* e = getenv("MLA_LAGA_ATTN_VARIANT");
+    return e ? atoi(e) : 1;
+  }();
+  return v;
+}
+
 }  // namespace
 
-// Up-projection into the forward layouts (shared with the backward, which
-// asks for other layouts through the same GEMM).
+// Rebuild per-head keys and values from the latent (MFMA GEMMs), in the
+// layouts the attention kernels read; null outputs are skipped.
+//   Kfull  [n_h][Kpad][192]  key rows: K_nope | k_rope       (forward, backward)
+//   KfullT [n_h][192][Kpad]  its transpose                    (backward dQ)
+//   Vt     [n_h][128][Kpad]  V transposed                     (forward)
+//   Vkm    [n_h][Kpad][128]  V key rows                       (backward)
+// WT receives [W_UK | W_UV] transposed (bf16 [2*n_h*128][d_c]).
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
-                           const void* W_UV, uint16_t* WT, _Float16* Knope, _Float16* Vt,
-                           _Float16* Vkm, _Float16* Krope, _Float16* KnopeT, _Float16* KropeT,
-                           hipStream_t st) {
+                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* KfullT,
+                           _Float16* Vt, _Float16* Vkm, hipStream_t st) {
   const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
   const uint16_t* ckv = static_cast<const uint16_t*>(c_kv) + p.key_lo * p.d_c;
   const uint16_t* kr = static_cast<const uint16_t*>(k_rope) + p.key_lo * 64;
+  const uint16_t* WTv = WT + nk * p.d_c;
   mla_status s;
-  // WT[n][c]: rows 0..nk-1 from W_UK, nk..2nk-1 from W_UV
   if ((s = launch_transpose(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, WT, p.d_c,
                             0, Elem::BF16, 1, st, "prep_w")) != MLA_OK) return s;
   if ((s = launch_transpose(static_cast<const uint16_t*>(W_UV), nk, 0, p.d_c, p.d_c, nk,
                             WT + nk * p.d_c, p.d_c, 0, Elem::BF16, 1, st, "prep_w")) != MLA_OK)
     return s;
-  if (Krope &&
-      (s = launch_convert(kr, 64, 0, p.Kn, p.Kpad, 64, Krope, 64, 0, Elem::F16, 1, st,
-                          "prep_rope")) != MLA_OK)
-    return s;
-  if (KropeT &&
-      (s = launch_transpose(kr, 64, 0, p.Kn, p.Kpad, 64, KropeT, p.Kpad, 0, Elem::F16, 1, st,
-                            "prep_rope")) != MLA_OK)
-    return s;
-  // K_nope key-major: Out[key][h*128 + d] = c_kv[key] . WT[h*128 + d]
-  if (Knope &&
-      (s = launch_gemm_nt(ckv, p.d_c, p.Kn, WT, p.d_c, nk, p.d_c, Knope, 128, p.Kpad * 128, p.Kpad,
-                          nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
-    return s;
-  // K_nope d-major: Out[h*128 + d][key]
-  if (KnopeT &&
-      (s = launch_gemm_nt(WT, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, KnopeT, p.Kpad, 128, nk, p.Kpad,
-                          Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
-    return s;
-  // V d-major (V^T): Out[h*128 + d][key]
+  if (Kfull) {
+    // Out[key][h*128 + d] = c_kv[key] . WT[h*128 + d] -> Kfull[h][key][d]
+    if ((s = launch_gemm_nt(ckv, p.d_c, p.Kn, WT, p.d_c, nk, p.d_c, Kfull, 192, 128 * 192,
+                            p.Kpad * 192, p.Kpad, nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
+      return s;
+    if ((s = launch_broadcast_rows_f16(kr, 64, p.Kn, p.Kpad, 64, Kfull + 128, 192, p.Kpad * 192,
+                                       p.n_h, st, "prep_rope")) != MLA_OK)
+      return s;
+  }
+  if (KfullT) {
+    // Out[h*128 + d][key] -> KfullT[h][d][key]
+    if ((s = launch_gemm_nt(WT, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, KfullT, p.Kpad, 192 * p.Kpad,
+                            128, nk, p.Kpad, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
+      return s;
+    if ((s = launch_transpose(kr, 64, 0, p.Kn, p.Kpad, 64, KfullT + 128 * p.Kpad, p.Kpad,
+                              192 * p.Kpad, Elem::F16, p.n_h, st, "prep_rope")) != MLA_OK)
+      return s;
+  }
   if (Vt &&
-      (s = launch_gemm_nt(WT + nk * p.d_c, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, Vt, p.Kpad, 128, nk,
+      (s = launch_gemm_nt(WTv, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, Vt, p.Kpad, 128 * p.Kpad, 128, nk,
                           p.Kpad, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
     return s;
-  // V key-major: Out[key][h*128 + d]
   if (Vkm &&
-      (s = launch_gemm_nt(ckv, p.d_c, p.Kn, WT + nk * p.d_c, p.d_c, nk, p.d_c, Vkm, 128,
-                          p.Kpad * 128, p.Kpad, nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
+      (s = launch_gemm_nt(ckv, p.d_c, p.Kn, WTv, p.d_c, nk, p.d_c, Vkm, 128, 128 * 128, p.Kpad * 128,
+                          p.Kpad, nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
     return s;
   return MLA_OK;
 }
@@ -315,24 +343,29 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st) {
   const FwdLayout L = fwd_layout(p);
+  if (p.Kpad * 192 >= (int64_t(1) << 31) || p.S + 256 >= (int64_t(1) << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "fast path takes fewer than 2^23 latent rows per call");
   uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.WT);
-  _Float16* Knope = reinterpret_cast<_Float16*>(ws + L.Knope);
+  _Float16* Kfull = reinterpret_cast<_Float16*>(ws + L.Kfull);
   _Float16* Vt = reinterpret_cast<_Float16*>(ws + L.Vt);
-  _Float16* Krope = reinterpret_cast<_Float16*>(ws + L.Krope);
-  mla_status s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Knope, Vt, nullptr, Krope,
-                                 nullptr, nullptr, st);
+  mla_status s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, Vt, nullptr, st);
   if (s != MLA_OK) return s;
-  if (p.Kpad * 128 >= (int64_t(1) << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "fast path takes fewer than 2^24 latent rows per call");
   const int n_qt = static_cast<int>((p.S_loc + FQ - 1) / FQ);
   const int64_t blocks = static_cast<int64_t>(n_qt) * p.n_h;
   if (blocks > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups");
   const float scale_log2 = p.scale * 1.44269504088896340736f;
+  const int S_loc = static_cast<int>(p.S_loc), q_off = static_cast<int>(p.q_offset),
+            key_lo = static_cast<int>(p.key_lo), Kpad = static_cast<int>(p.Kpad);
   {
     KernelTimer kt("attn_fwd", st);
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), Knope, Krope, Vt, cu_dev, out, lse, p.n_h,
-                       p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kpad, n_qt, scale_log2);
+    if (attn_fwd_variant() == 2)
+      hipLaunchKernelGGL((attn_fwd_kernel<2, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, out, lse, p.n_h,
+                         p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<1, 8>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
+                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, out, lse, p.n_h,
+                         p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
   }
   return check_launch("attention forward");
 }

@@ -21,7 +21,7 @@ template <typename InT, typename OutT>
 __global__ void __launch_bounds__(256)
 gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __restrict__ Y,
                int64_t ldy, int64_t C, int64_t K, OutT* __restrict__ out, int64_t ldo,
-               int64_t ct_stride, int64_t R_store, int64_t C_store) {
+               int64_t rt_stride, int64_t ct_stride, int64_t R_store, int64_t C_store) {
   typedef typename MfmaOp<InT>::vec vec;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][kT * kLS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -111,12 +111,11 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   __syncthreads();
   constexpr int EPC = 16 / sizeof(OutT);   // elements per 16-byte piece
   constexpr int CPR = kT / EPC;            // pieces per row
-  OutT* base = out + (c0 / kT) * ct_stride;
+  OutT* base = out + (r0 / kT) * rt_stride + (c0 / kT) * ct_stride;
   for (int c = tid; c < kT * CPR; c += 256) {
     const int row = c / CPR, cc = (c % CPR) * EPC;
-    const int64_t gr = r0 + row;
-    if (gr >= R_store || c0 + cc >= C_store) continue;
-    *reinterpret_cast<u32x4*>(base + gr * ldo + cc) =
+    if (r0 + row >= R_store || c0 + cc >= C_store) continue;
+    *reinterpret_cast<u32x4*>(base + row * ldo + cc) =
         *reinterpret_cast<const u32x4*>(stg + row * SS + cc);
   }
 }
@@ -170,7 +169,46 @@ convert_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
   }
 }
 
+// out[b][r][0..cols) = fp16(in[r][0..cols)) for r < rows_valid, 0 for
+// rows_valid <= r < rows; b < batch (out advanced by out_batch). 16 bytes per
+// thread; cols, ld_in and ld_out multiples of 8.
+__global__ void __launch_bounds__(256)
+broadcast_rows_f16_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t rows_valid,
+                          int64_t rows, int cols, _Float16* __restrict__ out, int64_t ld_out,
+                          int64_t out_batch, int batch) {
+  const int cpr = cols / 8;
+  const int64_t n = static_cast<int64_t>(batch) * rows * cpr;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(e % cpr);
+    const int64_t r = (e / cpr) % rows;
+    const int64_t b = e / (cpr * rows);
+    half8 v;
+    if (r < rows_valid) {
+      v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(in + r * ld_in + c * 8));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
+    }
+    *reinterpret_cast<half8*>(out + b * out_batch + r * ld_out + c * 8) = v;
+  }
+}
+
 }  // namespace
+
+mla_status launch_broadcast_rows_f16(const uint16_t* in, int64_t ld_in, int64_t rows_valid,
+                                     int64_t rows, int cols, _Float16* out, int64_t ld_out,
+                                     int64_t out_batch, int batch, hipStream_t st,
+                                     const char* name) {
+  if (cols % 8 || ld_in % 8 || ld_out % 8 || out_batch % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: widths must be multiples of 8", name);
+  int64_t blocks = (static_cast<int64_t>(batch) * rows * (cols / 8) + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
+  KernelTimer kt(name, st);
+  hipLaunchKernelGGL(broadcast_rows_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     st, in, ld_in, rows_valid, rows, cols, out, ld_out, out_batch, batch);
+  return check_launch(name);
+}
 
 mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                             int64_t rows, int64_t cols, void* out, int64_t ld_out,
@@ -206,9 +244,9 @@ mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, i
 }
 
 mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
-                          int64_t C, int64_t K, void* out, int64_t ldo, int64_t ct_stride,
-                          int64_t R_store, int64_t C_store, Elem in_t, Elem out_t, hipStream_t st,
-                          const char* name) {
+                          int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
+                          int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
+                          Elem out_t, hipStream_t st, const char* name) {
   if (K % kKC != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: K=%lld not a multiple of 64", name, (long long)K);
   if (C_store % 8 != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: C_store not a multiple of 8", name);
   const int64_t gr = (R_store + kT - 1) / kT, gc = (C_store + kT - 1) / kT;
@@ -218,15 +256,15 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
   if (in_t == Elem::BF16 && out_t == Elem::F16)
     hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16>), grid, dim3(256), 0, st,
                        static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
-                       C, K, static_cast<_Float16*>(out), ldo, ct_stride, R_store, C_store);
+                       C, K, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
   else if (in_t == Elem::F16 && out_t == Elem::F32)
     hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float>), grid, dim3(256), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
-                       ldy, C, K, static_cast<float*>(out), ldo, ct_stride, R_store, C_store);
+                       ldy, C, K, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
   else if (in_t == Elem::F16 && out_t == Elem::F16)
     hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16>), grid, dim3(256), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
-                       ldy, C, K, static_cast<_Float16*>(out), ldo, ct_stride, R_store, C_store);
+                       ldy, C, K, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
   else
     return fail(MLA_ERR_UNSUPPORTED, "%s: GEMM type combination not built", name);
   return check_launch(name);

@@ -34,20 +34,21 @@ struct Plan {
 struct FwdLayout {
   // plain fp32 path
   int64_t K, V;
-  // fast path
-  int64_t WT, Knope, Vt, Krope;
+  // fast path: [W_UK | W_UV]^T bf16, keys [n_h][Kpad][192] fp16, V^T [n_h][128][Kpad] fp16
+  int64_t WT, Kfull, Vt;
   int64_t total;
 };
 struct BwdLayout {
-  FwdLayout f;  // plain path: K, V; fast path: WT, Knope, Krope (Vt unused)
+  FwdLayout f;  // plain path: K, V; fast path: WT, Kfull (Vt unused)
   // plain path: D [S_loc][n_h], dK/dV fp32 [n_h][Kn][.]
   // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128],
   //             dV = its transpose [2*n_h*128][Kpad], dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
-  // fast path only (fp16): K_nope^T [n_h][128][Kpad], k_rope^T [64][Kpad],
-  // V key-major [n_h][Kpad][128], [W_UK | W_UV] [d_c][2*n_h*128],
-  // c_kv^T [d_c][Kpad], q and dout per head: [n_h][S_pad][.] and [n_h][.][S_pad]
-  int64_t KnopeT, KropeT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
+  // fast path only (fp16): keys transposed [n_h][192][Kpad], V key-major
+  // [n_h][Kpad][128], [W_UK | W_UV] [d_c][2*n_h*128], c_kv^T [d_c][Kpad],
+  // q and dout per head: [n_h][S_pad][.] and [n_h][.][S_pad]
+  int64_t KfullT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
+  int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
   int64_t total;
 };
 
@@ -100,9 +101,8 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st);
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
-                           const void* W_UV, uint16_t* WT, _Float16* Knope, _Float16* Vt,
-                           _Float16* Vkm, _Float16* Krope, _Float16* KnopeT, _Float16* KropeT,
-                           hipStream_t st);
+                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* KfullT,
+                           _Float16* Vt, _Float16* Vkm, hipStream_t st);
 mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
                     const void* k_rope, const void* W_UK, const void* W_UV,
                     const int32_t* cu_dev, const float* out, const float* lse, float* dq,
