@@ -30,7 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libmla_laga.so")
+    """The in-tree build, unless MLA_LAGA_LIBRARY names another build of it."""
+    return os.environ.get("MLA_LAGA_LIBRARY") or os.path.join(_HERE, "libmla_laga.so")
 
 
 class MLAError(RuntimeError):

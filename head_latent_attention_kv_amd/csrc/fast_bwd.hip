@@ -9,8 +9,9 @@
 //   dkdv      key-outer: each wave owns 32 keys. S = Q K^T lands with lanes
 //             on keys and registers on query rows, so P and dS feed
 //             dV^T += dO^T P and dK^T += Q^T dS without leaving registers.
-//   dq        query-outer: each wave owns 32 rows; S^T, dP^T per lane = row,
-//             dQ^T += K^T dS^T. No atomics: the result is deterministic.
+//   dq        query-outer: each wave owns 32 rows (two waves per SIMD); S^T,
+//             dP^T per lane = row, dQ^T += K^T dS^T. No atomics: the result
+//             is deterministic.
 //   GEMMs     dc_kv = [dK_nope | dV] [W_UK | W_UV]^T,  dW = c_kv^T [dK_nope | dV]
 //   reduce    dk_rope = sum over heads of the per-head rope-key gradients
 //
@@ -398,7 +399,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
 }
 
 // ------------------------------------------------------------------ dQ
-constexpr int QW = 128;     // query rows per workgroup (4 waves x 32)
+constexpr int QW = 256;     // query rows per workgroup (8 waves x 32, two per SIMD)
 constexpr int KS = 64;      // keys per step
 constexpr int K_ROW = DQK * 2 + 16, V_ROW = DV * 2 + 16, KT_ROW = KS * 2 + 16;  // 400, 272, 144
 // stage (bytes): K [64 keys][192] | V [64 keys][128] | K^T [192 dims][64 keys]
@@ -406,14 +407,14 @@ constexpr int D_K = 0, D_V = KS * K_ROW, D_KT = D_V + KS * V_ROW, D_BYTES = D_KT
 constexpr int D_PIECES = D_BYTES / 1024;
 static_assert(D_V % 1024 == 0 && D_KT % 1024 == 0 && D_BYTES % 1024 == 0, "dq stage layout");
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ D,
                    const _Float16* __restrict__ Kfull, const _Float16* __restrict__ Vkm,
                    const _Float16* __restrict__ KfullT, const int32_t* __restrict__ cu,
                    float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
                    int key_lo, int Kpad, int n_qt, float scale, float scale_log2) {
-  constexpr int NP = (D_PIECES + 3) / 4;
+  constexpr int NP = (D_PIECES + 7) / 8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * D_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -677,7 +678,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
     KernelTimer kt("attn_bwd_dq", st);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(256),
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
                        lse, D, Kfull, Vkm, KfullT, cu_dev, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
                        key_lo, Kpad, n_qt, p.scale, scale_log2);
