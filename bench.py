@@ -60,22 +60,76 @@ def kernel_flops(name, cfg, pairs, kn):
     return table.get(name)
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")
+# kernel symbol fragment -> (timer name, sources whose text decides its code)
+COUNTED_KERNELS = {
+    "attn_fwd_kernel": ("attn_fwd", ["fast_fwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dq_kernel": ("attn_bwd_dq", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 512 * 2**20
+
+
+def sources_sha(sources):
+    h = hashlib.sha256()
+    for name in sources:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "head_latent_attention_kv_amd", "build.py"), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the kernel source as it is now."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    it was taken on the kernel source (and build flags) as they are now."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    rec = json.load(open(TRAFFIC_JSON)).get(f"{kernel}@{workload}")
     if not rec:
         return None
-    src = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc", rec["source"])
-    if not os.path.exists(src):
+    if any(not os.path.exists(os.path.join(CSRC, s)) for s in rec["sources"]):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if sha != rec["sha"]:
+    if sources_sha(rec["sources"]) != rec["sha"]:
         return None
     return rec["bytes_per_launch"]
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload):
+    """Turn two rocprofv3 --pmc csv files (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of a --counter-step run into HBM bytes per launch. Each counter
+    is scaled by bytes / counter of the plain device copy in the same run."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    fcopy = [v for k, v in fetch.items() if COPY_KERNEL in k][0]
+    wcopy = [v for k, v in write.items() if COPY_KERNEL in k][0]
+    fscale = COPY_BYTES / (sum(fcopy) / len(fcopy))
+    wscale = COPY_BYTES / (sum(wcopy) / len(wcopy))
+    table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    for frag, (timer, sources) in COUNTED_KERNELS.items():
+        fk = [v for k, v in fetch.items() if frag in k]
+        wk = [v for k, v in write.items() if frag in k]
+        if not fk or not wk:
+            continue
+        fb = sum(fk[0]) / len(fk[0]) * fscale
+        wb = sum(wk[0]) / len(wk[0]) * wscale
+        table[f"{timer}@{workload}"] = {
+            "bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+            "write_bytes": int(round(wb)), "fetch_scale": round(fscale, 4),
+            "write_scale": round(wscale, 4), "sources": sources, "sha": sources_sha(sources)}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return table
 
 
 def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
@@ -112,7 +166,15 @@ def main():
     ap.add_argument("--workload", default="h128_s16k_shard")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--counter-step", action="store_true",
+                    help="run one warm-up and one step, then a plain 512 MiB device copy "
+                         "(the scale reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two --counter-step counter csv files")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from_counters(*args.traffic_from, args.workload), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's query shard: the library has no multi-GPU path "
@@ -145,6 +207,16 @@ def main():
     def step():
         call.fwd(*a, out=out, lse=lse)
         call.bwd(dev["dout"], *a, out, lse, grads=grads)
+
+    if args.counter_step:
+        step()
+        src = torch.full((COPY_BYTES // 4,), 1.0, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"counter step done: {cfg.name}, copy of {COPY_BYTES} bytes", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
