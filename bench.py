@@ -38,24 +38,32 @@ def flops(cfg, pairs, kn, backward):
 
 
 def kernel_flops(name, cfg, pairs, kn):
-    """Algorithmic FLOPs one launch of `name` does (None: not a contraction)."""
+    """(algorithmic, executed) FLOPs of one launch of `name`; None if it is
+    not a contraction. The algorithmic figures split the step's FLOP count
+    (640 per visible pair and head forward, 1664 backward, plus the
+    up-projection of the needed keys) over the kernels, each product once:
+    the backward's S = Q K^T and dP = dO V^T go to the dK kernel, which is
+    the only one that needs both; the dV and dQ kernels recompute them, and
+    the backward's K/V rebuild launches recompute the up-projection."""
     d_qk = cfg.d_nope + cfg.d_rope
     up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
+    per_pair = lambda d: 2 * cfg.n_h * d * pairs  # noqa: E731
     table = {
-        # the fast path rebuilds K_nope and V in separate launches (half each)
-        "upproj": up // 2, "plain_upproj": up,
-        "attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
-        "plain_attn_fwd": 2 * cfg.n_h * (d_qk + cfg.d_v) * pairs,
-        # dK/dV pass: S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q
-        "attn_bwd_dkdv": 2 * cfg.n_h * (2 * d_qk + 2 * cfg.d_v) * pairs,
-        "plain_attn_bwd_dkdv": 2 * cfg.n_h * (2 * d_qk + 2 * cfg.d_v) * pairs,
-        # dQ pass: S = Q K^T, dP = dO V^T, dQ = dS K
-        "attn_bwd_dq": 2 * cfg.n_h * (2 * d_qk + cfg.d_v) * pairs,
-        "plain_attn_bwd_dq": 2 * cfg.n_h * (2 * d_qk + cfg.d_v) * pairs,
+        # forward launches rebuild K_nope and V separately (half each)
+        "upproj": (up // 2, up // 2), "plain_upproj": (up, up),
+        "attn_fwd": (per_pair(d_qk + cfg.d_v),) * 2,
+        "plain_attn_fwd": (per_pair(d_qk + cfg.d_v),) * 2,
+        # dK: S, dP, dK += dS^T Q;  dV: dV += P^T dO (S recomputed);  dQ: dQ = dS K
+        # (S and dP recomputed)
+        "attn_bwd_dk": (per_pair(2 * d_qk + cfg.d_v),) * 2,
+        "attn_bwd_dv": (per_pair(cfg.d_v), per_pair(d_qk + cfg.d_v)),
+        "attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
+        "plain_attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
+        "plain_attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
         # dc_kv = [dK_nope | dV] W^T and dW = c_kv^T [dK_nope | dV]: one up-projection each
-        "grad_latent": up, "plain_grad_latent": up,
+        "grad_latent": (up, up), "plain_grad_latent": (up, up),
         # dW_UK and dW_UV are separate launches on the fast path
-        "grad_w": up // 2, "plain_grad_w": up,
+        "grad_w": (up // 2, up // 2), "plain_grad_w": (up, up),
     }
     return table.get(name)
 
@@ -65,7 +73,8 @@ CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")
 # kernel symbol fragment -> (timer name, sources whose text decides its code)
 COUNTED_KERNELS = {
     "attn_fwd_kernel": ("attn_fwd", ["fast_fwd.hip", "fast_common.h", "device_common.h"]),
-    "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dkv_kernelILb1": ("attn_bwd_dk", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dkv_kernelILb0": ("attn_bwd_dv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dq_kernel": ("attn_bwd_dq", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -251,14 +260,16 @@ def main():
         per_launch_s = kern[dom]["ms_per_launch"] / 1e3
         traffic = recorded_traffic(dom, cfg.name)
         if kf is not None:
-            ach = kf / per_launch_s / 1e12
+            ach = kf[0] / per_launch_s / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                         "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS, 4),
-                        "traffic": traffic, "ms_per_launch": round(kern[dom]["ms_per_launch"], 4)}
+                        "traffic": traffic, "ms_per_launch": round(kern[dom]["ms_per_launch"], 4),
+                        "mfma_tflops_executed": round(kf[1] / per_launch_s / 1e12, 2)}
     for name, k in kern.items():
         kf = kernel_flops(name, cfg, pairs, kn)
         if kf is not None:
-            k["tflops"] = round(kf / (k["ms_per_launch"] / 1e3) / 1e12, 2)
+            k["tflops"] = round(kf[0] / (k["ms_per_launch"] / 1e3) / 1e12, 2)
+            k["mfma_tflops_executed"] = round(kf[1] / (k["ms_per_launch"] / 1e3) / 1e12, 2)
         for f in ("ms_per_launch", "ms_per_step"):
             k[f] = round(k[f], 4)
 

@@ -6,9 +6,9 @@
 //   prep      D = rowsum(dout * out); q and dout to fp16, per head, both
 //             row-major [row][dim] and column-major [dim][row]
 //   rebuild   K_nope and V again (fp16), in the layouts the kernels read
-//   dkdv      key-outer: each wave owns 32 keys. S = Q K^T lands with lanes
-//             on keys and registers on query rows, so P and dS feed
-//             dV^T += dO^T P and dK^T += Q^T dS without leaving registers.
+//   dK, dV    key-outer, two launches: each wave owns 32 keys and steps
+//             over query rows; S = Q K^T lands with lanes on keys, so P and
+//             dS feed dV^T += dO^T P and dK^T += Q^T dS from registers.
 //   dq        query-outer: each wave owns 32 rows (two waves per SIMD); S^T,
 //             dP^T per lane = row, dQ^T += K^T dS^T. No atomics: the result
 //             is deterministic.
@@ -119,65 +119,79 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
 }
 
 // ------------------------------------------------------------------ dK, dV
-// LDS tiles carry a 16-byte pad per row (row strides of 25, 17 or 5 sixteen-
+// Key-outer, in two launches: one accumulates dK (S, dP, dS, then Q^T dS),
+// the other dV (S, P, then dO^T P). Computing S twice costs 12 of every 52
+// products, but it keeps each wave's live registers (its keys' K and V rows,
+// 96 or 64 accumulators) within 256, so two waves share each SIMD and one's
+// softmax overlaps the other's MFMAs. A workgroup owns 256 keys (8 waves x
+// 32) and steps over query blocks of 64 rows (two sub-blocks of 32).
+//
+// S = Q K^T lands with lanes on keys and registers on query rows; with the
+// query rows loaded in swap23 order, register j of the fp16 P (or dS) pair
+// ks holds query 16 ks + 8 lh + j, which is the k-slot order of the next
+// product's B operand, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS
+// without leaving registers.
+//
+// LDS tiles carry a 16-byte pad per row (row strides of 25, 17 or 9 sixteen-
 // byte slots, all odd): the 16 lanes served together then hit 16 different
 // slots of the 64 banks, and fragment addresses are a per-lane base plus a
 // compile-time offset. Tile regions start on 1 KiB boundaries so each DMA
 // wave instruction (1 KiB) lies in one region.
-constexpr int KB = 128;     // keys per workgroup (4 waves x 32)
-constexpr int QB = 32;      // query rows per step
-constexpr int QN_ROW = DQK * 2 + 16, DON_ROW = DV * 2 + 16, QT_ROW = QB * 2 + 16;  // 400, 272, 80
-// stage (bytes): Qn [32 rows] | dOn [32] | Qt [192] | dOt [128] | row info
-constexpr int S_QN = 0, S_DON = 13 * 1024, S_QT = 22 * 1024, S_DOT = 37 * 1024,
-              S_INFO = 47 * 1024, S_BYTES = 48 * 1024;
-// after the two stages: V rows of the workgroup's 128 keys, resident (34 KiB)
-constexpr int VRES_ROW = DV * 2 + 16, VRES_B = KB * VRES_ROW, VRES_PIECES = VRES_B / 1024;
-static_assert(S_DON >= QB * QN_ROW && S_QT - S_DON >= QB * DON_ROW &&
-              S_DOT - S_QT >= DQK * QT_ROW && S_INFO - S_DOT >= DV * QT_ROW, "dkdv stage layout");
+constexpr int KW = 256;     // keys per workgroup (8 waves x 32)
+constexpr int QB = 64;      // query rows per step
+constexpr int QN_ROW = DQK * 2 + 16, DON_ROW = DV * 2 + 16, QT_ROW = QB * 2 + 16;  // 400, 272, 144
+// stage (bytes), dK launch: Qn [64 rows] | dOn [64] | Qt [192 dims] | row info
+//                dV launch: Qn [64 rows] | dOt [128 dims] | row info
+constexpr int SK_QN = 0, SK_DON = 25 * 1024, SK_QT = 42 * 1024, SK_INFO = 69 * 1024,
+              SK_BYTES = 70 * 1024;
+constexpr int SV_QN = 0, SV_DOT = 25 * 1024, SV_INFO = 43 * 1024, SV_BYTES = 44 * 1024;
+static_assert(SK_DON >= QB * QN_ROW && SK_QT - SK_DON >= QB * DON_ROW &&
+              SK_INFO - SK_QT >= DQK * QT_ROW && SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
+static_assert(SV_QN == SK_QN && SV_DOT == SK_DON, "Qn is the first region of both stages");
+static_assert(SV_DOT >= QB * QN_ROW && SV_INFO - SV_DOT >= DV * QT_ROW &&
+              SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ Qt,
-                     const _Float16* __restrict__ dOn, const _Float16* __restrict__ dOt,
-                     const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
-                     const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
-                     _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
-                     float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
-                     int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S_BYTES + VRES_B];
+template <bool kDK>
+__global__ void __launch_bounds__(512)
+attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ Qt,
+                    const _Float16* __restrict__ dOn, const _Float16* __restrict__ dOt,
+                    const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
+                    const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
+                    _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
+                    float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
+                    int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+  constexpr int BYTES = kDK ? SK_BYTES : SV_BYTES;
+  constexpr int INFO = kDK ? SK_INFO : SV_INFO;
+  constexpr int PIECES = BYTES / 1024;          // DMA wave instructions per stage
+  constexpr int NPW = (PIECES + 7) / 8;         // per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
   int h, kt;
   work_item(blockIdx.x, n_h, n_kt, &h, &kt);
-  char* const vres = smem + 2 * S_BYTES;
-  const int t0 = kt * KB;                     // workspace key row of the workgroup
+  const int t0 = kt * KW;                     // workspace key row of the workgroup
   const int tw = t0 + 32 * w;                 // this wave's first key
   const int gkey = key_lo + tw + lr;          // this lane's key (global)
-  const int gk_min = key_lo + t0, gk_max = key_lo + t0 + KB - 1;
+  const int gk_min = key_lo + t0, gk_max = key_lo + t0 + KW - 1;
   const int gw_min = key_lo + tw, gw_max = gw_min + 31;
 
-  // K rows of this lane's key as MFMA B fragments; the V rows of the
-  // workgroup's keys go to LDS once and are read from there
-  half8 kf[12];
+  // this lane's key row of K (and, for dK, of V) as MFMA B fragments
+  half8 kf[12], vf[kDK ? 8 : 1];
   {
     const _Float16* kr = Kfull + (static_cast<int64_t>(h) * Kpad + tw + lr) * DQK + 8 * lh;
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kr + 16 * kk);
-    const _Float16* vsrc = Vkm + (static_cast<int64_t>(h) * Kpad + t0) * DV;
+    if constexpr (kDK) {
+      const _Float16* vr = Vkm + (static_cast<int64_t>(h) * Kpad + tw + lr) * DV + 8 * lh;
 #pragma unroll
-    for (int j = 0; j < (VRES_PIECES + 3) / 4; ++j) {
-      const int I = w * ((VRES_PIECES + 3) / 4) + j;
-      if (I < VRES_PIECES) {
-        const int o = I * 1024 + lane * 16;
-        const int row = o / VRES_ROW, pc = min((o % VRES_ROW) >> 4, DV / 8 - 1);
-        lds_dma16(vsrc + row * DV + pc * 8, vres + I * 1024);
-      }
+      for (int kk = 0; kk < 8; ++kk) vf[kk] = *reinterpret_cast<const half8*>(vr + 16 * kk);
     }
   }
 
-  // query rows that see any key of the block: from the first row at or past
-  // the block's first key to the last row whose sample starts by its last key
-  int i_begin = max(gk_min - q_offset, 0);
+  // query rows that see any key of the workgroup: from the first row at or
+  // past its first key to the last row whose sample starts by its last key
+  const int i_begin = max(gk_min - q_offset, 0);
   int i_end = S_loc;
   if (n_seqs > 0) {
     // first sample start after gk_max (none: S): rows from there on see nothing here
@@ -191,67 +205,64 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
   const int qb_begin = (i_begin / QB) * QB;
   const int nq = i_end > qb_begin ? (i_end - qb_begin + QB - 1) / QB : 0;
 
-  // DMA: 48 pieces per stage, 12 per wave; per-lane source offsets (elements)
-  // relative to the region's row qb (a region's pad and tail slots reload a
-  // valid element and are never read back)
+  // DMA: per-lane source offsets (elements) relative to the region's first
+  // row qb; a region's pad slots reload a valid element and are never read
   const _Float16* Qn_h = Qn + static_cast<int64_t>(h) * S_pad * DQK;
   const _Float16* dOn_h = dOn + static_cast<int64_t>(h) * S_pad * DV;
   const _Float16* Qt_h = Qt + static_cast<int64_t>(h) * DQK * S_pad;
   const _Float16* dOt_h = dOt + static_cast<int64_t>(h) * DV * S_pad;
-  const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / QB) * 128;
-  int doff[12];
+  const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / 32) * 128;
+  int doff[NPW];
 #pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int o = (w * 12 + j) * 1024 + lane * 16;
-    int off;
-    if (o < S_DON) {
+  for (int j = 0; j < NPW; ++j) {
+    const int o = (w * NPW + j) * 1024 + lane * 16;
+    int off = 0;
+    if (o < SK_DON) {   // Qn (same place in both layouts)
       const int row = min(o / QN_ROW, QB - 1), pc = min((o % QN_ROW) >> 4, DQK / 8 - 1);
       off = row * DQK + pc * 8;
-    } else if (o < S_QT) {
-      const int oo = o - S_DON, row = min(oo / DON_ROW, QB - 1), pc = min((oo % DON_ROW) >> 4, DV / 8 - 1);
+    } else if (o >= INFO) {
+      off = min((o - INFO) >> 2, 2 * 128 - 4);   // 4-byte elements, 128 per 32 rows
+    } else if (kDK && o < SK_QT) {
+      const int oo = o - SK_DON, row = min(oo / DON_ROW, QB - 1), pc = min((oo % DON_ROW) >> 4, DV / 8 - 1);
       off = row * DV + pc * 8;
-    } else if (o < S_DOT) {
-      const int oo = o - S_QT, row = min(oo / QT_ROW, DQK - 1), pc = min((oo % QT_ROW) >> 4, QB / 8 - 1);
+    } else {            // Qt (dK) or dOt (dV): rows are dims, columns the block's rows
+      const int oo = o - (kDK ? SK_QT : SV_DOT);
+      const int row = min(oo / QT_ROW, (kDK ? DQK : DV) - 1), pc = min((oo % QT_ROW) >> 4, QB / 8 - 1);
       off = row * S_pad + pc * 8;
-    } else if (o < S_INFO) {
-      const int oo = o - S_DOT, row = min(oo / QT_ROW, DV - 1), pc = min((oo % QT_ROW) >> 4, QB / 8 - 1);
-      off = row * S_pad + pc * 8;
-    } else {
-      off = min((o - S_INFO) >> 2, 124);   // 4-byte elements, 128 per block
     }
     doff[j] = off;
   }
   auto issue = [&](int qb, int st) {
-    char* base = smem + st * S_BYTES;
+    char* sbase = smem + st * BYTES;
 #pragma unroll
-    for (int j = 0; j < 12; ++j) {
-      const int I = w * 12 + j;   // wave-uniform region choice
-      const void* src;
-      if (I * 1024 < S_DON) src = Qn_h + static_cast<int64_t>(qb) * DQK + doff[j];
-      else if (I * 1024 < S_QT) src = dOn_h + static_cast<int64_t>(qb) * DV + doff[j];
-      else if (I * 1024 < S_DOT) src = Qt_h + qb + doff[j];
-      else if (I * 1024 < S_INFO) src = dOt_h + qb + doff[j];
-      else src = info_h + (qb / QB) * 128 + doff[j];
-      lds_dma16(src, base + I * 1024);
+    for (int j = 0; j < NPW; ++j) {
+      const int I = w * NPW + j;   // wave-uniform region choice
+      if (I < PIECES) {
+        // the per-lane offset is opaque to the optimizer, so it cannot hoist
+        // one 64-bit address per (piece, region) out of the loop
+        int off = doff[j];
+        asm volatile("" : "+v"(off));
+        const void* src;
+        if (I * 1024 < SK_DON) src = Qn_h + static_cast<int64_t>(qb) * DQK + off;
+        else if (I * 1024 >= INFO) src = info_h + (qb / 32) * 128 + off;
+        else if (kDK && I * 1024 < SK_QT) src = dOn_h + static_cast<int64_t>(qb) * DV + off;
+        else src = (kDK ? Qt_h : dOt_h) + qb + off;
+        lds_dma16(src, sbase + I * 1024);
+      }
     }
   };
 
-  f32x16 dk[6], dv[4];
+  constexpr int NACC = kDK ? 6 : 4;   // 32-dim tiles of dK^T (192) or dV^T (128)
+  f32x16 acc[NACC];
 #pragma unroll
-  for (int a = 0; a < 6; ++a)
+  for (int a = 0; a < NACC; ++a)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dk[a][e] = 0.f;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dv[a][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
 
   const int qrow = swap23(lr);   // A-operand row loaded by this lane
-  const int a_qn = S_QN + qrow * QN_ROW + lh * 16;
-  const int a_don = S_DON + qrow * DON_ROW + lh * 16;
-  const int a_dot = S_DOT + lr * QT_ROW + lh * 16;
-  const int a_qt = S_QT + lr * QT_ROW + lh * 16;
-  const char* const v_lane = vres + (32 * w + lr) * VRES_ROW + lh * 16;   // B rows of dP
+  const int a_qn = SK_QN + qrow * QN_ROW + lh * 16;
+  const int a_don = SK_DON + qrow * DON_ROW + lh * 16;
+  const int a_t = (kDK ? SK_QT : SV_DOT) + lr * QT_ROW + lh * 16;   // Q^T or dO^T rows
 
   if (nq > 0) issue(qb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -260,96 +271,101 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     const int st = b & 1;
     const int qb = qb_begin + b * QB;
     if (b + 1 < nq) issue(qb + QB, st ^ 1);
-    const char* base = smem + st * S_BYTES;
-    const float* rinfo = reinterpret_cast<const float*>(base + S_INFO);
-    const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 2 * QB);
-    // global positions of the step's rows: q_offset + qb ..; rows past S_loc have p = -1
-    const int p_first = q_offset + qb;
-    const int p_last = q_offset + min(qb + QB, S_loc) - 1;
-    const bool skip = p_last < gw_min || iinfo[0] > gw_max;
-    if (!skip) {
-      const bool full = qb + QB <= S_loc && p_first >= gw_max && iinfo[QB - 1] <= gw_min;
-      // S = Q K^T (12 steps), then P = exp2(S log2e scale - lse log2e) in fp16
-      half8 pf[2], dsf[2];
+    const char* base = smem + st * BYTES;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int q0 = qb + 32 * mt;
+      const float* rinfo = reinterpret_cast<const float*>(base + INFO + mt * 512);
+      const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 64);
+      // positions of the sub-block's rows: q_offset + q0 ..; rows past S_loc have p = -1
+      const int p_first = q_offset + q0;
+      const int p_last = q_offset + min(q0 + 32, S_loc) - 1;
+      const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
+      if (skip) continue;
+      const bool full = q0 + 32 <= S_loc && p_first >= gw_max && iinfo[31] <= gw_min;
+      // S = Q K^T (12 steps)
+      f32x16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
       {
-        f32x16 s;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
-        half8 fa[2];
-        fa[0] = *reinterpret_cast<const half8*>(base + a_qn);
-#pragma unroll
-        for (int k = 0; k < 12; ++k) {
-          if (k + 1 < 12) fa[(k + 1) % 2] = *reinterpret_cast<const half8*>(base + a_qn + 32 * (k + 1));
-          s = mfma_f16(fa[k % 2], kf[k], s);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!full) {
-          // rows that do not see this lane's key get weight 0 (score -> -inf)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int r0 = swap23(d_row(4 * g, lh));
-            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(iinfo + r0);
-            const u32x4 p4 = *reinterpret_cast<const u32x4*>(iinfo + QB + r0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gkey < static_cast<int>(lo4[e]) || gkey > static_cast<int>(p4[e])) s[4 * g + e] = -INFINITY;
-          }
-        }
-        // register r holds row swap23(d_row(r, lh)); groups of 4 are consecutive rows
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            pf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
-          }
-        }
-      }
-      // dP = dO V^T (8 steps, V from the resident tile), then dS = P (dP - D)
-      {
-        f32x16 dp;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dp[e] = 0.f;
-        half8 fa[2], fv[2];
-        fa[0] = *reinterpret_cast<const half8*>(base + a_don);
-        fv[0] = *reinterpret_cast<const half8*>(v_lane);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k + 1 < 8) {
-            fa[(k + 1) % 2] = *reinterpret_cast<const half8*>(base + a_don + 32 * (k + 1));
-            fv[(k + 1) % 2] = *reinterpret_cast<const half8*>(v_lane + 32 * (k + 1));
-          }
-          dp = mfma_f16(fa[k % 2], fv[k % 2], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + QB + swap23(d_row(4 * g, lh)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const float pv = static_cast<float>(pf[r >> 3][r & 7]);
-            dsf[r >> 3][r & 7] = static_cast<_Float16>(pv * (dp[r] - Dd[e]));
-          }
-        }
-      }
-      {
-        // 20 products: per ks, 4 into dV^T then 6 into dK^T (query rows = k-slots)
         auto frag = [&](int k) {
-          const int ks = k / 10, j = k % 10;
-          return j < 4 ? *reinterpret_cast<const half8*>(base + a_dot + j * 32 * QT_ROW + ks * 32)
-                       : *reinterpret_cast<const half8*>(base + a_qt + (j - 4) * 32 * QT_ROW + ks * 32);
+          return *reinterpret_cast<const half8*>(base + a_qn + mt * 32 * QN_ROW + 32 * k);
         };
         half8 fa[3];
         fa[0] = frag(0);
         fa[1] = frag(1);
 #pragma unroll
-        for (int k = 0; k < 20; ++k) {
-          if (k + 2 < 20) fa[(k + 2) % 3] = frag(k + 2);
-          const int ks = k / 10, j = k % 10;
-          if (j < 4) dv[j] = mfma_f16(fa[k % 3], pf[ks], dv[j]);
-          else dk[j - 4] = mfma_f16(fa[k % 3], dsf[ks], dk[j - 4]);
+        for (int k = 0; k < 12; ++k) {
+          if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
+          s = mfma_f16(fa[k % 3], kf[k], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!full) {
+        // rows that do not see this lane's key get weight 0 (score -> -inf)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = swap23(d_row(4 * g, lh));
+          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(iinfo + r0);
+          const u32x4 p4 = *reinterpret_cast<const u32x4*>(iinfo + 32 + r0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (gkey < static_cast<int>(lo4[e]) || gkey > static_cast<int>(p4[e])) s[4 * g + e] = -INFINITY;
+        }
+      }
+      // P = exp2(S scale log2e - lse log2e) in fp16. Register r holds row
+      // swap23(d_row(r, lh)); groups of 4 are consecutive rows.
+      half8 bf[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          bf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
+        }
+      }
+      if constexpr (kDK) {
+        // dP = dO V^T (8 steps), then dS = P (dP - D) in place of P
+        f32x16 dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+        auto frag = [&](int k) {
+          return *reinterpret_cast<const half8*>(base + a_don + mt * 32 * DON_ROW + 32 * k);
+        };
+        half8 fa[3];
+        fa[0] = frag(0);
+        fa[1] = frag(1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
+          dp = mfma_f16(fa[k % 3], vf[k], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            bf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(bf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
+          }
+        }
+      }
+      // acc^T (dims x keys) += A^T (dims x rows) . bf (rows x keys), rows as k-slots
+      {
+        constexpr int NM = 2 * NACC;
+        auto frag = [&](int k) {
+          const int ks = k / NACC, dm = k % NACC;
+          return *reinterpret_cast<const half8*>(base + a_t + dm * 32 * QT_ROW + (2 * mt + ks) * 32);
+        };
+        half8 fa[3];
+        fa[0] = frag(0);
+        fa[1] = frag(1);
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+          if (k + 2 < NM) fa[(k + 2) % 3] = frag(k + 2);
+          acc[k % NACC] = mfma_f16(fa[k % 3], bf[k / NACC], acc[k % NACC]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -358,18 +374,19 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     __syncthreads();
   }
 
-  // write: lane = key t, registers = columns (four consecutive per group)
+  // write: lane = key t, registers = dims (four consecutive per group)
   const int64_t t = tw + lr;
   const int64_t nk = static_cast<int64_t>(n_h) * 128;
 #pragma unroll
-  for (int mt = 0; mt < 6; ++mt)
+  for (int mt = 0; mt < NACC; ++mt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3
-      const float v0 = dk[mt][4 * g] * scale, v1 = dk[mt][4 * g + 1] * scale,
-                  v2 = dk[mt][4 * g + 2] * scale, v3 = dk[mt][4 * g + 3] * scale;
+      const float sc = kDK ? scale : 1.f;
+      const float v0 = acc[mt][4 * g] * sc, v1 = acc[mt][4 * g + 1] * sc,
+                  v2 = acc[mt][4 * g + 2] * sc, v3 = acc[mt][4 * g + 3] * sc;
       if (d < 128) {
-        const int64_t col = static_cast<int64_t>(h) * 128 + d;
+        const int64_t col = (kDK ? 0 : nk) + static_cast<int64_t>(h) * 128 + d;
         const half4 hv = {static_cast<_Float16>(v0), static_cast<_Float16>(v1),
                           static_cast<_Float16>(v2), static_cast<_Float16>(v3)};
         *reinterpret_cast<half4*>(dKV + t * (2 * nk) + col) = hv;
@@ -381,20 +398,6 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         const f32x4 fv = {v0, v1, v2, v3};
         *reinterpret_cast<f32x4*>(dKr + (static_cast<int64_t>(h) * Kpad + t) * 64 + (d - 128)) = fv;
       }
-    }
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * dt + 8 * g + 4 * lh;
-      const int64_t col = nk + static_cast<int64_t>(h) * 128 + d;
-      const half4 hv = {static_cast<_Float16>(dv[dt][4 * g]), static_cast<_Float16>(dv[dt][4 * g + 1]),
-                        static_cast<_Float16>(dv[dt][4 * g + 2]), static_cast<_Float16>(dv[dt][4 * g + 3])};
-      *reinterpret_cast<half4*>(dKV + t * (2 * nk) + col) = hv;
-      dKVT[(col + 0) * Kpad + t] = hv[0];
-      dKVT[(col + 1) * Kpad + t] = hv[1];
-      dKVT[(col + 2) * Kpad + t] = hv[2];
-      dKVT[(col + 3) * Kpad + t] = hv[3];
     }
 }
 
@@ -668,13 +671,23 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
   {
-    const int n_kt = static_cast<int>(p.Kpad / KB);
-    KernelTimer kt("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(256),
-                       0, st, Qn, Qt, dOn, dOt, info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h,
-                       p.n_seqs, S_loc, Sp, q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+    const int n_kt = static_cast<int>(p.Kpad / KW);
+    const unsigned grid = static_cast<unsigned>(n_kt * p.n_h);
+    {
+      KernelTimer kt("attn_bwd_dk", st);
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<true>, dim3(grid), dim3(512), 0, st, Qn, Qt, dOn, dOt,
+                         info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
+                         q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+    }
+    if ((s = check_launch("attention backward dK")) != MLA_OK) return s;
+    {
+      KernelTimer kt("attn_bwd_dv", st);
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<false>, dim3(grid), dim3(512), 0, st, Qn, Qt, dOn, dOt,
+                         info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
+                         q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+    }
   }
-  if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
+  if ((s = check_launch("attention backward dV")) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
     KernelTimer kt("attn_bwd_dq", st);

@@ -16,7 +16,7 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 constexpr int kFastDNope = 128;
 constexpr int kFastDV = 128;
 constexpr int kFastDRope = 64;
-constexpr int kKeyTile = 128;  // up-projection key tile; rebuilt-K/V rows are padded to it
+constexpr int kKeyTile = 256;  // key tile of the backward's key-outer kernels; rebuilt-K/V rows are padded to it
 
 struct Plan {
   int n_h, d_c, d_rope, d_nope, d_v, d_qk, n_seqs;
