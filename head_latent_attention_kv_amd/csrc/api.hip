@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -109,14 +110,13 @@ BwdLayout bwd_layout(const Plan& p) {
     off += align_up(bytes, kAlign);
     return o;
   };
-  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = -1;
+  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
     const int64_t S_pad = align_up(p.S_loc, 64);
     L.f.K = L.f.V = L.f.Vt = -1;
     L.f.WT = take(2 * nk * p.d_c * 2);
     L.f.Kfull = take(p.n_h * p.Kpad * 192 * 2);
-    L.KfullT = take(p.n_h * p.Kpad * 192 * 2);
     L.Vkm = take(nk * p.Kpad * 2);
     L.W16 = take(static_cast<int64_t>(p.d_c) * 2 * nk * 2);
     L.ckvT = take(static_cast<int64_t>(p.d_c) * p.Kpad * 2);
@@ -129,6 +129,8 @@ BwdLayout bwd_layout(const Plan& p) {
     L.dV = take(p.Kpad * 2 * nk * 2);
     L.dKrope = take(p.n_h * p.Kpad * 64 * 4);
     L.info = take(p.n_h * S_pad * 16);
+    L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
+                            gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
     L.f.total = -1;
   } else {
     L.f = fwd_layout(p, false);

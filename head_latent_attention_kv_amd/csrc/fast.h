@@ -30,15 +30,18 @@ mla_status launch_broadcast_rows_f16(const uint16_t* in, int64_t ld_in, int64_t 
                                      int64_t out_batch, int batch, hipStream_t st,
                                      const char* name);
 
-// Out[r][c] = sum_k X[r][k] * Y[c][k] on MFMA, 128x128 tiles, K % 64 == 0.
-// X rows >= R and Y rows >= C read as 0. Element (r, c) is stored at
+// Out[r][c] = sum_k X[r][k] * Y[c][k] on MFMA, K % 64 == 0. X rows >= R and
+// Y rows >= C count as 0. Element (r, c) is stored at
 //   out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride + c % 128
-// for r < R_store and c < C_store (C_store a multiple of 8). A plain row-major
-// matrix has rt_stride = 128 * ldo and ct_stride = 128.
-// in_t: BF16 or F16 (both operands); out_t: F16 or F32.
+// for r < R_store and c < C_store (C_store a multiple of 8; R_store and
+// C_store may pad R and C up to the 256-row tile that holds their last row).
+// A plain row-major matrix has rt_stride = 128 * ldo and ct_stride = 128.
+// in_t: BF16 or F16 (both operands); out_t: F16 or F32. An fp32 output with
+// few tiles splits K when `part` holds gemm_splitk_bytes() bytes.
 mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
                           int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
                           int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
-                          Elem out_t, hipStream_t st, const char* name);
+                          Elem out_t, hipStream_t st, const char* name, float* part = nullptr,
+                          int64_t part_bytes = 0);
 
 }  // namespace mla

@@ -19,6 +19,8 @@
 // double-buffered, as in the forward.
 #include <math.h>
 
+#include <algorithm>
+
 #include "fast.h"
 #include "fast_common.h"
 
@@ -27,10 +29,6 @@ namespace {
 
 constexpr int DQK = 192, DV = 128;
 constexpr float kLog2e = 1.44269504088896340736f;
-
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
-}
 
 __device__ __forceinline__ void work_item(int bid, int n_h, int n_t, int* h, int* t) {
   // as in the forward: all tiles of a head on one XCD when n_h % 8 == 0
@@ -404,18 +402,18 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
 // ------------------------------------------------------------------ dQ
 constexpr int QW = 256;     // query rows per workgroup (8 waves x 32, two per SIMD)
 constexpr int KS = 64;      // keys per step
-constexpr int K_ROW = DQK * 2 + 16, V_ROW = DV * 2 + 16, KT_ROW = KS * 2 + 16;  // 400, 272, 144
-// stage (bytes): K [64 keys][192] | V [64 keys][128] | K^T [192 dims][64 keys]
-constexpr int D_K = 0, D_V = KS * K_ROW, D_KT = D_V + KS * V_ROW, D_BYTES = D_KT + DQK * KT_ROW;
+constexpr int K_ROW = DQK * 2 + 16, V_ROW = DV * 2 + 16;  // 400, 272
+// stage (bytes): K [64 keys][192] | V [64 keys][128]; the K^T fragments of
+// dQ^T += K^T dS^T are transposed reads of the K tile
+constexpr int D_K = 0, D_V = KS * K_ROW, D_BYTES = D_V + KS * V_ROW;
 constexpr int D_PIECES = D_BYTES / 1024;
-static_assert(D_V % 1024 == 0 && D_KT % 1024 == 0 && D_BYTES % 1024 == 0, "dq stage layout");
+static_assert(D_V % 1024 == 0 && D_BYTES % 1024 == 0, "dq stage layout");
 
 __global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ D,
                    const _Float16* __restrict__ Kfull, const _Float16* __restrict__ Vkm,
-                   const _Float16* __restrict__ KfullT, const int32_t* __restrict__ cu,
-                   float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
+                   const int32_t* __restrict__ cu, float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
                    int key_lo, int Kpad, int n_qt, float scale, float scale_log2) {
   constexpr int NP = (D_PIECES + 7) / 8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * D_BYTES];
@@ -467,7 +465,6 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const _Float16* Kh = Kfull + static_cast<int64_t>(h) * Kpad * DQK;
   const _Float16* Vh = Vkm + static_cast<int64_t>(h) * Kpad * DV;
-  const _Float16* KTh = KfullT + static_cast<int64_t>(h) * DQK * Kpad;
   // DMA pieces of this wave (NP of the 69 per stage): per-lane source offsets
   // relative to the region's first key row kb
   int doff[NP];
@@ -478,12 +475,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     if (o < D_V) {
       const int row = o / K_ROW, pc = min((o % K_ROW) >> 4, DQK / 8 - 1);
       off = row * DQK + pc * 8;
-    } else if (o < D_KT) {
+    } else if (o < D_BYTES) {
       const int oo = o - D_V, row = oo / V_ROW, pc = min((oo % V_ROW) >> 4, DV / 8 - 1);
       off = row * DV + pc * 8;
-    } else if (o < D_BYTES) {
-      const int oo = o - D_KT, row = oo / KT_ROW, pc = min((oo % KT_ROW) >> 4, KS / 8 - 1);
-      off = row * Kpad + pc * 8;
     }
     doff[j] = off;
   }
@@ -494,8 +488,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const int I = w * NP + j;   // wave-uniform
       if (I < D_PIECES) {
         const _Float16* src = I * 1024 < D_V ? Kh + static_cast<int64_t>(kb) * DQK
-                            : I * 1024 < D_KT ? Vh + static_cast<int64_t>(kb) * DV
-                            : KTh + kb;
+                                             : Vh + static_cast<int64_t>(kb) * DV;
         lds_dma16(src + doff[j], base + I * 1024);
       }
     }
@@ -508,7 +501,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
   const int a_k = D_K + swap23(lr) * K_ROW + lh * 16;
   const int a_v = D_V + swap23(lr) * V_ROW + lh * 16;
-  const int a_kt = D_KT + lr * KT_ROW + lh * 16;
+  const int a_kt = D_K + tr_lane_offset(lane, K_ROW);   // K^T fragments: transposed reads
 
   if (nblk > 0) issue(kb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -554,10 +547,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           dsf[r >> 3][r & 7] = static_cast<_Float16>(pv * (dp[r] - Di));
         }
         {
-          // key piece 4mt + 2ksl + lh holds keys 32mt + 16ksl + 8lh ..
+          // K^T fragment: dims 32dm + lr, keys 32mt + 16ksl + 8lh + j (transposed read)
           auto frag = [&](int k) {
             const int ksl = k / 6, dm = k % 6;
-            return *reinterpret_cast<const half8*>(base + a_kt + dm * 32 * KT_ROW + (4 * mt + 2 * ksl) * 16);
+            return frag_tr<K_ROW>(base + a_kt + (32 * mt + 16 * ksl) * K_ROW + 32 * dm * 2);
           };
           half8 fa[3];
           fa[0] = frag(0);
@@ -630,7 +623,6 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   auto at = [&](int64_t off) { return ws + off; };
   uint16_t* WT = reinterpret_cast<uint16_t*>(at(L.f.WT));
   _Float16* Kfull = reinterpret_cast<_Float16*>(at(L.f.Kfull));
-  _Float16* KfullT = reinterpret_cast<_Float16*>(at(L.KfullT));
   _Float16* Vkm = reinterpret_cast<_Float16*>(at(L.Vkm));
   _Float16* W16 = reinterpret_cast<_Float16*>(at(L.W16));
   _Float16* ckvT = reinterpret_cast<_Float16*>(at(L.ckvT));
@@ -649,7 +641,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   mla_status s;
 
   // keys (row- and column-major) and V key-major
-  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, KfullT, nullptr, Vkm, st)) != MLA_OK)
+  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, nullptr, Vkm, st)) != MLA_OK)
     return s;
   // [W_UK | W_UV] rows in fp16 and c_kv^T in fp16 for the gradient GEMMs
   if ((s = launch_convert(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, W16, 2 * nk,
@@ -693,14 +685,17 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     KernelTimer kt("attn_bwd_dq", st);
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       lse, D, Kfull, Vkm, KfullT, cu_dev, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
+                       lse, D, Kfull, Vkm, cu_dev, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
                        key_lo, Kpad, n_qt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0
+  float* gpart = reinterpret_cast<float*>(at(L.gpart));
+  const int64_t gpart_bytes = std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
+                                       gemm_splitk_bytes(p.d_c, nk, p.Kpad));
   if ((s = launch_gemm_nt(dKV, 2 * nk, p.Kn, W16, 2 * nk, p.d_c, 2 * nk, dc_kv + p.key_lo * p.d_c,
                           p.d_c, 128 * p.d_c, 128, p.Kn, p.d_c, Elem::F16, Elem::F32, st,
-                          "grad_latent")) != MLA_OK)
+                          "grad_latent", gpart, gpart_bytes)) != MLA_OK)
     return s;
   {
     KernelTimer kt("zero_rows", st);
@@ -714,10 +709,11 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   if ((s = check_launch("zero rows")) != MLA_OK) return s;
   // dW_UK = c_kv^T dK_nope, dW_UV = c_kv^T dV (contract over the shard's keys)
   if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT, p.Kpad, nk, p.Kpad, dW_UK, nk, 128 * nk, 128,
-                          p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w")) != MLA_OK)
+                          p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart, gpart_bytes)) != MLA_OK)
     return s;
   if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT + nk * p.Kpad, p.Kpad, nk, p.Kpad, dW_UV, nk,
-                          128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w")) != MLA_OK)
+                          128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart,
+                          gpart_bytes)) != MLA_OK)
     return s;
   {
     KernelTimer kt("reduce_rope", st);

@@ -59,6 +59,34 @@ __device__ __forceinline__ half8 bf16x8_to_half8(u32x4 v) {
   return h;
 }
 
+// MFMA A fragment (32 m x 16 k, 16-bit elements) of the transpose of an LDS
+// tile T whose rows are k and whose m run contiguously: lane (l % 32, l / 32)
+// gets T[8 (l / 32) + j][l % 32], j = 0..7, from two ds_read_b64_tr_b16. In
+// one such read, lane i of each 16-lane group receives element i % 4 of the
+// 8-byte pieces fetched by lanes i / 4 + 4e (e = 0..3) of its group; so lane
+// p of group g fetches row 8 (g / 2) + p / 4 at columns 16 (g % 2) + 4 (p % 4)
+// (tr_lane_offset), and every lane of the group then holds four consecutive
+// rows of its own column. `p` is the tile corner (k0, m0) plus that offset.
+__device__ __forceinline__ int tr_lane_offset(int lane, int row_bytes) {
+  const int g = lane >> 4, p = lane & 15;
+  return (8 * (g >> 1) + (p >> 2)) * row_bytes + (16 * (g & 1) + 4 * (p & 3)) * 2;
+}
+typedef short short4v __attribute__((ext_vector_type(4)));
+template <int kRowBytes>
+__device__ __forceinline__ half8 frag_tr(const char* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * kRowBytes));
+  const half4 l = __builtin_bit_cast(half4, lo), h = __builtin_bit_cast(half4, hi);
+  return half8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+}
+
+// One wave instruction of global_load_lds (16 bytes per lane): lane l's 16
+// bytes land at lds_dst + 16 l, so the wave fills 1 KiB of LDS contiguously.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+
 __device__ __forceinline__ float wave_max_pair(float x) {
   // lanes l and l ^ 32 hold the same MFMA column
   return fmaxf(x, __shfl_xor(x, 32, 64));

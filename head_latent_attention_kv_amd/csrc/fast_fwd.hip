@@ -55,10 +55,6 @@ __device__ __forceinline__ void work_item(int bid, int n_h, int n_qt, int* h, in
   }
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
-}
-
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // NT: 32-row query tiles per wave; NW: waves per workgroup (NT*NW*32 = 256).

@@ -4,120 +4,264 @@
 // gathered latent) and the backward's latent and weight gradients are all
 // plain GEMMs with K = d_c, n_h*(d_nope+d_v) or the key count. One kernel
 // covers them: both operands are read k-contiguous (so a lane's 8 k-values
-// are one 16-byte LDS read), 128x128 output tiles, 64-deep k-chunks staged
-// through LDS with a register prefetch of the next chunk, and the result is
-// staged through LDS so every global store is a full 16-byte row piece.
+// are one 16-byte LDS read), 256x256 output tiles over four waves of
+// 128x128, and the result is staged through LDS so every global store is a
+// full 16-byte row piece. Thin outputs (the gradients of c_kv and of the
+// weights) split K over more workgroups and sum the fp32 partials in a fixed
+// order afterwards.
+#include <algorithm>
+#include <type_traits>
+
 #include "fast.h"
 #include "fast_common.h"
 
 namespace mla {
 namespace {
 
-constexpr int kT = 128;        // tile rows / cols
-constexpr int kKC = 64;        // k per chunk
-constexpr int kLS = kKC + 8;   // LDS row stride (elements): 144 B, conflict-free 16 B reads
+constexpr int GT = 256;                 // output tile rows and columns
+constexpr int GK = 32;                  // k per chunk: one 64-byte LDS row per operand row
+constexpr int G_OP = GT * GK * 2;       // one operand's tile (16 KiB)
+constexpr int G_STAGE = 2 * G_OP;       // X and Y tiles
+constexpr int G_NST = 5;                // stages in the ring: four chunks in flight
+constexpr int G_NPW = G_OP / 2048;      // DMA pieces per wave and chunk (two waves per operand): 8
+constexpr int G_MIN_BLOCKS = 512;       // split K until the grid has this many workgroups
+static_assert(G_NST * G_STAGE <= 160 * 1024, "ring fits the LDS");
+static_assert((G_NST - 2) * G_NPW <= 63, "outstanding DMA count fits vmcnt");
 
-template <typename InT, typename OutT>
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (n in {0, 8, 16, 24}; gfx9 encoding of s_waitcnt: vmcnt bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    default: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+  }
+}
+
+// Tile of workgroup `bid`. Tiles run in groups of 8 tile rows (all columns of
+// a group before the next group); when the count divides by 8, XCD x (blocks
+// x, x + 8, ...) takes the x-th eighth of that order, so the tiles one XCD
+// holds at a time share rows and columns in its L2.
+__device__ __forceinline__ void gemm_tile(int bid, int n_tr, int n_tc, int* tr, int* tc) {
+  const int n = n_tr * n_tc;
+  const int L = (n & 7) == 0 ? (bid & 7) * (n >> 3) + (bid >> 3) : bid;
+  constexpr int G = 8;
+  const int group = L / (G * n_tc);
+  const int first = group * G;
+  const int rows = min(G, n_tr - first);
+  const int within = L - group * G * n_tc;
+  *tr = first + within % rows;
+  *tc = within / rows;
+}
+
+// Out[r][c] = sum_k X[r][k] Y[c][k] over one K range (blockIdx.y selects it):
+// 256x256 tiles, four waves of 128x128 (16 MFMA accumulators each), 32-deep
+// k-chunks DMA-filled (global_load_lds) into a ring of five LDS stages, so
+// four chunks are in flight while one is consumed: with one workgroup per
+// CU, that depth is what covers the latency of the operand reads that miss
+// in L2. A 64-byte operand row holds its four 16-byte k-slots in the order
+// slot ^ ((row / 4) % 4), so the 16 rows read together by a fragment load
+// fall on 16 different slots of the 64 banks. Rows of X past R and of Y past
+// C are clamped to the last valid row when loading and their results are
+// written as 0. With kPart, the tile goes unmasked to part[blockIdx.y][r][c]
+// (fp32) for a split-K reduction; otherwise to `out` in the tiled layout of
+// launch_gemm_nt.
+template <typename InT, typename OutT, bool kPart>
 __global__ void __launch_bounds__(256)
 gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __restrict__ Y,
-               int64_t ldy, int64_t C, int64_t K, OutT* __restrict__ out, int64_t ldo,
-               int64_t rt_stride, int64_t ct_stride, int64_t R_store, int64_t C_store) {
+               int64_t ldy, int64_t C, int64_t k_len, OutT* __restrict__ out, int64_t ldo,
+               int64_t rt_stride, int64_t ct_stride, int64_t R_store, int64_t C_store,
+               float* __restrict__ part, int n_tr, int n_tc) {
   typedef typename MfmaOp<InT>::vec vec;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][kT * kLS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the ring, reused afterwards to stage an fp16 output tile
+  __shared__ __attribute__((aligned(1024))) char smem[G_NST * G_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kT;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT;
-  const int rw = (w & 1) * 64, cw = (w >> 1) * 64;
+  int tr, tc;
+  gemm_tile(blockIdx.x, n_tr, n_tc, &tr, &tc);
+  const int64_t r0 = static_cast<int64_t>(tr) * GT, c0 = static_cast<int64_t>(tc) * GT;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_len;
+  const int wr = w >> 1, wc = w & 1;   // this wave's 128x128 quarter
+  const bool live = R > 0 && C > 0;
 
-  f32x16 acc[2][2];
+  // waves 0-1 fill the X tile, 2-3 the Y tile (18 pieces of 1 KiB each); a
+  // row's pad slot reloads a valid element and is never read back
+  const bool is_x = w < 2;
+  const int64_t ld = is_x ? ldx : ldy;
+  const InT* src = live ? (is_x ? X + r0 * ldx : Y + c0 * ldy) + kbeg : nullptr;
+  const int last = static_cast<int>((is_x ? R - r0 : C - c0) - 1);   // >= 0 for live tiles
+  // piece p of an operand tile = rows 16p .. 16p + 15; lane l fills row
+  // 16p + l / 4, physical slot l % 4, which holds k-slot (l % 4) ^ ((row / 4) % 4)
+  int doff[G_NPW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < G_NPW; ++j) {
+    const int row = 16 * ((w & 1) * G_NPW + j) + (lane >> 2);
+    const int slot = (lane & 3) ^ ((row >> 2) & 3);
+    doff[j] = min(row, last) * static_cast<int>(ld) + slot * 8;
+  }
+  auto issue = [&](int c, int st) {
+    char* dst = smem + st * G_STAGE + (is_x ? 0 : G_OP) + (w & 1) * G_NPW * 1024;
+    const InT* s0 = src + static_cast<int64_t>(c) * GK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < G_NPW; ++j) {
+      // opaque to the optimizer, so no 64-bit address per piece is hoisted
+      int off = doff[j];
+      asm volatile("" : "+v"(off));
+      lds_dma16(s0 + off, dst + j * 1024);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 pre[8];
-  auto load = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int64_t gr = r0 + row, gc = c0 + row;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      pre[i] = gr < R ? *reinterpret_cast<const u32x4*>(X + gr * ldx + k0 + col) : z;
-      pre[4 + i] = gc < C ? *reinterpret_cast<const u32x4*>(Y + gc * ldy + k0 + col) : z;
-    }
-  };
-  auto store = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&smem[st][0][row * kLS + col]) = pre[i];
-      *reinterpret_cast<u32x4*>(&smem[st][1][row * kLS + col]) = pre[4 + i];
-    }
-  };
-
-  const int nk = static_cast<int>(K / kKC);
-  load(0);
-  store(0);
-  __syncthreads();
+  // fragment rows are wave base + 32 i + lr, so (row / 4) % 4 = (lr / 4) % 4
+  const int so0 = ((0 + lh) ^ ((lr >> 2) & 3)) * 16, so1 = ((2 + lh) ^ ((lr >> 2) & 3)) * 16;
+  const int nk = live ? static_cast<int>(k_len / GK) : 0;
+  for (int c = 0; c < min(nk, G_NST - 1); ++c) issue(c, c);
   for (int kc = 0; kc < nk; ++kc) {
-    const int st = kc & 1;
-    if (kc + 1 < nk) load(static_cast<int64_t>(kc + 1) * kKC);
-    const uint16_t* sx = smem[st][0];
-    const uint16_t* sy = smem[st][1];
+    // this wave's pieces of chunk kc have landed once at most the later
+    // chunks already issued are outstanding; the barrier then makes every
+    // wave's pieces visible and shows that every wave is done with the
+    // stage the next issue refills
+    wait_vm(min(nk - 1 - kc, G_NST - 2) * G_NPW);
+    // a bare s_barrier: __syncthreads() would also drain every outstanding
+    // load (vmcnt 0) and with it the ring's look-ahead
+    asm volatile("s_barrier" ::: "memory");
+    const int st = kc % G_NST;
+    const char* xa = smem + st * G_STAGE + (wr * 128 + lr) * (GK * 2);
+    const char* ya = smem + st * G_STAGE + G_OP + (wc * 128 + lr) * (GK * 2);
+    vec a[2][4], b[2][4];
+    auto frags = [&](int so, int buf) {
 #pragma unroll
-    for (int s = 0; s < kKC / 16; ++s) {
-      vec a[2], b[2];
+      for (int i = 0; i < 4; ++i) a[buf][i] = *reinterpret_cast<const vec*>(ya + i * 32 * GK * 2 + so);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const vec*>(sy + (cw + 32 * i + lr) * kLS + 16 * s + 8 * lh);
+      for (int j = 0; j < 4; ++j) b[buf][j] = *reinterpret_cast<const vec*>(xa + j * 32 * GK * 2 + so);
+    };
+    frags(so0, 0);
+    if (kc + G_NST - 1 < nk) issue(kc + G_NST - 1, (kc + G_NST - 1) % G_NST);
+    frags(so1, 1);
+    // the first k16 step's products wait only for its own fragments; the
+    // second step's reads complete under them
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const vec*>(sx + (rw + 32 * j + lr) * kLS + 16 * s + 8 * lh);
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<InT>::run(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = MfmaOp<InT>::run(a[s2][i], b[s2][j], acc[i][j]);
     }
-    if (kc + 1 < nk) store(st ^ 1);
-    __syncthreads();
   }
+  __syncthreads();   // every wave is done with the ring before it holds the output
 
-  // D[m = c][n = r]: this lane holds output row r, four consecutive columns per group
-  constexpr int SS = kT + (sizeof(OutT) == 4 ? 4 : 8);
-  OutT* stg = reinterpret_cast<OutT*>(&smem[0][0][0]);
+  // acc[i][j] is D[m = c][n = r]: this lane holds output row
+  // r0 + 128 wr + 32 j + lr, four consecutive columns per register group.
+  // fp32 results go straight from the accumulators as 16-byte stores; fp16
+  // results are staged through LDS so that each global store is a full
+  // 16-byte piece of a row. Only tiles on the bottom or right edge mask
+  // (a uniform branch). Stores are streaming: the output is not read again
+  // here and would otherwise evict operand rows other tiles still need.
+  static_assert(sizeof(OutT) == 4 || __is_same(OutT, _Float16), "fp32 or fp16 output");
+  constexpr int SH = GT + 8;   // fp16 staging pitch (elements)
+  static_assert(GT * SH * 2 <= G_NST * G_STAGE, "output staging fits the ring");
+  const int rlim = static_cast<int>(min<int64_t>(R - r0, GT));        // valid rows in the tile
+  const int clim = static_cast<int>(min<int64_t>(C - c0, GT));
+  const int rstore = static_cast<int>(min<int64_t>(R_store - r0, GT));
+  const int cstore = static_cast<int>(min<int64_t>(C_store - c0, GT));
+  const bool edge = !kPart && (rlim < GT || clim < GT);
+  auto tile_val = [&](int i, int j, int g, int rt, int ct, bool masked) {
+    f32x4 v;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int e = 0; e < 4; ++e)
+      v[e] = (!masked || (rt < rlim && ct + e < clim)) ? acc[i][j][4 * g + e] : 0.f;
+    return v;
+  };
+  if constexpr (sizeof(OutT) == 4 || kPart) {
+    const int64_t PR = static_cast<int64_t>(n_tr) * GT, PC = static_cast<int64_t>(n_tc) * GT;
+    auto put = [&](bool masked) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = rw + 32 * j + lr;
-        const int c = cw + 32 * i + 8 * g + 4 * lh;
-        if constexpr (sizeof(OutT) == 4) {
-          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                     acc[i][j][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(stg + r * SS + c) = v;
-        } else {
-          half4 v = {static_cast<_Float16>(acc[i][j][4 * g]),
-                     static_cast<_Float16>(acc[i][j][4 * g + 1]),
-                     static_cast<_Float16>(acc[i][j][4 * g + 2]),
-                     static_cast<_Float16>(acc[i][j][4 * g + 3])};
-          *reinterpret_cast<half4*>(stg + r * SS + c) = v;
-        }
-      }
-  __syncthreads();
-  constexpr int EPC = 16 / sizeof(OutT);   // elements per 16-byte piece
-  constexpr int CPR = kT / EPC;            // pieces per row
-  OutT* base = out + (r0 / kT) * rt_stride + (c0 / kT) * ct_stride;
-  for (int c = tid; c < kT * CPR; c += 256) {
-    const int row = c / CPR, cc = (c % CPR) * EPC;
-    if (r0 + row >= R_store || c0 + cc >= C_store) continue;
-    *reinterpret_cast<u32x4*>(base + row * ldo + cc) =
-        *reinterpret_cast<const u32x4*>(stg + row * SS + cc);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int rt = wr * 128 + 32 * j + lr, ct = wc * 128 + 32 * i + 8 * g + 4 * lh;
+            const f32x4 v = tile_val(i, j, g, rt, ct, masked);
+            const int64_t r = r0 + rt, c = c0 + ct;
+            if constexpr (kPart) {
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(part + (blockIdx.y * PR + r) * PC + c));
+            } else if (rt < rstore && ct < cstore) {
+              __builtin_nontemporal_store(
+                  v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (r / 128) * rt_stride +
+                                              (r % 128) * ldo + (c / 128) * ct_stride + c % 128));
+            }
+          }
+    };
+    if (edge) put(true);
+    else put(false);
+  } else {
+    _Float16* sth = reinterpret_cast<_Float16*>(smem);
+    auto stage = [&](bool masked) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int rt = wr * 128 + 32 * j + lr, ct = wc * 128 + 32 * i + 8 * g + 4 * lh;
+            const f32x4 v = tile_val(i, j, g, rt, ct, masked);
+            const half4 hv = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]),
+                              static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
+            *reinterpret_cast<half4*>(sth + rt * SH + ct) = hv;
+          }
+    };
+    if (edge) stage(true);
+    else stage(false);
+    __syncthreads();
+    for (int pc = tid; pc < GT * (GT / 8); pc += 256) {
+      const int rt = pc / (GT / 8), ct = (pc % (GT / 8)) * 8;
+      const int64_t r = r0 + rt, c = c0 + ct;
+      if (rt < rstore && ct < cstore)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sth + rt * SH + ct),
+                                    reinterpret_cast<u32x4*>(out + (r / 128) * rt_stride +
+                                                             (r % 128) * ldo +
+                                                             (c / 128) * ct_stride + c % 128));
+    }
   }
+}
+
+// out(r, c) = sum_z part[z][r][c] for r < R_store, c < C_store (0 past R or
+// C), in the tiled layout of launch_gemm_nt; four columns per thread, the
+// splits summed in order (deterministic).
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t PR, int64_t PC,
+                     float* __restrict__ out, int64_t ldo, int64_t rt_stride, int64_t ct_stride,
+                     int64_t R, int64_t C, int64_t R_store, int64_t C_store) {
+  const int64_t cq = C_store / 4, n = R_store * cq;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = e / cq, c = (e % cq) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(part + (z * PR + r) * PC + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (r >= R || c + q >= C) acc[q] = 0.f;
+    *reinterpret_cast<f32x4*>(out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride +
+                              c % 128) = acc;
+  }
+}
+
+int gemm_splits(int64_t R_store, int64_t C_store, int64_t K) {
+  const int64_t tiles = ((R_store + GT - 1) / GT) * ((C_store + GT - 1) / GT);
+  int s = 1;
+  while (tiles * s < G_MIN_BLOCKS && s < 8 && K % (2 * s * GK) == 0 && K / (2 * s) >= 8 * GK) s *= 2;
+  return s;
 }
 
 template <typename OutT>
@@ -243,30 +387,61 @@ mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, i
   return check_launch(name);
 }
 
+int64_t gemm_splitk_bytes(int64_t R_store, int64_t C_store, int64_t K) {
+  const int sp = gemm_splits(R_store, C_store, K);
+  if (sp == 1) return 0;
+  return static_cast<int64_t>(sp) * ((R_store + GT - 1) / GT) * GT * ((C_store + GT - 1) / GT) * GT * 4;
+}
+
 mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
                           int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
                           int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
-                          Elem out_t, hipStream_t st, const char* name) {
-  if (K % kKC != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: K=%lld not a multiple of 64", name, (long long)K);
+                          Elem out_t, hipStream_t st, const char* name, float* part,
+                          int64_t part_bytes) {
+  if (K % GK != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: K=%lld not a multiple of 32", name, (long long)K);
   if (C_store % 8 != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: C_store not a multiple of 8", name);
-  const int64_t gr = (R_store + kT - 1) / kT, gc = (C_store + kT - 1) / kT;
-  if (gr > 65535) return fail(MLA_ERR_UNSUPPORTED, "%s: too many row tiles", name);
-  dim3 grid(static_cast<unsigned>(gc), static_cast<unsigned>(gr));
+  const int64_t n_tr = (R_store + GT - 1) / GT, n_tc = (C_store + GT - 1) / GT;
+  // every tile must hold a valid row of X and of Y (loads clamp to them)
+  if (R > 0 && C > 0 && (n_tr != (R + GT - 1) / GT || n_tc != (C + GT - 1) / GT))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: stored extent reaches a tile past the operands", name);
+  if (ldx >= (int64_t(1) << 23) || ldy >= (int64_t(1) << 23) || n_tr * n_tc >= (int64_t(1) << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: operand too wide", name);
+  int sp = out_t == Elem::F32 ? gemm_splits(R_store, C_store, K) : 1;
+  if (sp > 1 && (part == nullptr || part_bytes < gemm_splitk_bytes(R_store, C_store, K))) sp = 1;
+  dim3 grid(static_cast<unsigned>(n_tr * n_tc), static_cast<unsigned>(sp));
+  float* pp = sp > 1 ? part : nullptr;
+  const int64_t kl = K / sp;
+  const int ntr = static_cast<int>(n_tr), ntc = static_cast<int>(n_tc);
   KernelTimer kt(name, st);
-  if (in_t == Elem::BF16 && out_t == Elem::F16)
-    hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16>), grid, dim3(256), 0, st,
+  if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false>), grid, dim3(256), 0, st,
                        static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
-                       C, K, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
+                       C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
+                       C_store, nullptr, ntr, ntc);
+  else if (in_t == Elem::F16 && out_t == Elem::F32 && sp == 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false>), grid, dim3(256), 0, st,
+                       static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                       ldy, C, kl, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store,
+                       C_store, nullptr, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F32)
-    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true>), grid, dim3(256), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
-                       ldy, C, K, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
-  else if (in_t == Elem::F16 && out_t == Elem::F16)
-    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16>), grid, dim3(256), 0, st,
+                       ldy, C, kl, static_cast<float*>(nullptr), ldo, rt_stride, ct_stride,
+                       R_store, C_store, pp, ntr, ntc);
+  else if (in_t == Elem::F16 && out_t == Elem::F16 && sp == 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16, false>), grid, dim3(256), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
-                       ldy, C, K, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store, C_store);
+                       ldy, C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
+                       C_store, nullptr, ntr, ntc);
   else
     return fail(MLA_ERR_UNSUPPORTED, "%s: GEMM type combination not built", name);
+  if (sp > 1) {
+    const int64_t n = R_store * (C_store / 4);
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 16384));
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(g), dim3(256), 0, st, part, sp, n_tr * GT,
+                       n_tc * GT, static_cast<float*>(out), ldo, rt_stride, ct_stride, R, C,
+                       R_store, C_store);
+  }
   return check_launch(name);
 }
 

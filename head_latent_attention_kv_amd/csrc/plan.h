@@ -44,11 +44,13 @@ struct BwdLayout {
   // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128],
   //             dV = its transpose [2*n_h*128][Kpad], dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
-  // fast path only (fp16): keys transposed [n_h][192][Kpad], V key-major
+  // fast path only (fp16): keys transposed [n_h][192][Kpad] (unused: the
+  // backward reads K^T fragments as transposed LDS reads of K), V key-major
   // [n_h][Kpad][128], [W_UK | W_UV] [d_c][2*n_h*128], c_kv^T [d_c][Kpad],
   // q and dout per head: [n_h][S_pad][.] and [n_h][.][S_pad]
   int64_t KfullT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
   int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
+  int64_t gpart;  // fast path: split-K partial sums of the gradient GEMMs (fp32)
   int64_t total;
 };
 
@@ -97,6 +99,9 @@ mla_status generic_bwd(const Plan& p, const void* dout, const void* q, const voi
 mla_status zero_fill(float* p, int64_t n, hipStream_t st);
 
 // ---- fast path (fast_*.hip)
+// Bytes of fp32 partial sums launch_gemm_nt uses to split K for an fp32
+// output of R_store x C_store (0 when it does not split).
+int64_t gemm_splitk_bytes(int64_t R_store, int64_t C_store, int64_t K);
 mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st);
