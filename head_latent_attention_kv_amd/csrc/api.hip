@@ -121,9 +121,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.W16 = take(static_cast<int64_t>(p.d_c) * 2 * nk * 2);
     L.ckvT = take(static_cast<int64_t>(p.d_c) * p.Kpad * 2);
     L.Qn = take(p.n_h * S_pad * 192 * 2);
-    L.Qt = take(p.n_h * S_pad * 192 * 2);
     L.dOn = take(p.n_h * S_pad * 128 * 2);
-    L.dOt = take(p.n_h * S_pad * 128 * 2);
     L.D = take(p.n_h * S_pad * 4);
     L.dK = take(p.Kpad * 2 * nk * 2);
     L.dV = take(p.Kpad * 2 * nk * 2);

@@ -3,8 +3,8 @@
 // rebuilt from the latent, so their gradients flow back into c_kv, k_rope,
 // W_UK and W_UV).
 //
-//   prep      D = rowsum(dout * out); q and dout to fp16, per head, both
-//             row-major [row][dim] and column-major [dim][row]
+//   prep      D = rowsum(dout * out); q and dout to fp16, per head,
+//             row-major [row][dim]
 //   rebuild   K_nope and V again (fp16), in the layouts the kernels read
 //   dK, dV    key-outer, two launches: each wave owns 32 keys and steps
 //             over query rows; S = Q K^T lands with lanes on keys, so P and
@@ -44,19 +44,16 @@ __device__ __forceinline__ void work_item(int bid, int n_h, int n_t, int* h, int
 
 // ------------------------------------------------------------------ prep
 // grid (ceil(S_loc/64), n_h). D[h][i] = dout[i,h,:] . out[i,h,:]; fp16 copies
-// Qn[h][i][192], Qt[h][192][i], dOn[h][i][128], dOt[h][128][i] (rows past
-// S_loc are zero); and per 32-row block the row info the dK/dV kernel reads:
+// Qn[h][i][192] and dOn[h][i][128] (rows past S_loc are zero); and per
+// 32-row block the row info the dK/dV kernels read:
 // info[h][i/32] = {lse*log2(e) [32], D [32], sample start [32], position [32]}
 // (rows past S_loc: start INT32_MAX, position -1, so they see no key).
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                 const float* __restrict__ out, const float* __restrict__ lse,
                 const int32_t* __restrict__ cu, float* __restrict__ D, _Float16* __restrict__ Qn,
-                _Float16* __restrict__ Qt, _Float16* __restrict__ dOn, _Float16* __restrict__ dOt,
-                uint32_t* __restrict__ info, int n_h, int n_seqs, int64_t S_loc, int64_t S_pad,
-                int64_t q_offset) {
-  constexpr int TS = DQK + 2;  // LDS row stride (halfs)
-  __shared__ _Float16 t[64 * TS];
+                _Float16* __restrict__ dOn, uint32_t* __restrict__ info, int n_h, int n_seqs,
+                int64_t S_loc, int64_t S_pad, int64_t q_offset) {
   const int h = blockIdx.y;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -82,14 +79,12 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
       blk[96 + r] = ok ? static_cast<uint32_t>(q_offset + i) : 0xffffffffu;
     }
   }
-  // q then dout: natural rows to global and LDS, then the transpose
+  // q then dout, 16 bytes per thread
   for (int pass = 0; pass < 2; ++pass) {
     const int width = pass == 0 ? DQK : DV;
     const uint16_t* src = pass == 0 ? q : dout;
     _Float16* nat = (pass == 0 ? Qn : dOn) + static_cast<int64_t>(h) * S_pad * width;
-    _Float16* tr = (pass == 0 ? Qt : dOt) + static_cast<int64_t>(h) * width * S_pad;
     const int chunks = width / 8;
-    __syncthreads();
     for (int e = tid; e < 64 * chunks; e += 256) {
       const int row = e / chunks, ch = e % chunks;
       const int64_t i = i0 + row;
@@ -102,16 +97,6 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
         for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
       }
       *reinterpret_cast<half8*>(nat + (i0 + row) * width + ch * 8) = v;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) t[row * TS + ch * 8 + k] = v[k];
-    }
-    __syncthreads();
-    for (int e = tid; e < width * 8; e += 256) {
-      const int dim = e / 8, qc = e % 8;
-      half8 v;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = t[(qc * 8 + k) * TS + dim];
-      *reinterpret_cast<half8*>(tr + dim * S_pad + i0 + qc * 8) = v;
     }
   }
 }
@@ -137,22 +122,22 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
 // wave instruction (1 KiB) lies in one region.
 constexpr int KW = 256;     // keys per workgroup (8 waves x 32)
 constexpr int QB = 64;      // query rows per step
-constexpr int QN_ROW = DQK * 2 + 16, DON_ROW = DV * 2 + 16, QT_ROW = QB * 2 + 16;  // 400, 272, 144
-// stage (bytes), dK launch: Qn [64 rows] | dOn [64] | Qt [192 dims] | row info
-//                dV launch: Qn [64 rows] | dOt [128 dims] | row info
-constexpr int SK_QN = 0, SK_DON = 25 * 1024, SK_QT = 42 * 1024, SK_INFO = 69 * 1024,
-              SK_BYTES = 70 * 1024;
-constexpr int SV_QN = 0, SV_DOT = 25 * 1024, SV_INFO = 43 * 1024, SV_BYTES = 44 * 1024;
-static_assert(SK_DON >= QB * QN_ROW && SK_QT - SK_DON >= QB * DON_ROW &&
-              SK_INFO - SK_QT >= DQK * QT_ROW && SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
-static_assert(SV_QN == SK_QN && SV_DOT == SK_DON, "Qn is the first region of both stages");
-static_assert(SV_DOT >= QB * QN_ROW && SV_INFO - SV_DOT >= DV * QT_ROW &&
-              SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
+// Row strides: Q 400 B; dO 272 B where it is read row-wise (dP = dO V^T in
+// the dK launch) and 304 B where it is read transposed (dV^T += dO^T P): a
+// transposed read of rows 256 or 272 B apart runs at half rate.
+constexpr int QN_ROW = DQK * 2 + 16, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 48;  // 400, 272, 304
+// stage (bytes): Qn [64 rows] | dOn [64 rows] | row info. Q^T and dO^T
+// fragments (the A operands of dK^T and dV^T) are transposed reads of them.
+constexpr int S_QN = 0, S_DON = 25 * 1024;
+constexpr int SK_INFO = 42 * 1024, SK_BYTES = 43 * 1024;
+constexpr int SV_INFO = 44 * 1024, SV_BYTES = 45 * 1024;
+static_assert(S_DON >= QB * QN_ROW && SK_INFO - S_DON >= QB * DONK_ROW &&
+              SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
+static_assert(SV_INFO - S_DON >= QB * DONV_ROW && SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
 
 template <bool kDK>
 __global__ void __launch_bounds__(512)
-attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ Qt,
-                    const _Float16* __restrict__ dOn, const _Float16* __restrict__ dOt,
+attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
                     const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                     const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
                     _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
@@ -160,6 +145,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
                     int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
   constexpr int BYTES = kDK ? SK_BYTES : SV_BYTES;
   constexpr int INFO = kDK ? SK_INFO : SV_INFO;
+  constexpr int DON_ROW = kDK ? DONK_ROW : DONV_ROW;
   constexpr int PIECES = BYTES / 1024;          // DMA wave instructions per stage
   constexpr int NPW = (PIECES + 7) / 8;         // per wave
   __shared__ __attribute__((aligned(1024))) char smem[2 * BYTES];
@@ -207,26 +193,20 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
   // row qb; a region's pad slots reload a valid element and are never read
   const _Float16* Qn_h = Qn + static_cast<int64_t>(h) * S_pad * DQK;
   const _Float16* dOn_h = dOn + static_cast<int64_t>(h) * S_pad * DV;
-  const _Float16* Qt_h = Qt + static_cast<int64_t>(h) * DQK * S_pad;
-  const _Float16* dOt_h = dOt + static_cast<int64_t>(h) * DV * S_pad;
   const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / 32) * 128;
   int doff[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
     const int o = (w * NPW + j) * 1024 + lane * 16;
     int off = 0;
-    if (o < SK_DON) {   // Qn (same place in both layouts)
+    if (o < S_DON) {
       const int row = min(o / QN_ROW, QB - 1), pc = min((o % QN_ROW) >> 4, DQK / 8 - 1);
       off = row * DQK + pc * 8;
     } else if (o >= INFO) {
       off = min((o - INFO) >> 2, 2 * 128 - 4);   // 4-byte elements, 128 per 32 rows
-    } else if (kDK && o < SK_QT) {
-      const int oo = o - SK_DON, row = min(oo / DON_ROW, QB - 1), pc = min((oo % DON_ROW) >> 4, DV / 8 - 1);
+    } else {
+      const int oo = o - S_DON, row = min(oo / DON_ROW, QB - 1), pc = min((oo % DON_ROW) >> 4, DV / 8 - 1);
       off = row * DV + pc * 8;
-    } else {            // Qt (dK) or dOt (dV): rows are dims, columns the block's rows
-      const int oo = o - (kDK ? SK_QT : SV_DOT);
-      const int row = min(oo / QT_ROW, (kDK ? DQK : DV) - 1), pc = min((oo % QT_ROW) >> 4, QB / 8 - 1);
-      off = row * S_pad + pc * 8;
     }
     doff[j] = off;
   }
@@ -241,10 +221,9 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
         int off = doff[j];
         asm volatile("" : "+v"(off));
         const void* src;
-        if (I * 1024 < SK_DON) src = Qn_h + static_cast<int64_t>(qb) * DQK + off;
+        if (I * 1024 < S_DON) src = Qn_h + static_cast<int64_t>(qb) * DQK + off;
         else if (I * 1024 >= INFO) src = info_h + (qb / 32) * 128 + off;
-        else if (kDK && I * 1024 < SK_QT) src = dOn_h + static_cast<int64_t>(qb) * DV + off;
-        else src = (kDK ? Qt_h : dOt_h) + qb + off;
+        else src = dOn_h + static_cast<int64_t>(qb) * DV + off;
         lds_dma16(src, sbase + I * 1024);
       }
     }
@@ -258,9 +237,10 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
 
   const int qrow = swap23(lr);   // A-operand row loaded by this lane
-  const int a_qn = SK_QN + qrow * QN_ROW + lh * 16;
-  const int a_don = SK_DON + qrow * DON_ROW + lh * 16;
-  const int a_t = (kDK ? SK_QT : SV_DOT) + lr * QT_ROW + lh * 16;   // Q^T or dO^T rows
+  const int a_qn = S_QN + qrow * QN_ROW + lh * 16;
+  const int a_don = S_DON + qrow * DON_ROW + lh * 16;
+  // Q^T (dK) or dO^T (dV) fragments: transposed reads of the row tiles
+  const int a_t = kDK ? S_QN + tr_lane_offset(lane, QN_ROW) : S_DON + tr_lane_offset(lane, DON_ROW);
 
   if (nq > 0) issue(qb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -355,7 +335,9 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
         constexpr int NM = 2 * NACC;
         auto frag = [&](int k) {
           const int ks = k / NACC, dm = k % NACC;
-          return *reinterpret_cast<const half8*>(base + a_t + dm * 32 * QT_ROW + (2 * mt + ks) * 32);
+          // dims 32 dm + lr, rows 32 mt + 16 ks + 8 lh + j
+          constexpr int TROW = kDK ? QN_ROW : DONV_ROW;
+          return frag_tr<TROW>(base + a_t + (32 * mt + 16 * ks) * TROW + 32 * dm * 2);
         };
         half8 fa[3];
         fa[0] = frag(0);
@@ -627,9 +609,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   _Float16* W16 = reinterpret_cast<_Float16*>(at(L.W16));
   _Float16* ckvT = reinterpret_cast<_Float16*>(at(L.ckvT));
   _Float16* Qn = reinterpret_cast<_Float16*>(at(L.Qn));
-  _Float16* Qt = reinterpret_cast<_Float16*>(at(L.Qt));
   _Float16* dOn = reinterpret_cast<_Float16*>(at(L.dOn));
-  _Float16* dOt = reinterpret_cast<_Float16*>(at(L.dOt));
   float* D = reinterpret_cast<float*>(at(L.D));
   _Float16* dKV = reinterpret_cast<_Float16*>(at(L.dK));
   _Float16* dKVT = reinterpret_cast<_Float16*>(at(L.dV));
@@ -657,7 +637,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     KernelTimer kt("bwd_prep", st);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(S_pad / 64), p.n_h), dim3(256),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       out, lse, cu_dev, D, Qn, Qt, dOn, dOt, info, p.n_h, p.n_seqs, p.S_loc,
+                       out, lse, cu_dev, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
                        S_pad, p.q_offset);
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
@@ -667,14 +647,14 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     const unsigned grid = static_cast<unsigned>(n_kt * p.n_h);
     {
       KernelTimer kt("attn_bwd_dk", st);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<true>, dim3(grid), dim3(512), 0, st, Qn, Qt, dOn, dOt,
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<true>, dim3(grid), dim3(512), 0, st, Qn, dOn,
                          info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
                          q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
     }
     if ((s = check_launch("attention backward dK")) != MLA_OK) return s;
     {
       KernelTimer kt("attn_bwd_dv", st);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<false>, dim3(grid), dim3(512), 0, st, Qn, Qt, dOn, dOt,
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<false>, dim3(grid), dim3(512), 0, st, Qn, dOn,
                          info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
                          q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
     }

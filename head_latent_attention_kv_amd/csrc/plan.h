@@ -44,10 +44,10 @@ struct BwdLayout {
   // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128],
   //             dV = its transpose [2*n_h*128][Kpad], dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
-  // fast path only (fp16): keys transposed [n_h][192][Kpad] (unused: the
-  // backward reads K^T fragments as transposed LDS reads of K), V key-major
-  // [n_h][Kpad][128], [W_UK | W_UV] [d_c][2*n_h*128], c_kv^T [d_c][Kpad],
-  // q and dout per head: [n_h][S_pad][.] and [n_h][.][S_pad]
+  // fast path only (fp16): V key-major [n_h][Kpad][128], [W_UK | W_UV]
+  // [d_c][2*n_h*128], c_kv^T [d_c][Kpad], q and dout per head [n_h][S_pad][.].
+  // KfullT, Qt and dOt stay -1: the kernels read those transposes from the
+  // row-major tiles with transposed LDS reads.
   int64_t KfullT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
   int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
   int64_t gpart;  // fast path: split-K partial sums of the gradient GEMMs (fp32)
