@@ -123,14 +123,14 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
 constexpr int KW = 256;     // keys per workgroup (8 waves x 32)
 constexpr int QB = 64;      // query rows per step
 // Row strides: Q 400 B; dO 272 B where it is read row-wise (dP = dO V^T in
-// the dK launch) and 304 B where it is read transposed (dV^T += dO^T P): a
+// the dK launch) and 320 B where it is read transposed (dV^T += dO^T P): a
 // transposed read of rows 256 or 272 B apart runs at half rate.
-constexpr int QN_ROW = DQK * 2 + 16, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 48;  // 400, 272, 304
+constexpr int QN_ROW = DQK * 2 + 16, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 64;  // 400, 272, 320
 // stage (bytes): Qn [64 rows] | dOn [64 rows] | row info. Q^T and dO^T
 // fragments (the A operands of dK^T and dV^T) are transposed reads of them.
 constexpr int S_QN = 0, S_DON = 25 * 1024;
 constexpr int SK_INFO = 42 * 1024, SK_BYTES = 43 * 1024;
-constexpr int SV_INFO = 44 * 1024, SV_BYTES = 45 * 1024;
+constexpr int SV_INFO = 45 * 1024, SV_BYTES = 46 * 1024;
 static_assert(S_DON >= QB * QN_ROW && SK_INFO - S_DON >= QB * DONK_ROW &&
               SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
 static_assert(SV_INFO - S_DON >= QB * DONV_ROW && SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
