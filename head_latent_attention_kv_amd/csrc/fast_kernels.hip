@@ -9,6 +9,8 @@
 // full 16-byte row piece. Thin outputs (the gradients of c_kv and of the
 // weights) split K over more workgroups and sum the fp32 partials in a fixed
 // order afterwards.
+#include <stdlib.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -23,19 +25,22 @@ constexpr int GK = 32;                  // k per chunk: one 64-byte LDS row per 
 constexpr int G_OP = GT * GK * 2;       // one operand's tile (16 KiB)
 constexpr int G_STAGE = 2 * G_OP;       // X and Y tiles
 constexpr int G_NST = 5;                // stages in the ring: four chunks in flight
-constexpr int G_NPW = G_OP / 2048;      // DMA pieces per wave and chunk (two waves per operand): 8
+constexpr int G_PIECES = 2 * G_OP / 1024;  // DMA wave instructions per chunk: 32
 constexpr int G_MIN_BLOCKS = 512;       // split K until the grid has this many workgroups
 static_assert(G_NST * G_STAGE <= 160 * 1024, "ring fits the LDS");
-static_assert((G_NST - 2) * G_NPW <= 63, "outstanding DMA count fits vmcnt");
+static_assert((G_NST - 2) * G_PIECES / 4 <= 63, "outstanding DMA count fits vmcnt");
 
 // Wait until at most n of this wave's vector-memory operations are
-// outstanding (n in {0, 8, 16, 24}; gfx9 encoding of s_waitcnt: vmcnt bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+// outstanding (n a multiple of 4 up to 24; gfx9 encoding of s_waitcnt:
+// vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
     default: __builtin_amdgcn_s_waitcnt(0x4F78); break;
   }
 }
@@ -68,13 +73,17 @@ __device__ __forceinline__ void gemm_tile(int bid, int n_tr, int n_tc, int* tr, 
 // written as 0. With kPart, the tile goes unmasked to part[blockIdx.y][r][c]
 // (fp32) for a split-K reduction; otherwise to `out` in the tiled layout of
 // launch_gemm_nt.
-template <typename InT, typename OutT, bool kPart>
-__global__ void __launch_bounds__(256)
+template <typename InT, typename OutT, bool kPart, int kW>
+__global__ void __launch_bounds__(kW * 64)
 gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __restrict__ Y,
                int64_t ldy, int64_t C, int64_t k_len, OutT* __restrict__ out, int64_t ldo,
                int64_t rt_stride, int64_t ct_stride, int64_t R_store, int64_t C_store,
                float* __restrict__ part, int n_tr, int n_tc) {
   typedef typename MfmaOp<InT>::vec vec;
+  static_assert(kW == 4 || kW == 8, "four waves of 128x128 or eight of 128x64");
+  constexpr int NI = kW == 8 ? 2 : 4;   // 32-column tiles per wave
+  constexpr int NPW = G_PIECES / kW;    // DMA pieces per wave and chunk
+  constexpr int HW = kW / 2;            // waves per operand (DMA) and per row half
   // the ring, reused afterwards to stage an fp16 output tile
   __shared__ __attribute__((aligned(1024))) char smem[G_NST * G_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -84,29 +93,28 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   gemm_tile(blockIdx.x, n_tr, n_tc, &tr, &tc);
   const int64_t r0 = static_cast<int64_t>(tr) * GT, c0 = static_cast<int64_t>(tc) * GT;
   const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * k_len;
-  const int wr = w >> 1, wc = w & 1;   // this wave's 128x128 quarter
+  const int wr = w / HW, wc = w % HW;  // rows 128 wr .., columns 32 NI wc ..
   const bool live = R > 0 && C > 0;
 
-  // waves 0-1 fill the X tile, 2-3 the Y tile (18 pieces of 1 KiB each); a
-  // row's pad slot reloads a valid element and is never read back
-  const bool is_x = w < 2;
+  // the first half of the waves fill the X tile, the second the Y tile
+  const bool is_x = w < HW;
   const int64_t ld = is_x ? ldx : ldy;
   const InT* src = live ? (is_x ? X + r0 * ldx : Y + c0 * ldy) + kbeg : nullptr;
   const int last = static_cast<int>((is_x ? R - r0 : C - c0) - 1);   // >= 0 for live tiles
   // piece p of an operand tile = rows 16p .. 16p + 15; lane l fills row
   // 16p + l / 4, physical slot l % 4, which holds k-slot (l % 4) ^ ((row / 4) % 4)
-  int doff[G_NPW];
+  int doff[NPW];
 #pragma unroll
-  for (int j = 0; j < G_NPW; ++j) {
-    const int row = 16 * ((w & 1) * G_NPW + j) + (lane >> 2);
+  for (int j = 0; j < NPW; ++j) {
+    const int row = 16 * ((w % HW) * NPW + j) + (lane >> 2);
     const int slot = (lane & 3) ^ ((row >> 2) & 3);
     doff[j] = min(row, last) * static_cast<int>(ld) + slot * 8;
   }
   auto issue = [&](int c, int st) {
-    char* dst = smem + st * G_STAGE + (is_x ? 0 : G_OP) + (w & 1) * G_NPW * 1024;
+    char* dst = smem + st * G_STAGE + (is_x ? 0 : G_OP) + (w % HW) * NPW * 1024;
     const InT* s0 = src + static_cast<int64_t>(c) * GK;
 #pragma unroll
-    for (int j = 0; j < G_NPW; ++j) {
+    for (int j = 0; j < NPW; ++j) {
       // opaque to the optimizer, so no 64-bit address per piece is hoisted
       int off = doff[j];
       asm volatile("" : "+v"(off));
@@ -114,9 +122,9 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[NI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -125,43 +133,65 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   // fragment rows are wave base + 32 i + lr, so (row / 4) % 4 = (lr / 4) % 4
   const int so0 = ((0 + lh) ^ ((lr >> 2) & 3)) * 16, so1 = ((2 + lh) ^ ((lr >> 2) & 3)) * 16;
   const int nk = live ? static_cast<int>(k_len / GK) : 0;
+  // fragments: [k16 step of the chunk][tile]
+  vec a[2][NI], b[2][4];
+  auto frags = [&](int kc, int step) {
+    const int st = kc % G_NST, so = step ? so1 : so0;
+    const char* xa = smem + st * G_STAGE + (wr * 128 + lr) * (GK * 2) + so;
+    const char* ya = smem + st * G_STAGE + G_OP + (wc * 32 * NI + lr) * (GK * 2) + so;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[step][i] = *reinterpret_cast<const vec*>(ya + i * 32 * GK * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[step][j] = *reinterpret_cast<const vec*>(xa + j * 32 * GK * 2);
+  };
+  // half 0 / 1: the first / second half of the column tiles
+  auto products = [&](int step, int half) {
+#pragma unroll
+    for (int i = half * NI / 2; i < (half + 1) * NI / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = MfmaOp<InT>::run(a[step][i], b[step][j], acc[i][j]);
+  };
+  // Each chunk runs as two steps of 16 products. The wait, the barrier and
+  // the next DMA issue sit between the steps, and each step's fragment reads
+  // are issued halfway through the step before it: the LDS-DMA loads make
+  // the compiler's waits before the products conservative (all LDS reads
+  // done), so the reads must have completed by then anyway. Before chunk
+  // kc + 1 is read, this wave's pieces of it have landed once at most the
+  // later chunks already issued are outstanding, and the barrier makes every
+  // wave's pieces visible; it also shows that every wave has read all of
+  // chunk kc - 1, whose stage the issue refills.
   for (int c = 0; c < min(nk, G_NST - 1); ++c) issue(c, c);
-  for (int kc = 0; kc < nk; ++kc) {
-    // this wave's pieces of chunk kc have landed once at most the later
-    // chunks already issued are outstanding; the barrier then makes every
-    // wave's pieces visible and shows that every wave is done with the
-    // stage the next issue refills
-    wait_vm(min(nk - 1 - kc, G_NST - 2) * G_NPW);
+  if (nk > 0) {
+    wait_vm(min(nk - 1, G_NST - 2) * NPW);
     // a bare s_barrier: __syncthreads() would also drain every outstanding
     // load (vmcnt 0) and with it the ring's look-ahead
     asm volatile("s_barrier" ::: "memory");
-    const int st = kc % G_NST;
-    const char* xa = smem + st * G_STAGE + (wr * 128 + lr) * (GK * 2);
-    const char* ya = smem + st * G_STAGE + G_OP + (wc * 128 + lr) * (GK * 2);
-    vec a[2][4], b[2][4];
-    auto frags = [&](int so, int buf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[buf][i] = *reinterpret_cast<const vec*>(ya + i * 32 * GK * 2 + so);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[buf][j] = *reinterpret_cast<const vec*>(xa + j * 32 * GK * 2 + so);
-    };
-    frags(so0, 0);
-    if (kc + G_NST - 1 < nk) issue(kc + G_NST - 1, (kc + G_NST - 1) % G_NST);
-    frags(so1, 1);
-    // the first k16 step's products wait only for its own fragments; the
-    // second step's reads complete under them
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = MfmaOp<InT>::run(a[s2][i], b[s2][j], acc[i][j]);
+    frags(0, 0);
+  }
+  for (int kc = 0; kc < nk; ++kc) {
+    products(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(kc, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = kc + 1 < nk;
+    if (more) {
+      wait_vm(min(nk - 2 - kc, G_NST - 3) * NPW);
+      asm volatile("s_barrier" ::: "memory");
+      if (kc + G_NST - 1 < nk) issue(kc + G_NST - 1, (kc + G_NST - 1) % G_NST);
     }
+    products(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) frags(kc + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    products(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();   // every wave is done with the ring before it holds the output
 
   // acc[i][j] is D[m = c][n = r]: this lane holds output row
-  // r0 + 128 wr + 32 j + lr, four consecutive columns per register group.
+  // r0 + 128 wr + 32 j + lr, columns c0 + 32 NI wc + 32 i + 8 g + 4 lh + e.
   // fp32 results go straight from the accumulators as 16-byte stores; fp16
   // results are staged through LDS so that each global store is a full
   // 16-byte piece of a row. Only tiles on the bottom or right edge mask
@@ -186,12 +216,12 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
     const int64_t PR = static_cast<int64_t>(n_tr) * GT, PC = static_cast<int64_t>(n_tc) * GT;
     auto put = [&](bool masked) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int rt = wr * 128 + 32 * j + lr, ct = wc * 128 + 32 * i + 8 * g + 4 * lh;
+            const int rt = wr * 128 + 32 * j + lr, ct = wc * 32 * NI + 32 * i + 8 * g + 4 * lh;
             const f32x4 v = tile_val(i, j, g, rt, ct, masked);
             const int64_t r = r0 + rt, c = c0 + ct;
             if constexpr (kPart) {
@@ -209,12 +239,12 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
     _Float16* sth = reinterpret_cast<_Float16*>(smem);
     auto stage = [&](bool masked) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int rt = wr * 128 + 32 * j + lr, ct = wc * 128 + 32 * i + 8 * g + 4 * lh;
+            const int rt = wr * 128 + 32 * j + lr, ct = wc * 32 * NI + 32 * i + 8 * g + 4 * lh;
             const f32x4 v = tile_val(i, j, g, rt, ct, masked);
             const half4 hv = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]),
                               static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
@@ -224,7 +254,7 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
     if (edge) stage(true);
     else stage(false);
     __syncthreads();
-    for (int pc = tid; pc < GT * (GT / 8); pc += 256) {
+    for (int pc = tid; pc < GT * (GT / 8); pc += kW * 64) {
       const int rt = pc / (GT / 8), ct = (pc % (GT / 8)) * 8;
       const int64_t r = r0 + rt, c = c0 + ct;
       if (rt < rstore && ct < cstore)
@@ -255,6 +285,16 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t PR, int
     *reinterpret_cast<f32x4*>(out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride +
                               c % 128) = acc;
   }
+}
+
+// Waves per GEMM workgroup: 8 (128x64 each, two per SIMD, the default) or 4
+// (128x128 each); MLA_LAGA_GEMM_WAVES overrides it.
+int gemm_waves() {
+  static const int v = [] {
+    const char* e = getenv("MLA_LAGA_GEMM_WAVES");
+    return e && atoi(e) == 4 ? 4 : 8;
+  }();
+  return v;
 }
 
 int gemm_splits(int64_t R_store, int64_t C_store, int64_t K) {
@@ -413,23 +453,46 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
   const int64_t kl = K / sp;
   const int ntr = static_cast<int>(n_tr), ntc = static_cast<int>(n_tc);
   KernelTimer kt(name, st);
-  if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
-    hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false>), grid, dim3(256), 0, st,
+  if (gemm_waves() == 4) {
+    if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
+      hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false, 4>), grid, dim3(256), 0, st,
+                         static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
+                         C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
+                         C_store, nullptr, ntr, ntc);
+    else if (in_t == Elem::F16 && out_t == Elem::F32 && sp == 1)
+      hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false, 4>), grid, dim3(256), 0, st,
+                         static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                         ldy, C, kl, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store,
+                         C_store, nullptr, ntr, ntc);
+    else if (in_t == Elem::F16 && out_t == Elem::F32)
+      hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true, 4>), grid, dim3(256), 0, st,
+                         static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                         ldy, C, kl, static_cast<float*>(nullptr), ldo, rt_stride, ct_stride,
+                         R_store, C_store, pp, ntr, ntc);
+    else if (in_t == Elem::F16 && out_t == Elem::F16 && sp == 1)
+      hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16, false, 4>), grid, dim3(256), 0, st,
+                         static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                         ldy, C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
+                         C_store, nullptr, ntr, ntc);
+    else
+      return fail(MLA_ERR_UNSUPPORTED, "%s: GEMM type combination not built", name);
+  } else if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
                        C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
                        C_store, nullptr, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F32 && sp == 1)
-    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store,
                        C_store, nullptr, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F32)
-    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<float*>(nullptr), ldo, rt_stride, ct_stride,
                        R_store, C_store, pp, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F16 && sp == 1)
-    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16, false>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
                        C_store, nullptr, ntr, ntc);
