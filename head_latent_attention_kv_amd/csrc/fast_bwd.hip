@@ -122,15 +122,16 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
 // wave instruction (1 KiB) lies in one region.
 constexpr int KW = 256;     // keys per workgroup (8 waves x 32)
 constexpr int QB = 64;      // query rows per step
-// Row strides: Q 400 B; dO 272 B where it is read row-wise (dP = dO V^T in
-// the dK launch) and 320 B where it is read transposed (dV^T += dO^T P): a
+// Row strides: Q 448 B, swizzled (read row-wise and, in the dK launch,
+// transposed); dO 272 B where it is read row-wise (dP = dO V^T in the dK
+// launch) and 320 B where it is read transposed (dV^T += dO^T P): a
 // transposed read of rows 256 or 272 B apart runs at half rate.
-constexpr int QN_ROW = DQK * 2 + 16, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 64;  // 400, 272, 320
+constexpr int QN_ROW = XS_ROW, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 64;  // 448, 272, 320
 // stage (bytes): Qn [64 rows] | dOn [64 rows] | row info. Q^T and dO^T
 // fragments (the A operands of dK^T and dV^T) are transposed reads of them.
-constexpr int S_QN = 0, S_DON = 25 * 1024;
-constexpr int SK_INFO = 42 * 1024, SK_BYTES = 43 * 1024;
-constexpr int SV_INFO = 45 * 1024, SV_BYTES = 46 * 1024;
+constexpr int S_QN = 0, S_DON = 28 * 1024;
+constexpr int SK_INFO = 45 * 1024, SK_BYTES = 46 * 1024;
+constexpr int SV_INFO = 48 * 1024, SV_BYTES = 49 * 1024;
 static_assert(S_DON >= QB * QN_ROW && SK_INFO - S_DON >= QB * DONK_ROW &&
               SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
 static_assert(SV_INFO - S_DON >= QB * DONV_ROW && SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
@@ -199,9 +200,9 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
   for (int j = 0; j < NPW; ++j) {
     const int o = (w * NPW + j) * 1024 + lane * 16;
     int off = 0;
-    if (o < S_DON) {
-      const int row = min(o / QN_ROW, QB - 1), pc = min((o % QN_ROW) >> 4, DQK / 8 - 1);
-      off = row * DQK + pc * 8;
+    if (o < S_DON) {   // swizzled Q rows; pad slots 24..27 reload slot 0
+      const int row = min(o / QN_ROW, QB - 1), ph = (o % QN_ROW) >> 4;
+      off = row * DQK + (ph < DQK / 8 ? xs_slot(row, ph) : 0) * 8;
     } else if (o >= INFO) {
       off = min((o - INFO) >> 2, 2 * 128 - 4);   // 4-byte elements, 128 per 32 rows
     } else {
@@ -237,10 +238,11 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
 
   const int qrow = swap23(lr);   // A-operand row loaded by this lane
-  const int a_qn = S_QN + qrow * QN_ROW + lh * 16;
+  const int a_qn0 = S_QN + xs_row_base(qrow, lh, 0), a_qn1 = S_QN + xs_row_base(qrow, lh, 1);
   const int a_don = S_DON + qrow * DON_ROW + lh * 16;
   // Q^T (dK) or dO^T (dV) fragments: transposed reads of the row tiles
-  const int a_t = kDK ? S_QN + tr_lane_offset(lane, QN_ROW) : S_DON + tr_lane_offset(lane, DON_ROW);
+  const int a_t0 = kDK ? S_QN + xs_tr_base(lane, 0) : S_DON + tr_lane_offset(lane, DON_ROW);
+  const int a_t1 = kDK ? S_QN + xs_tr_base(lane, 1) : 0;
 
   if (nq > 0) issue(qb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -267,7 +269,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
       {
         auto frag = [&](int k) {
-          return *reinterpret_cast<const half8*>(base + a_qn + mt * 32 * QN_ROW + 32 * k);
+          return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_qn1 : a_qn0) + mt * 32 * QN_ROW + 64 * (k >> 1));
         };
         half8 fa[3];
         fa[0] = frag(0);
@@ -336,8 +338,12 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
         auto frag = [&](int k) {
           const int ks = k / NACC, dm = k % NACC;
           // dims 32 dm + lr, rows 32 mt + 16 ks + 8 lh + j
-          constexpr int TROW = kDK ? QN_ROW : DONV_ROW;
-          return frag_tr<TROW>(base + a_t + (32 * mt + 16 * ks) * TROW + 32 * dm * 2);
+          if constexpr (kDK) {
+            const int o = (32 * mt + 16 * ks) * QN_ROW + 64 * dm;
+            return frag_tr2(base + a_t0 + o, base + a_t1 + o);
+          } else {
+            return frag_tr<DONV_ROW>(base + a_t0 + (32 * mt + 16 * ks) * DONV_ROW + 32 * dm * 2);
+          }
         };
         half8 fa[3];
         fa[0] = frag(0);
@@ -384,7 +390,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
 // ------------------------------------------------------------------ dQ
 constexpr int QW = 256;     // query rows per workgroup (8 waves x 32, two per SIMD)
 constexpr int KS = 64;      // keys per step
-constexpr int K_ROW = DQK * 2 + 16, V_ROW = DV * 2 + 16;  // 400, 272
+constexpr int K_ROW = XS_ROW, V_ROW = DV * 2 + 16;  // 448 (swizzled), 272
 // stage (bytes): K [64 keys][192] | V [64 keys][128]; the K^T fragments of
 // dQ^T += K^T dS^T are transposed reads of the K tile
 constexpr int D_K = 0, D_V = KS * K_ROW, D_BYTES = D_V + KS * V_ROW;
@@ -454,9 +460,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   for (int j = 0; j < NP; ++j) {
     const int o = (w * NP + j) * 1024 + lane * 16;
     int off = 0;
-    if (o < D_V) {
-      const int row = o / K_ROW, pc = min((o % K_ROW) >> 4, DQK / 8 - 1);
-      off = row * DQK + pc * 8;
+    if (o < D_V) {   // swizzled K rows; pad slots 24..27 reload slot 0
+      const int row = o / K_ROW, ph = (o % K_ROW) >> 4;
+      off = row * DQK + (ph < DQK / 8 ? xs_slot(row, ph) : 0) * 8;
     } else if (o < D_BYTES) {
       const int oo = o - D_V, row = oo / V_ROW, pc = min((oo % V_ROW) >> 4, DV / 8 - 1);
       off = row * DV + pc * 8;
@@ -481,9 +487,10 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   for (int a = 0; a < 6; ++a)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
-  const int a_k = D_K + swap23(lr) * K_ROW + lh * 16;
+  const int a_k0 = D_K + xs_row_base(swap23(lr), lh, 0), a_k1 = D_K + xs_row_base(swap23(lr), lh, 1);
   const int a_v = D_V + swap23(lr) * V_ROW + lh * 16;
-  const int a_kt = D_K + tr_lane_offset(lane, K_ROW);   // K^T fragments: transposed reads
+  // K^T fragments: transposed reads of the K tile
+  const int a_kt0 = D_K + xs_tr_base(lane, 0), a_kt1 = D_K + xs_tr_base(lane, 1);
 
   if (nblk > 0) issue(kb_begin, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -504,7 +511,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
         {
           auto frag = [&](int k) {
-            return k < 12 ? *reinterpret_cast<const half8*>(base + a_k + mt * 32 * K_ROW + 32 * k)
+            return k < 12 ? *reinterpret_cast<const half8*>(base + ((k & 1) ? a_k1 : a_k0) + mt * 32 * K_ROW + 64 * (k >> 1))
                           : *reinterpret_cast<const half8*>(base + a_v + mt * 32 * V_ROW + 32 * (k - 12));
           };
           half8 fa[3];
@@ -532,7 +539,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           // K^T fragment: dims 32dm + lr, keys 32mt + 16ksl + 8lh + j (transposed read)
           auto frag = [&](int k) {
             const int ksl = k / 6, dm = k % 6;
-            return frag_tr<K_ROW>(base + a_kt + (32 * mt + 16 * ksl) * K_ROW + 32 * dm * 2);
+            const int o = (32 * mt + 16 * ksl) * K_ROW + 64 * dm;
+            return frag_tr2(base + a_kt0 + o, base + a_kt1 + o);
           };
           half8 fa[3];
           fa[0] = frag(0);
