@@ -217,15 +217,16 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
     for (int j = 0; j < NPW; ++j) {
       const int I = w * NPW + j;   // wave-uniform region choice
       if (I < PIECES) {
-        // the per-lane offset is opaque to the optimizer, so it cannot hoist
-        // one 64-bit address per (piece, region) out of the loop
-        int off = doff[j];
+        // wave-uniform base plus an unsigned 32-bit lane offset in bytes
+        // (the scalar-base form of the load); the offset is opaque to the
+        // optimizer, so it cannot hoist one 64-bit address per piece
+        uint32_t off = static_cast<uint32_t>(doff[j]) * (I * 1024 >= INFO ? 4u : 2u);
         asm volatile("" : "+v"(off));
-        const void* src;
-        if (I * 1024 < S_DON) src = Qn_h + static_cast<int64_t>(qb) * DQK + off;
-        else if (I * 1024 >= INFO) src = info_h + (qb / 32) * 128 + off;
-        else src = dOn_h + static_cast<int64_t>(qb) * DV + off;
-        lds_dma16(src, sbase + I * 1024);
+        const char* ub;
+        if (I * 1024 < S_DON) ub = reinterpret_cast<const char*>(Qn_h + static_cast<int64_t>(qb) * DQK);
+        else if (I * 1024 >= INFO) ub = reinterpret_cast<const char*>(info_h + (qb / 32) * 128);
+        else ub = reinterpret_cast<const char*>(dOn_h + static_cast<int64_t>(qb) * DV);
+        lds_dma16(ub + off, sbase + I * 1024);
       }
     }
   };
@@ -293,20 +294,12 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
             if (gkey < static_cast<int>(lo4[e]) || gkey > static_cast<int>(p4[e])) s[4 * g + e] = -INFINITY;
         }
       }
-      // P = exp2(S scale log2e - lse log2e) in fp16. Register r holds row
-      // swap23(d_row(r, lh)); groups of 4 are consecutive rows.
+      // P = exp2(S scale log2e - lse log2e). Register r holds row
+      // swap23(d_row(r, lh)); groups of 4 are consecutive rows. The dV launch
+      // feeds P (fp16) on; the dK launch computes dP = dO V^T and then
+      // dS = P (dP - D) from the fp32 P.
       half8 bf[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          bf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
-        }
-      }
       if constexpr (kDK) {
-        // dP = dO V^T (8 steps), then dS = P (dP - D) in place of P
         f32x16 dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[e] = 0.f;
@@ -324,11 +317,23 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
           const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            bf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(bf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e]));
+            bf[r >> 3][r & 7] = static_cast<_Float16>(pr * (dp[r] - Dd[e]));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            bf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
           }
         }
       }
@@ -475,9 +480,13 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int j = 0; j < NP; ++j) {
       const int I = w * NP + j;   // wave-uniform
       if (I < D_PIECES) {
-        const _Float16* src = I * 1024 < D_V ? Kh + static_cast<int64_t>(kb) * DQK
-                                             : Vh + static_cast<int64_t>(kb) * DV;
-        lds_dma16(src + doff[j], base + I * 1024);
+        // wave-uniform base plus an opaque unsigned 32-bit lane offset in
+        // bytes (the scalar-base form of the load)
+        const char* ub = reinterpret_cast<const char*>(I * 1024 < D_V ? Kh + static_cast<int64_t>(kb) * DQK
+                                                                      : Vh + static_cast<int64_t>(kb) * DV);
+        uint32_t off = static_cast<uint32_t>(doff[j]) * 2u;
+        asm volatile("" : "+v"(off));
+        lds_dma16(ub + off, base + I * 1024);
       }
     }
   };

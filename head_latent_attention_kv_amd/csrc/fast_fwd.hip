@@ -125,8 +125,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int I = w * NP + j;   // wave-uniform
-      if (I < STAGE_PIECES)
-        lds_dma16((I * 1024 < K_TILE_B ? kbase : vbase) + dsrc[j], dst + I * 1024);
+      if (I < STAGE_PIECES) {
+        // wave-uniform base plus an opaque unsigned 32-bit lane offset in
+        // bytes (the scalar-base form of the load)
+        uint32_t off = static_cast<uint32_t>(dsrc[j]) * 2u;
+        asm volatile("" : "+v"(off));
+        lds_dma16(reinterpret_cast<const char*>(I * 1024 < K_TILE_B ? kbase : vbase) + off, dst + I * 1024);
+      }
     }
   };
 

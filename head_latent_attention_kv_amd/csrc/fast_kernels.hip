@@ -112,11 +112,13 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   }
   auto issue = [&](int c, int st) {
     char* dst = smem + st * G_STAGE + (is_x ? 0 : G_OP) + (w % HW) * NPW * 1024;
-    const InT* s0 = src + static_cast<int64_t>(c) * GK;
+    const char* s0 = reinterpret_cast<const char*>(src + static_cast<int64_t>(c) * GK);
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-      // opaque to the optimizer, so no 64-bit address per piece is hoisted
-      int off = doff[j];
+      // wave-uniform base plus an unsigned 32-bit lane offset in bytes (the
+      // scalar-base form of the load), opaque to the optimizer so that no
+      // 64-bit address per piece is hoisted
+      uint32_t off = static_cast<uint32_t>(doff[j]) * static_cast<uint32_t>(sizeof(InT));
       asm volatile("" : "+v"(off));
       lds_dma16(s0 + off, dst + j * 1024);
     }
@@ -444,7 +446,8 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
   // every tile must hold a valid row of X and of Y (loads clamp to them)
   if (R > 0 && C > 0 && (n_tr != (R + GT - 1) / GT || n_tc != (C + GT - 1) / GT))
     return fail(MLA_ERR_UNSUPPORTED, "%s: stored extent reaches a tile past the operands", name);
-  if (ldx >= (int64_t(1) << 23) || ldy >= (int64_t(1) << 23) || n_tr * n_tc >= (int64_t(1) << 31))
+  // (lane offsets within a 256-row tile stay below 2^31 bytes)
+  if (ldx >= (int64_t(1) << 22) || ldy >= (int64_t(1) << 22) || n_tr * n_tc >= (int64_t(1) << 31))
     return fail(MLA_ERR_UNSUPPORTED, "%s: operand too wide", name);
   int sp = out_t == Elem::F32 ? gemm_splits(R_store, C_store, K) : 1;
   if (sp > 1 && (part == nullptr || part_bytes < gemm_splitk_bytes(R_store, C_store, K))) sp = 1;
