@@ -42,8 +42,8 @@ def kernel_flops(name, cfg, pairs, kn):
     not a contraction. The algorithmic figures split the step's FLOP count
     (640 per visible pair and head forward, 1664 backward, plus the
     up-projection of the needed keys) over the kernels, each product once:
-    the backward's S = Q K^T and dP = dO V^T go to the dK kernel, which is
-    the only one that needs both; the dV and dQ kernels recompute them, and
+    the backward's S = Q K^T and dP = dO V^T go to the dK/dV kernel; the dQ
+    kernel recomputes them (and, on the split path, the dV kernel S), and
     the backward's K/V rebuild launches recompute the up-projection."""
     d_qk = cfg.d_nope + cfg.d_rope
     up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
@@ -53,8 +53,10 @@ def kernel_flops(name, cfg, pairs, kn):
         "upproj": (up // 2, up // 2), "plain_upproj": (up, up),
         "attn_fwd": (per_pair(d_qk + cfg.d_v),) * 2,
         "plain_attn_fwd": (per_pair(d_qk + cfg.d_v),) * 2,
-        # dK: S, dP, dK += dS^T Q;  dV: dV += P^T dO (S recomputed);  dQ: dQ = dS K
-        # (S and dP recomputed)
+        # paired dK/dV: S, dP, dV += P^T dO, dK += dS^T Q (each once)
+        "attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
+        # split dK/dV launches: dK: S, dP, dK += dS^T Q;  dV: dV += P^T dO (S
+        # recomputed);  dQ: dQ = dS K (S and dP recomputed)
         "attn_bwd_dk": (per_pair(2 * d_qk + cfg.d_v),) * 2,
         "attn_bwd_dv": (per_pair(cfg.d_v), per_pair(d_qk + cfg.d_v)),
         "attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
@@ -73,6 +75,7 @@ CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")
 # kernel symbol fragment -> (timer name, sources whose text decides its code)
 COUNTED_KERNELS = {
     "attn_fwd_kernel": ("attn_fwd", ["fast_fwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dkv_kernelILb1": ("attn_bwd_dk", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dkv_kernelILb0": ("attn_bwd_dv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dq_kernel": ("attn_bwd_dq", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),

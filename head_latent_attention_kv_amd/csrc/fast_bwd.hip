@@ -18,8 +18,10 @@
 // Query/key tiles are DMA-filled (global_load_lds) into padded LDS rows and
 // double-buffered, as in the forward.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "fast.h"
 #include "fast_common.h"
@@ -392,6 +394,308 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
     }
 }
 
+// ------------------------------------------------------------------ dK + dV, paired waves
+// One launch for dK and dV without computing S twice. A workgroup owns 128
+// keys and runs 8 waves as 4 pairs; the pair p owns keys 32 p .. 32 p + 31.
+// Wave p ("A") holds the keys' K rows, computes S = Q K^T and P, publishes P
+// (fp16) in a 2 KiB LDS slot and accumulates dV^T += dO^T P. Wave p + 4
+// ("B") holds the keys' V rows, computes dP = dO V^T, takes P from the slot,
+// forms dS = P (dP - D) and accumulates dK^T += Q^T dS. Each role does 20 of
+// the 40 products of a 32 x 32 sub-block and keeps under 256 registers, so
+// two waves share each SIMD. One barrier per 32-row sub-block separates the
+// publication of P from its use; the slot is double-buffered, so A writes
+// P(t + 2) only after the barrier that follows B's read of P(t).
+//
+// Tiles: q rows (swizzled 448-byte rows, read row-wise by A and transposed by
+// B) and dout rows (swizzled 320-byte rows, read row-wise by B and transposed
+// by A), double-buffered per 64-row block and DMA-filled.
+constexpr int PW = 128;                        // keys per workgroup
+constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
+constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
+constexpr int P_PIECES = P_BYTES / 1024;       // 49
+constexpr int P_NPW = (P_PIECES + 7) / 8;      // 7 per wave
+constexpr int P_XCH = 2 * P_BYTES;             // P slots: [pair][buffer] x 2 KiB
+static_assert(P_DON >= QB * XS_ROW && P_INFO - P_DON >= QB * PD_ROW && P_BYTES - P_INFO >= QB * 16,
+              "paired dK/dV stage layout");
+
+__global__ void __launch_bounds__(512)
+attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
+                     const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
+                     const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
+                     _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
+                     float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
+                     int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 4 * 2 * 2048];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lr = lane & 31, lh = lane >> 5;
+  const bool role_a = w < 4;
+  const int pi = w & 3;                       // pair index
+  int h, kt;
+  work_item(blockIdx.x, n_h, n_kt, &h, &kt);
+  const int t0 = kt * PW;                     // workspace key row of the workgroup
+  const int tw = t0 + 32 * pi;                // the pair's first key
+  const int gkey = key_lo + tw + lr;          // this lane's key (global)
+  const int gk_min = key_lo + t0, gk_max = key_lo + t0 + PW - 1;
+  const int gw_min = key_lo + tw, gw_max = gw_min + 31;
+  char* const xslot = smem + P_XCH + pi * 4096;   // this pair's two P slots
+
+  // query rows that see any key of the workgroup: from the first row at or
+  // past its first key to the last row whose sample starts by its last key
+  const int i_begin = max(gk_min - q_offset, 0);
+  int i_end = S_loc;
+  if (n_seqs > 0) {
+    // first sample start after gk_max (none: S): rows from there on see nothing here
+    int lo_i = 0, hi_i = n_seqs + 1;
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (cu[mid] <= gk_max) lo_i = mid; else hi_i = mid;
+    }
+    if (lo_i + 1 <= n_seqs) i_end = min(i_end, cu[lo_i + 1] - q_offset);
+  }
+  const int qb_begin = (i_begin / QB) * QB;
+  const int nq = i_end > qb_begin ? (i_end - qb_begin + QB - 1) / QB : 0;
+
+  // DMA: per-lane source offsets (elements) relative to the region's first
+  // row qb; a row's pad slots reload its slot 0 and are never read back
+  const _Float16* Qn_h = Qn + static_cast<int64_t>(h) * S_pad * DQK;
+  const _Float16* dOn_h = dOn + static_cast<int64_t>(h) * S_pad * DV;
+  const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / 32) * 128;
+  int doff[P_NPW];
+#pragma unroll
+  for (int j = 0; j < P_NPW; ++j) {
+    const int o = (w * P_NPW + j) * 1024 + lane * 16;
+    int off = 0;
+    if (o < P_DON) {
+      const int row = min(o / XS_ROW, QB - 1), ph = (o % XS_ROW) >> 4;
+      off = row * DQK + (ph < DQK / 8 ? xs_slot(row, ph) : 0) * 8;
+    } else if (o < P_INFO) {
+      const int oo = o - P_DON, row = min(oo / PD_ROW, QB - 1), ph = (oo % PD_ROW) >> 4;
+      off = row * DV + (ph < DV / 8 ? xs_slot(row, ph) : 0) * 8;
+    } else {
+      off = min((o - P_INFO) >> 2, 2 * 128 - 4);   // 4-byte elements, 128 per 32 rows
+    }
+    doff[j] = off;
+  }
+  auto issue = [&](int qb, int st) {
+    char* sbase = smem + st * P_BYTES;
+#pragma unroll
+    for (int j = 0; j < P_NPW; ++j) {
+      const int I = w * P_NPW + j;   // wave-uniform region choice
+      if (I < P_PIECES) {
+        // wave-uniform base plus an opaque unsigned 32-bit lane offset in
+        // bytes (the scalar-base form of the load)
+        uint32_t off = static_cast<uint32_t>(doff[j]) * (I * 1024 >= P_INFO ? 4u : 2u);
+        asm volatile("" : "+v"(off));
+        const char* ub;
+        if (I * 1024 < P_DON) ub = reinterpret_cast<const char*>(Qn_h + static_cast<int64_t>(qb) * DQK);
+        else if (I * 1024 < P_INFO) ub = reinterpret_cast<const char*>(dOn_h + static_cast<int64_t>(qb) * DV);
+        else ub = reinterpret_cast<const char*>(info_h + (qb / 32) * 128);
+        lds_dma16(ub + off, sbase + I * 1024);
+      }
+    }
+  };
+
+  // The two roles run separate copies of the loop, so that the registers of
+  // one (K rows, dV^T) and of the other (V rows, dK^T) can share storage;
+  // both copies pass the same barriers in the same order.
+  auto run = [&](auto role) {
+    constexpr bool kA = decltype(role)::value;
+    // A: the keys' K rows; B: their V rows (MFMA B fragments)
+    half8 kf[kA ? 12 : 1], vf[kA ? 1 : 8];
+    if constexpr (kA) {
+      const _Float16* kr = Kfull + (static_cast<int64_t>(h) * Kpad + tw + lr) * DQK + 8 * lh;
+#pragma unroll
+      for (int kk = 0; kk < 12; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kr + 16 * kk);
+    } else {
+      const _Float16* vr = Vkm + (static_cast<int64_t>(h) * Kpad + tw + lr) * DV + 8 * lh;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) vf[kk] = *reinterpret_cast<const half8*>(vr + 16 * kk);
+    }
+    // A: dV^T tiles (4 x 32 dims); B: dK^T tiles (6 x 32 dims)
+    f32x16 acc[6];
+  #pragma unroll
+    for (int a = 0; a < 6; ++a)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
+
+    const int qrow = swap23(lr);   // row-operand row loaded by this lane
+    // A: q rows (S) and dout^T (dV); B: dout rows (dP) and q^T (dK)
+    const int a_r0 = kA ? P_QN + xs_row_base<XS_ROW>(qrow, lh, 0) : P_DON + xs_row_base<PD_ROW>(qrow, lh, 0);
+    const int a_r1 = kA ? P_QN + xs_row_base<XS_ROW>(qrow, lh, 1) : P_DON + xs_row_base<PD_ROW>(qrow, lh, 1);
+    const int a_t0 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 0) : P_QN + xs_tr_base<XS_ROW>(lane, 0);
+    const int a_t1 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 1) : P_QN + xs_tr_base<XS_ROW>(lane, 1);
+
+    if (nq > 0) issue(qb_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int b = 0; b < nq; ++b) {
+      const int st = b & 1;
+      const int qb = qb_begin + b * QB;
+      if (b + 1 < nq) issue(qb + QB, st ^ 1);
+      const char* base = smem + st * P_BYTES;
+  #pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int q0 = qb + 32 * mt;
+        char* xs = xslot + mt * 2048;          // sub-block parity: buffer mt
+        const float* rinfo = reinterpret_cast<const float*>(base + P_INFO + mt * 512);
+        const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 64);
+        // positions of the sub-block's rows: q_offset + q0 ..; rows past S_loc have p = -1
+        const int p_first = q_offset + q0;
+        const int p_last = q_offset + min(q0 + 32, S_loc) - 1;
+        // the same for both waves of a pair (same keys, same rows)
+        const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
+        half8 pf[2];
+        f32x16 dp;
+        // ---- phase 1: A computes S and P and publishes P; B computes dP
+        if (!skip) {
+          if constexpr (kA) {
+            const bool full = q0 + 32 <= S_loc && p_first >= gw_max && iinfo[31] <= gw_min;
+            f32x16 s;
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = 0.f;
+            auto frag = [&](int k) {
+              return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_r1 : a_r0) + mt * 32 * XS_ROW + 64 * (k >> 1));
+            };
+            half8 fa[3];
+            fa[0] = frag(0);
+            fa[1] = frag(1);
+  #pragma unroll
+            for (int k = 0; k < 12; ++k) {
+              if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
+              s = mfma_f16(fa[k % 3], kf[k], s);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (!full) {
+              // rows that do not see this lane's key get weight 0 (score -> -inf)
+  #pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int r0 = swap23(d_row(4 * g, lh));
+                const u32x4 lo4 = *reinterpret_cast<const u32x4*>(iinfo + r0);
+                const u32x4 p4 = *reinterpret_cast<const u32x4*>(iinfo + 32 + r0);
+  #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (gkey < static_cast<int>(lo4[e]) || gkey > static_cast<int>(p4[e])) s[4 * g + e] = -INFINITY;
+              }
+            }
+            // P = exp2(S scale log2e - lse log2e) in fp16; register r holds row
+            // swap23(d_row(r, lh)) and groups of 4 are consecutive rows
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                pf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
+              }
+            }
+            *reinterpret_cast<half8*>(xs + lane * 16) = pf[0];
+            *reinterpret_cast<half8*>(xs + 1024 + lane * 16) = pf[1];
+          } else {
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+            auto frag = [&](int k) {
+              return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_r1 : a_r0) + mt * 32 * PD_ROW + 64 * (k >> 1));
+            };
+            half8 fa[3];
+            fa[0] = frag(0);
+            fa[1] = frag(1);
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
+              dp = mfma_f16(fa[k % 3], vf[k], dp);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        // P(t) visible to B; every wave, every sub-block
+        __syncthreads();
+        // ---- phase 2: A accumulates dV^T; B forms dS and accumulates dK^T
+        if (!skip) {
+          if constexpr (kA) {
+            // dV^T (dims x keys) += dO^T (dims x rows) . P (rows x keys)
+            auto frag = [&](int k) {
+              const int ks = k / 4, dt = k % 4;
+              const int o = (32 * mt + 16 * ks) * PD_ROW + 64 * dt;
+              return frag_tr2(base + a_t0 + o, base + a_t1 + o);
+            };
+            half8 fa[3];
+            fa[0] = frag(0);
+            fa[1] = frag(1);
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
+              acc[k % 4] = mfma_f16(fa[k % 3], pf[k / 4], acc[k % 4]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            pf[0] = *reinterpret_cast<const half8*>(xs + lane * 16);
+            pf[1] = *reinterpret_cast<const half8*>(xs + 1024 + lane * 16);
+            half8 dsf[2];
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
+              }
+            }
+            // dK^T (dims x keys) += Q^T (dims x rows) . dS (rows x keys)
+            auto frag = [&](int k) {
+              const int ks = k / 6, dm = k % 6;
+              const int o = (32 * mt + 16 * ks) * XS_ROW + 64 * dm;
+              return frag_tr2(base + a_t0 + o, base + a_t1 + o);
+            };
+            half8 fa[3];
+            fa[0] = frag(0);
+            fa[1] = frag(1);
+  #pragma unroll
+            for (int k = 0; k < 12; ++k) {
+              if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
+              acc[k % 6] = mfma_f16(fa[k % 3], dsf[k / 6], acc[k % 6]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+
+    // write: lane = key t, registers = dims (four consecutive per group)
+    const int64_t t = tw + lr;
+    const int64_t nk = static_cast<int64_t>(n_h) * 128;
+    const int nacc = kA ? 4 : 6;
+  #pragma unroll
+    for (int mt = 0; mt < 6; ++mt) {
+      if (mt >= nacc) break;
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3
+        const float sc = kA ? 1.f : scale;
+        const float v0 = acc[mt][4 * g] * sc, v1 = acc[mt][4 * g + 1] * sc,
+                    v2 = acc[mt][4 * g + 2] * sc, v3 = acc[mt][4 * g + 3] * sc;
+        if (d < 128) {
+          const int64_t col = (kA ? nk : 0) + static_cast<int64_t>(h) * 128 + d;
+          const half4 hv = {static_cast<_Float16>(v0), static_cast<_Float16>(v1),
+                            static_cast<_Float16>(v2), static_cast<_Float16>(v3)};
+          *reinterpret_cast<half4*>(dKV + t * (2 * nk) + col) = hv;
+          dKVT[(col + 0) * Kpad + t] = hv[0];
+          dKVT[(col + 1) * Kpad + t] = hv[1];
+          dKVT[(col + 2) * Kpad + t] = hv[2];
+          dKVT[(col + 3) * Kpad + t] = hv[3];
+        } else {
+          const f32x4 fv = {v0, v1, v2, v3};
+          *reinterpret_cast<f32x4*>(dKr + (static_cast<int64_t>(h) * Kpad + t) * 64 + (d - 128)) = fv;
+        }
+      }
+    }
+  };
+  if (role_a) run(std::true_type());
+  else run(std::false_type());
+}
+
 // ------------------------------------------------------------------ dQ
 constexpr int QW = 256;     // query rows per workgroup (8 waves x 32, two per SIMD)
 constexpr int KS = 64;      // keys per step
@@ -601,6 +905,15 @@ zero_rows_kernel(float* __restrict__ p, int64_t n) {
     p[e] = 0.f;
 }
 
+// dK and dV in one paired launch (default) or two (MLA_LAGA_BWD_SPLIT=1).
+bool bwd_paired() {
+  static const bool v = [] {
+    const char* e = getenv("MLA_LAGA_BWD_SPLIT");
+    return !(e && atoi(e) == 1);
+  }();
+  return v;
+}
+
 unsigned grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   return static_cast<unsigned>(g < 1 ? 1 : (g > 16384 ? 16384 : g));
@@ -659,7 +972,13 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
-  {
+  if (bwd_paired()) {
+    const int n_kt = static_cast<int>(p.Kpad / PW);
+    KernelTimer kt("attn_bwd_dkdv", st);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
+                       Sp, q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+  } else {
     const int n_kt = static_cast<int>(p.Kpad / KW);
     const unsigned grid = static_cast<unsigned>(n_kt * p.n_h);
     {

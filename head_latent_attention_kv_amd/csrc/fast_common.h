@@ -81,25 +81,28 @@ __device__ __forceinline__ half8 frag_tr(const char* p) {
   return half8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
 }
 
-// Swizzled LDS rows for 192-element (16-bit) tiles read both row-wise
-// (16-byte fragment loads) and transposed (ds_read_b64_tr_b16): rows 448
-// bytes apart, and the 16-byte slot s of row r stored at slot s ^ ((r / 4) % 4).
-// Row-wise loads of 16 consecutive rows then hit 16 different bank slots,
-// and a transposed load's four rows (r / 4 equal) share one permutation.
+// Swizzled LDS rows for 16-bit tiles read both row-wise (16-byte fragment
+// loads) and transposed (ds_read_b64_tr_b16): the 16-byte slot s of row r is
+// stored at slot s ^ ((r / 4) % 4). With a row pitch of 448 bytes (192
+// elements) or 320 bytes (128 elements), row-wise loads of 16 consecutive
+// rows then hit 16 different bank slots, and a transposed load's four rows
+// (r / 4 equal) share one permutation.
 constexpr int XS_ROW = 448;
 __device__ __forceinline__ int xs_slot(int row, int slot) { return slot ^ ((row >> 2) & 3); }
 // Row-wise fragment of row `row`, k-slots 16 k + 8 lh .. (logical 16-byte
 // slot 2 k + lh): byte offset xs_row_base(row, lh, k & 1) + 64 (k / 2).
+template <int kRowBytes = XS_ROW>
 __device__ __forceinline__ int xs_row_base(int row, int lh, int kpar) {
-  return row * XS_ROW + xs_slot(row, 2 * kpar + lh) * 16;
+  return row * kRowBytes + xs_slot(row, 2 * kpar + lh) * 16;
 }
 // Transposed fragment (see frag_tr) of rows k0 .. k0 + 15 (k0 a multiple of
 // 16) and columns 32 dm ..: the two reads are at xs_tr_base(lane, 0) and
-// xs_tr_base(lane, 1), each plus k0 * XS_ROW + 64 dm.
+// xs_tr_base(lane, 1), each plus k0 * row pitch + 64 dm.
+template <int kRowBytes = XS_ROW>
 __device__ __forceinline__ int xs_tr_base(int lane, int h) {
   const int g = lane >> 4, p = lane & 15;
   const int row = 8 * (g >> 1) + 4 * h + (p >> 2);
-  return row * XS_ROW + xs_slot(row, 2 * (g & 1) + ((p & 3) >> 1)) * 16 + 8 * (p & 1);
+  return row * kRowBytes + xs_slot(row, 2 * (g & 1) + ((p & 3) >> 1)) * 16 + 8 * (p & 1);
 }
 __device__ __forceinline__ half8 frag_tr2(const char* p0, const char* p1) {
   typedef __attribute__((address_space(3))) short4v lds_short4;
