@@ -93,8 +93,9 @@ FwdLayout fwd_layout(const Plan& p, bool fast) {
     L.WT = take(static_cast<int64_t>(p.n_h) * (p.d_nope + p.d_v) * p.d_c * 2);  // bf16
     L.Kfull = take(static_cast<int64_t>(p.n_h) * p.Kpad * p.d_qk * 2);         // fp16
     L.Vt = take(static_cast<int64_t>(p.n_h) * p.d_v * p.Kpad * 2);             // fp16
+    L.order = take(4 * ((p.S_loc + 255) / 256));
   } else {
-    L.WT = L.Kfull = L.Vt = -1;
+    L.WT = L.Kfull = L.Vt = L.order = -1;
     L.K = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_qk * 4);
     L.V = take(static_cast<int64_t>(p.n_h) * p.Kn * p.d_v * 4);
   }
@@ -110,11 +111,11 @@ BwdLayout bwd_layout(const Plan& p) {
     off += align_up(bytes, kAlign);
     return o;
   };
-  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = -1;
+  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = L.order = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
     const int64_t S_pad = align_up(p.S_loc, 64);
-    L.f.K = L.f.V = L.f.Vt = -1;
+    L.f.K = L.f.V = L.f.Vt = L.f.order = -1;
     L.f.WT = take(2 * nk * p.d_c * 2);
     L.f.Kfull = take(p.n_h * p.Kpad * 192 * 2);
     L.Vkm = take(nk * p.Kpad * 2);
@@ -129,6 +130,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.info = take(p.n_h * S_pad * 16);
     L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
                             gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
+    L.order = take(4 * ((p.S_loc + 255) / 256 + p.Kpad / 128));
     L.f.total = -1;
   } else {
     L.f = fwd_layout(p, false);

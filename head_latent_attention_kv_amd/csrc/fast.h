@@ -30,6 +30,16 @@ mla_status launch_broadcast_rows_f16(const uint16_t* in, int64_t ld_in, int64_t 
                                      int64_t out_batch, int batch, hipStream_t st,
                                      const char* name);
 
+// Tiles of a packed call that get a longest-processing-time order.
+constexpr int kMaxOrderTiles = 2048;
+
+// qorder[0 .. n_qt) / korder[0 .. n_kt) = query tiles (256 rows) / key tiles
+// (128 workspace keys) of a packed call by decreasing number of visible
+// (row, key) pairs; korder may be null. n_qt, n_kt <= kMaxOrderTiles.
+mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, int64_t q_offset,
+                             int64_t key_lo, int64_t Kn, int n_qt, int n_kt, int* qorder,
+                             int* korder, hipStream_t st);
+
 // Out[r][c] = sum_k X[r][k] * Y[c][k] on MFMA, K % 64 == 0. X rows >= R and
 // Y rows >= C count as 0. Element (r, c) is stored at
 //   out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride + c % 128

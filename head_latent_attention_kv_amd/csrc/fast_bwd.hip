@@ -410,6 +410,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
 // B) and dout rows (swizzled 320-byte rows, read row-wise by B and transposed
 // by A), double-buffered per 64-row block and DMA-filled.
 constexpr int PW = 128;                        // keys per workgroup
+constexpr int PF = 4;                          // fragment reads in flight ahead of the products
 constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
 constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
 constexpr int P_PIECES = P_BYTES / 1024;       // 49
@@ -422,6 +423,7 @@ __global__ void __launch_bounds__(512)
 attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
                      const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                      const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
+                     const int* __restrict__ korder,
                      _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
                      float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
                      int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
@@ -433,6 +435,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
   const int pi = w & 3;                       // pair index
   int h, kt;
   work_item(blockIdx.x, n_h, n_kt, &h, &kt);
+  if (korder != nullptr) kt = korder[kt];     // packed calls: heaviest key tiles first
   const int t0 = kt * PW;                     // workspace key row of the workgroup
   const int tw = t0 + 32 * pi;                // the pair's first key
   const int gkey = key_lo + tw + lr;          // this lane's key (global)
@@ -557,13 +560,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             auto frag = [&](int k) {
               return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_r1 : a_r0) + mt * 32 * XS_ROW + 64 * (k >> 1));
             };
-            half8 fa[3];
-            fa[0] = frag(0);
-            fa[1] = frag(1);
+            half8 fa[PF + 1];
+            #pragma unroll
+            for (int i = 0; i < PF; ++i) fa[i] = frag(i);
   #pragma unroll
             for (int k = 0; k < 12; ++k) {
-              if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
-              s = mfma_f16(fa[k % 3], kf[k], s);
+              if (k + PF < 12) fa[(k + PF) % (PF + 1)] = frag(k + PF);
+              s = mfma_f16(fa[k % (PF + 1)], kf[k], s);
               __builtin_amdgcn_sched_barrier(0);
             }
             if (!full) {
@@ -597,13 +600,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             auto frag = [&](int k) {
               return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_r1 : a_r0) + mt * 32 * PD_ROW + 64 * (k >> 1));
             };
-            half8 fa[3];
-            fa[0] = frag(0);
-            fa[1] = frag(1);
+            half8 fa[PF + 1];
+            #pragma unroll
+            for (int i = 0; i < PF; ++i) fa[i] = frag(i);
   #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
-              dp = mfma_f16(fa[k % 3], vf[k], dp);
+              if (k + PF < 8) fa[(k + PF) % (PF + 1)] = frag(k + PF);
+              dp = mfma_f16(fa[k % (PF + 1)], vf[k], dp);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -619,13 +622,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               const int o = (32 * mt + 16 * ks) * PD_ROW + 64 * dt;
               return frag_tr2(base + a_t0 + o, base + a_t1 + o);
             };
-            half8 fa[3];
-            fa[0] = frag(0);
-            fa[1] = frag(1);
+            half8 fa[PF + 1];
+            #pragma unroll
+            for (int i = 0; i < PF; ++i) fa[i] = frag(i);
   #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
-              acc[k % 4] = mfma_f16(fa[k % 3], pf[k / 4], acc[k % 4]);
+              if (k + PF < 8) fa[(k + PF) % (PF + 1)] = frag(k + PF);
+              acc[k % 4] = mfma_f16(fa[k % (PF + 1)], pf[k / 4], acc[k % 4]);
               __builtin_amdgcn_sched_barrier(0);
             }
           } else {
@@ -647,13 +650,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               const int o = (32 * mt + 16 * ks) * XS_ROW + 64 * dm;
               return frag_tr2(base + a_t0 + o, base + a_t1 + o);
             };
-            half8 fa[3];
-            fa[0] = frag(0);
-            fa[1] = frag(1);
+            half8 fa[PF + 1];
+            #pragma unroll
+            for (int i = 0; i < PF; ++i) fa[i] = frag(i);
   #pragma unroll
             for (int k = 0; k < 12; ++k) {
-              if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
-              acc[k % 6] = mfma_f16(fa[k % 3], dsf[k / 6], acc[k % 6]);
+              if (k + PF < 12) fa[(k + PF) % (PF + 1)] = frag(k + PF);
+              acc[k % 6] = mfma_f16(fa[k % (PF + 1)], dsf[k / 6], acc[k % 6]);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -699,6 +702,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
 // ------------------------------------------------------------------ dQ
 constexpr int QW = 256;     // query rows per workgroup (8 waves x 32, two per SIMD)
 constexpr int KS = 64;      // keys per step
+constexpr int QPF = 4;      // fragment reads in flight ahead of the products
 constexpr int K_ROW = XS_ROW, V_ROW = DV * 2 + 16;  // 448 (swizzled), 272
 // stage (bytes): K [64 keys][192] | V [64 keys][128]; the K^T fragments of
 // dQ^T += K^T dS^T are transposed reads of the K tile
@@ -710,7 +714,8 @@ __global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ D,
                    const _Float16* __restrict__ Kfull, const _Float16* __restrict__ Vkm,
-                   const int32_t* __restrict__ cu, float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
+                   const int32_t* __restrict__ cu, const int* __restrict__ qorder,
+                   float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
                    int key_lo, int Kpad, int n_qt, float scale, float scale_log2) {
   constexpr int NP = (D_PIECES + 7) / 8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * D_BYTES];
@@ -719,7 +724,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int lr = lane & 31, lh = lane >> 5;
   int h, qt;
   work_item(blockIdx.x, n_h, n_qt, &h, &qt);
-  qt = n_qt - 1 - qt;   // heaviest (latest) rows first
+  // heaviest tiles first: the latest rows, or the packed call's order
+  qt = qorder != nullptr ? qorder[qt] : n_qt - 1 - qt;
   const int q0 = qt * QW;
   const int wq0 = q0 + 32 * w;
   const int i = wq0 + lr;
@@ -827,14 +833,14 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             return k < 12 ? *reinterpret_cast<const half8*>(base + ((k & 1) ? a_k1 : a_k0) + mt * 32 * K_ROW + 64 * (k >> 1))
                           : *reinterpret_cast<const half8*>(base + a_v + mt * 32 * V_ROW + 32 * (k - 12));
           };
-          half8 fa[3];
-          fa[0] = frag(0);
-          fa[1] = frag(1);
+          half8 fa[QPF + 1];
+          #pragma unroll
+          for (int i = 0; i < QPF; ++i) fa[i] = frag(i);
 #pragma unroll
           for (int k = 0; k < 20; ++k) {
-            if (k + 2 < 20) fa[(k + 2) % 3] = frag(k + 2);
-            if (k < 12) s = mfma_f16(fa[k % 3], qf[k], s);
-            else dp = mfma_f16(fa[k % 3], df[k - 12], dp);
+            if (k + QPF < 20) fa[(k + QPF) % (QPF + 1)] = frag(k + QPF);
+            if (k < 12) s = mfma_f16(fa[k % (QPF + 1)], qf[k], s);
+            else dp = mfma_f16(fa[k % (QPF + 1)], df[k - 12], dp);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -855,13 +861,13 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             const int o = (32 * mt + 16 * ksl) * K_ROW + 64 * dm;
             return frag_tr2(base + a_kt0 + o, base + a_kt1 + o);
           };
-          half8 fa[3];
-          fa[0] = frag(0);
-          fa[1] = frag(1);
+          half8 fa[QPF + 1];
+          #pragma unroll
+          for (int i = 0; i < QPF; ++i) fa[i] = frag(i);
 #pragma unroll
           for (int k = 0; k < 12; ++k) {
-            if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
-            acc[k % 6] = mfma_f16(fa[k % 3], dsf[k / 6], acc[k % 6]);
+            if (k + QPF < 12) fa[(k + QPF) % (QPF + 1)] = frag(k + QPF);
+            acc[k % 6] = mfma_f16(fa[k % (QPF + 1)], dsf[k / 6], acc[k % 6]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -972,11 +978,24 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
+  // packed calls: query and key tiles in longest-processing-time order
+  int *qorder = nullptr, *korder = nullptr;
+  {
+    const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW), n_kt = static_cast<int>(p.Kpad / PW);
+    if (p.n_seqs > 0 && n_qt <= kMaxOrderTiles && n_kt <= kMaxOrderTiles) {
+      qorder = reinterpret_cast<int*>(at(L.order));
+      korder = qorder + n_qt;
+      if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kn, n_qt, n_kt,
+                                 qorder, bwd_paired() ? korder : nullptr, st)) != MLA_OK)
+        return s;
+      if (!bwd_paired()) korder = nullptr;
+    }
+  }
   if (bwd_paired()) {
     const int n_kt = static_cast<int>(p.Kpad / PW);
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
-                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
                        Sp, q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
   } else {
     const int n_kt = static_cast<int>(p.Kpad / KW);
@@ -1001,7 +1020,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     KernelTimer kt("attn_bwd_dq", st);
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       lse, D, Kfull, Vkm, cu_dev, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
+                       lse, D, Kfull, Vkm, cu_dev, qorder, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
                        key_lo, Kpad, n_qt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;

@@ -41,18 +41,23 @@ constexpr int STAGE_PIECES = STAGE_B / 1024;  // 43 DMA wave instructions
 constexpr float kTau = 8.f;         // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
-__device__ __forceinline__ void work_item(int bid, int n_h, int n_qt, int* h, int* qt) {
+__device__ __forceinline__ void work_item(int bid, int n_h, int n_qt, const int* order, int* h,
+                                          int* qt) {
   // consecutive workgroups land on different XCDs (round robin over 8); with
   // n_h % 8 == 0 all query tiles of a head run on one XCD and share its L2.
-  // Within a head the heaviest (latest) query tile goes first.
+  // Within a head the heaviest query tile goes first: the latest one for a
+  // single causal sample, the first of `order` (tiles by decreasing
+  // visible pairs) for a packed call.
+  int r;
   if ((n_h & 7) == 0) {
     const int xcd = bid & 7, slot = bid >> 3;
     *h = (slot / n_qt) * 8 + xcd;
-    *qt = n_qt - 1 - slot % n_qt;
+    r = slot % n_qt;
   } else {
     *h = bid % n_h;
-    *qt = n_qt - 1 - bid / n_h;
+    r = bid / n_h;
   }
+  *qt = order != nullptr ? order[r] : n_qt - 1 - r;
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -65,8 +70,9 @@ template <int NT, int NW>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfull,
                 const _Float16* __restrict__ Vt, const int32_t* __restrict__ cu,
-                float* __restrict__ out, float* __restrict__ lse, int n_h, int n_seqs,
-                int S_loc, int q_offset, int key_lo, int Kpad, int n_qt, float scale_log2) {
+                const int* __restrict__ order, float* __restrict__ out, float* __restrict__ lse,
+                int n_h, int n_seqs, int S_loc, int q_offset, int key_lo, int Kpad, int n_qt,
+                float scale_log2) {
   static_assert(NT * NW * 32 == FQ, "workgroup covers 256 query rows");
   constexpr int NP = (STAGE_PIECES + NW - 1) / NW;  // DMA pieces per wave and stage
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_B];
@@ -74,7 +80,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
   int h, qt;
-  work_item(blockIdx.x, n_h, n_qt, &h, &qt);
+  work_item(blockIdx.x, n_h, n_qt, order, &h, &qt);
   const int q0 = qt * FQ;
   const int wq0 = q0 + NT * 32 * w;
 
@@ -191,14 +197,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 #pragma unroll
           for (int e = 0; e < 16; ++e) s[nt][e] = 0.f;
         const char* skm = sk + mt * 32 * K_ROW_B;
-        half8 fa[3];
-        fa[0] = *reinterpret_cast<const half8*>(skm);
-        fa[1] = *reinterpret_cast<const half8*>(skm + 32);
+        // K fragment reads run FPF products ahead
+        constexpr int FPF = 4;
+        half8 fa[FPF + 1];
+#pragma unroll
+        for (int i = 0; i < FPF; ++i) fa[i] = *reinterpret_cast<const half8*>(skm + 32 * i);
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) {
-          if (kk + 2 < 12) fa[(kk + 2) % 3] = *reinterpret_cast<const half8*>(skm + 32 * (kk + 2));
+          if (kk + FPF < 12) fa[(kk + FPF) % (FPF + 1)] = *reinterpret_cast<const half8*>(skm + 32 * (kk + FPF));
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma_f16(fa[kk % 3], qf[nt][kk], s[nt]);
+          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma_f16(fa[kk % (FPF + 1)], qf[nt][kk], s[nt]);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (need_mask) {
@@ -355,17 +363,25 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   const int64_t blocks = static_cast<int64_t>(n_qt) * p.n_h;
   if (blocks > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups");
   const float scale_log2 = p.scale * 1.44269504088896340736f;
+  // packed calls: query tiles in longest-processing-time order
+  int* order = nullptr;
+  if (p.n_seqs > 0 && n_qt <= kMaxOrderTiles) {
+    order = reinterpret_cast<int*>(ws + L.order);
+    if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kn, n_qt, 0,
+                               order, nullptr, st)) != MLA_OK)
+      return s;
+  }
   const int S_loc = static_cast<int>(p.S_loc), q_off = static_cast<int>(p.q_offset),
             key_lo = static_cast<int>(p.key_lo), Kpad = static_cast<int>(p.Kpad);
   {
     KernelTimer kt("attn_fwd", st);
     if (attn_fwd_variant() == 2)
       hipLaunchKernelGGL((attn_fwd_kernel<2, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, out, lse, p.n_h,
+                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
                          p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
     else
       hipLaunchKernelGGL((attn_fwd_kernel<1, 8>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
-                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, out, lse, p.n_h,
+                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
                          p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
   }
   return check_launch("attention forward");

@@ -36,6 +36,7 @@ struct FwdLayout {
   int64_t K, V;
   // fast path: [W_UK | W_UV]^T bf16, keys [n_h][Kpad][192] fp16, V^T [n_h][128][Kpad] fp16
   int64_t WT, Kfull, Vt;
+  int64_t order;  // fast path, packed calls: query-tile order (int32 [ceil(S_loc / 256)])
   int64_t total;
 };
 struct BwdLayout {
@@ -51,6 +52,9 @@ struct BwdLayout {
   int64_t KfullT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
   int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
   int64_t gpart;  // fast path: split-K partial sums of the gradient GEMMs (fp32)
+  // fast path, packed calls: query-tile then key-tile order (int32
+  // [ceil(S_loc / 256) + Kpad / 128])
+  int64_t order;
   int64_t total;
 };
 
