@@ -22,6 +22,7 @@ differences, shard and segment identities). None is "parity unpinned".
 from .mla_oracle import (  # noqa: F401
     default_scale,
     segment_start,
+    row_positions,
     visible_range,
     visible_pairs,
     key_range,

@@ -19,9 +19,13 @@ Sources and readings
     - score s_ij = scale * q_i . K_j with scale = 1/sqrt(d_nope + d_rope)
       unless given; lse is the natural log of the sum of exp of the scaled
       scores.
-* Masking. A query's global position is p = q_offset + i (one sequence-
-  parallel shard holds a contiguous block of query rows, the full latent is
-  gathered). Without packing a query sees keys 0..p (causal). With packed
+* Masking. A query's global position is p = q_offset + i when a sequence-
+  parallel shard holds one contiguous block of query rows (the full latent
+  is gathered). A shard may instead hold several ascending, disjoint blocks
+  (zigzag or striped sharding, which evens out causal work across ranks;
+  pith.science review of Libra, Related Work beside Fig. 15): its local rows
+  are then those blocks concatenated, and row i's position is read off
+  that concatenation. Without packing a query sees keys 0..p (causal). With packed
   samples (Libra review page, "Axiom ledger": fixed-token packing, block-
   diagonal causal mask) it sees keys seg_lo(p)..p where seg_lo(p) is the
   start of the sample holding p; empty samples hold no position.
@@ -69,42 +73,66 @@ def segment_start(p: np.ndarray, cu_seqlens: Optional[np.ndarray]) -> np.ndarray
     return cu[k]
 
 
+def row_positions(S_loc: int, q_offset: int = 0,
+                  q_ranges: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+    """Global position of every local query row.
+
+    One contiguous block: q_offset + i. With ``q_ranges`` (a list of
+    (start, length) blocks), the local rows are the blocks' positions laid
+    end to end in the order given; their lengths must add up to S_loc.
+    """
+    if q_ranges is None:
+        return q_offset + np.arange(S_loc, dtype=np.int64)
+    parts = [np.arange(int(a), int(a) + int(n), dtype=np.int64) for a, n in q_ranges]
+    pos = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    if len(pos) != S_loc:
+        raise ValueError(f"q_ranges cover {len(pos)} rows, S_loc is {S_loc}")
+    return pos
+
+
 def visible_range(S_loc: int, q_offset: int,
-                  cu_seqlens: Optional[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
+                  cu_seqlens: Optional[np.ndarray],
+                  q_ranges: Optional[Sequence[Tuple[int, int]]] = None
+                  ) -> Tuple[np.ndarray, np.ndarray]:
     """Inclusive [lo, hi] key range each local query row sees."""
-    p = q_offset + np.arange(S_loc, dtype=np.int64)
+    p = row_positions(S_loc, q_offset, q_ranges)
     return segment_start(p, cu_seqlens), p
 
 
 def visible_pairs(S_loc: int, q_offset: int,
-                  cu_seqlens: Optional[np.ndarray] = None) -> int:
+                  cu_seqlens: Optional[np.ndarray] = None,
+                  q_ranges: Optional[Sequence[Tuple[int, int]]] = None) -> int:
     """Number of (query, key) pairs with nonzero attention weight, per head."""
-    lo, hi = visible_range(S_loc, q_offset, cu_seqlens)
+    lo, hi = visible_range(S_loc, q_offset, cu_seqlens, q_ranges)
     return int(np.sum(hi - lo + 1))
 
 
 def key_range(S_loc: int, q_offset: int,
-              cu_seqlens: Optional[np.ndarray] = None) -> Tuple[int, int]:
-    """Half-open range of keys any local query sees."""
-    lo, hi = visible_range(S_loc, q_offset, cu_seqlens)
+              cu_seqlens: Optional[np.ndarray] = None,
+              q_ranges: Optional[Sequence[Tuple[int, int]]] = None) -> Tuple[int, int]:
+    """Half-open range of keys any local query sees (the latent rows the
+    shard rebuilds keys and values for)."""
+    lo, hi = visible_range(S_loc, q_offset, cu_seqlens, q_ranges)
     return int(lo.min()), int(hi.max()) + 1
 
 
 def keys_needed(S_loc: int, q_offset: int,
-                cu_seqlens: Optional[np.ndarray] = None) -> int:
-    a, b = key_range(S_loc, q_offset, cu_seqlens)
+                cu_seqlens: Optional[np.ndarray] = None,
+                q_ranges: Optional[Sequence[Tuple[int, int]]] = None) -> int:
+    a, b = key_range(S_loc, q_offset, cu_seqlens, q_ranges)
     return b - a
 
 
 def attention_flops(n_h: int, d_c: int, d_rope: int, d_nope: int, d_v: int,
                     S_loc: int, q_offset: int,
                     cu_seqlens: Optional[np.ndarray] = None,
-                    backward: bool = False) -> int:
+                    backward: bool = False,
+                    q_ranges: Optional[Sequence[Tuple[int, int]]] = None) -> int:
     """Algorithmic FLOPs of the block: visible pairs plus the up-projection
     of the keys the shard needs (masked work and recomputation earn nothing;
     the backward counts the score recomputation, as flash attention does)."""
-    P = visible_pairs(S_loc, q_offset, cu_seqlens)
-    Kn = keys_needed(S_loc, q_offset, cu_seqlens)
+    P = visible_pairs(S_loc, q_offset, cu_seqlens, q_ranges)
+    Kn = keys_needed(S_loc, q_offset, cu_seqlens, q_ranges)
     d_qk = d_nope + d_rope
     if not backward:
         return 2 * n_h * (d_qk + d_v) * P + 2 * n_h * d_c * (d_nope + d_v) * Kn
@@ -155,13 +183,15 @@ def mla_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
                 scale: Optional[float] = None,
                 heads: Optional[Sequence[int]] = None,
                 rows: Optional[Sequence[int]] = None,
-                chunk: int = 512):
+                chunk: int = 512,
+                q_ranges: Optional[Sequence[Tuple[int, int]]] = None):
     """Explicit MLA forward for one query shard.
 
     q [S_loc, n_h, d_nope+d_rope], c_kv [S, d_c], k_rope [S, d_rope],
     W_UK [d_c, n_h*d_nope], W_UV [d_c, n_h*d_v]. Returns out
     [len(rows), len(heads), d_v] and lse [len(rows), len(heads)] in float64
-    (all rows/heads by default).
+    (all rows/heads by default). ``q_ranges`` replaces q_offset when the
+    shard's rows are several position blocks (see ``row_positions``).
     """
     q = np.asarray(q, F64); c_kv = np.asarray(c_kv, F64)
     k_rope = np.asarray(k_rope, F64)
@@ -171,7 +201,7 @@ def mla_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
         scale = default_scale(d_nope, d_rope)
     heads = list(range(n_h)) if heads is None else list(heads)
     rows = np.arange(S_loc) if rows is None else np.asarray(rows, dtype=np.int64)
-    lo, hi = visible_range(S_loc, q_offset, cu_seqlens)
+    lo, hi = visible_range(S_loc, q_offset, cu_seqlens, q_ranges)
     k0 = int(lo[rows].min()); k1 = int(hi[rows].max()) + 1
     keys = np.arange(k0, k1)
     out = np.zeros((len(rows), len(heads), d_v), F64)
@@ -190,7 +220,8 @@ def mla_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
 
 def mla_forward_absorbed(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
                          cu_seqlens: Optional[np.ndarray] = None,
-                         scale: Optional[float] = None):
+                         scale: Optional[float] = None,
+                         q_ranges: Optional[Sequence[Tuple[int, int]]] = None):
     """The absorbed reformulation (LAGA abstract: the form that folds W_UK
     into the query and attends in latent space). Per head h:
         s_ij  = scale * ((W_UK_h q_nope_i) . c_kv_j + q_rope_i . k_rope_j)
@@ -204,7 +235,7 @@ def mla_forward_absorbed(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
     S_loc, n_h, d_qk, d_rope, d_nope, d_v = _dims(q, k_rope, W_UV)
     if scale is None:
         scale = default_scale(d_nope, d_rope)
-    lo, hi = visible_range(S_loc, q_offset, cu_seqlens)
+    lo, hi = visible_range(S_loc, q_offset, cu_seqlens, q_ranges)
     keys = np.arange(c_kv.shape[0])
     vis = (keys[None, :] >= lo[:, None]) & (keys[None, :] <= hi[:, None])
     out = np.zeros((S_loc, n_h, d_v), F64)
@@ -225,7 +256,8 @@ def mla_backward(dout, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
                  cu_seqlens: Optional[np.ndarray] = None,
                  scale: Optional[float] = None,
                  heads: Optional[Sequence[int]] = None,
-                 chunk: int = 512):
+                 chunk: int = 512,
+                 q_ranges: Optional[Sequence[Tuple[int, int]]] = None):
     """Gradients of sum(out * dout) with respect to every input.
 
     Returns dq [S_loc,n_h,d_qk], dc_kv [S,d_c], dk_rope [S,d_rope],
@@ -242,7 +274,7 @@ def mla_backward(dout, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0,
     if scale is None:
         scale = default_scale(d_nope, d_rope)
     heads = list(range(n_h)) if heads is None else list(heads)
-    lo, hi = visible_range(S_loc, q_offset, cu_seqlens)
+    lo, hi = visible_range(S_loc, q_offset, cu_seqlens, q_ranges)
     k0 = int(lo.min()); k1 = int(hi.max()) + 1
     keys = np.arange(k0, k1)
 

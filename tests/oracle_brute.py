@@ -20,9 +20,11 @@ def sample_start(p, cu):
     return int(start)
 
 
-def brute_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset=0, cu=None, scale=None):
+def brute_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset=0, cu=None, scale=None,
+                  positions=None):
     """q[i][h][d], c_kv[t][c], k_rope[t][r], W_UK[c][h*dn+d], W_UV[c][h*dv+d]
-    as nested lists (or arrays indexed element by element)."""
+    as nested lists (or arrays indexed element by element). Row i sits at
+    positions[i] if given, else at q_offset + i."""
     S_loc, n_h, d_qk = len(q), len(q[0]), len(q[0][0])
     S, d_c = len(c_kv), len(c_kv[0])
     d_rope = len(k_rope[0])
@@ -42,7 +44,7 @@ def brute_forward(q, c_kv, k_rope, W_UK, W_UV, q_offset=0, cu=None, scale=None):
             Vfull.append([sum(float(c_kv[t][c]) * float(W_UV[c][h * d_v + d]) for c in range(d_c))
                           for d in range(d_v)])
         for i in range(S_loc):
-            p = q_offset + i
+            p = q_offset + i if positions is None else int(positions[i])
             lo = sample_start(p, cu)
             js = list(range(lo, p + 1))
             s = [scale * sum(float(q[i][h][d]) * Kfull[j][d] for d in range(d_qk)) for j in js]

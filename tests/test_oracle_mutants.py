@@ -93,3 +93,37 @@ BWD_MUTANTS = [
 @pytest.mark.parametrize("old,new", BWD_MUTANTS)
 def test_backward_mutant_caught_by_finite_differences(old, new):
     assert fd_error(mutant(old, new)) > 1e-4
+
+
+def ranges_error(mod):
+    ranges = [(3, 5), (8, 2), (16, 7)]
+    cu = [0, 4, 4, 5, 11, 18, 24]
+    x = rand_inputs(S=24, S_loc=14, seed=78)
+    out, lse = mod.mla_forward(**x, cu_seqlens=np.array(cu, np.int32), q_ranges=ranges)
+    pos = [a + k for a, n in ranges for k in range(n)]
+    bo, bl = brute_forward(x["q"].tolist(), x["c_kv"].tolist(), x["k_rope"].tolist(),
+                           x["W_UK"].tolist(), x["W_UV"].tolist(), cu=cu, positions=pos)
+    err = np.concatenate([np.abs(out - np.array(bo)).ravel(), np.abs(lse - np.array(bl)).ravel()])
+    return float(err.max()) if np.all(np.isfinite(err)) else math.inf
+
+
+RANGE_MUTANTS = [
+    # each block's rows counted from position 0 of the block list
+    ("parts = [np.arange(int(a), int(a) + int(n), dtype=np.int64) for a, n in q_ranges]",
+     "parts = [np.arange(0, int(n), dtype=np.int64) + int(q_ranges[0][0]) for a, n in q_ranges]"),
+    # blocks laid end to end in reverse
+    ("pos = np.concatenate(parts) if parts else",
+     "pos = np.concatenate(parts[::-1]) if parts else"),
+    # block end treated as inclusive, start shifted to compensate
+    ("parts = [np.arange(int(a), int(a) + int(n), dtype=np.int64) for a, n in q_ranges]",
+     "parts = [np.arange(int(a) + 1, int(a) + int(n) + 1, dtype=np.int64) for a, n in q_ranges]"),
+]
+
+
+def test_ranges_unmutated_passes():
+    assert ranges_error(M) < 1e-12
+
+
+@pytest.mark.parametrize("old,new", RANGE_MUTANTS)
+def test_ranges_mutant_caught_by_brute_force(old, new):
+    assert ranges_error(mutant(old, new)) > 1e-6

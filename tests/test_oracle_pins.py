@@ -13,7 +13,8 @@
   causal mask, Libra review page, "Axiom ledger");
 * sequence-parallel shards concatenate to the single-rank result and their
   latent / weight gradients sum to it (LAGA abstract: equivalence across SP
-  degrees);
+  degrees), for contiguous shards and for zigzag shards of two position
+  blocks each (Libra review page, Related Work beside Fig. 15);
 * gradients against central finite differences of the forward.
 """
 
@@ -200,10 +201,108 @@ def test_sequence_parallel_shard_identity(SP, cu):
         np.testing.assert_allclose(acc, ref, rtol=1e-12, atol=1e-13)
 
 
+RANGE_CASES = [
+    # (S, q_ranges, cu_seqlens): rows are the blocks laid end to end
+    (24, [(2, 3), (9, 4), (20, 2)], None),
+    (24, [(0, 1), (23, 1)], None),
+    (24, [(3, 5), (8, 2), (17, 7)], [0, 4, 4, 5, 11, 18, 24]),   # touching blocks
+    (24, [(4, 1), (10, 6)], [0, 4, 4, 5, 11, 18, 24]),           # a length-1 sample
+]
+
+
+@pytest.mark.parametrize("S,ranges,cu", RANGE_CASES)
+def test_forward_ranges_match_brute_force(S, ranges, cu):
+    S_loc = sum(n for _, n in ranges)
+    x = rand_inputs(S=S, S_loc=S_loc, seed=S + 3 * S_loc)
+    cu_a = None if cu is None else np.array(cu, dtype=np.int32)
+    out, lse = oracle.mla_forward(**x, cu_seqlens=cu_a, q_ranges=ranges)
+    pos = [a + k for a, n in ranges for k in range(n)]
+    bo, bl = brute_forward(x["q"].tolist(), x["c_kv"].tolist(), x["k_rope"].tolist(),
+                           x["W_UK"].tolist(), x["W_UV"].tolist(), cu=cu, positions=pos)
+    np.testing.assert_allclose(out, np.array(bo), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-12)
+    assert oracle.visible_pairs(S_loc, 0, cu_a, ranges) == sum(
+        brute_visible_pairs(1, p, cu) for p in pos)
+
+
+@pytest.mark.parametrize("cu", [None, [0, 7, 7, 8, 21, 32]])
+@pytest.mark.parametrize("SP", [2, 4])
+def test_zigzag_shard_identity(SP, cu):
+    """Rank r of SP holds blocks r and 2SP-1-r of 2SP equal blocks."""
+    S = 32
+    C = S // (2 * SP)
+    cu_a = None if cu is None else np.array(cu, dtype=np.int32)
+    x = rand_inputs(n_h=2, S=S, seed=23)
+    dout = np.random.default_rng(24).standard_normal((S, 2, 4))
+    o1, l1 = oracle.mla_forward(**x, cu_seqlens=cu_a)
+    g1 = oracle.mla_backward(dout, **x, cu_seqlens=cu_a)
+    out = np.full_like(o1, np.nan); lse = np.full_like(l1, np.nan); dq = np.full_like(g1[0], np.nan)
+    sums = [np.zeros_like(g) for g in g1[1:]]
+    for r in range(SP):
+        ranges = [(r * C, C), ((2 * SP - 1 - r) * C, C)]
+        rows = np.concatenate([np.arange(a, a + n) for a, n in ranges])
+        xs = dict(x, q=x["q"][rows])
+        o, l = oracle.mla_forward(**xs, cu_seqlens=cu_a, q_ranges=ranges)
+        g = oracle.mla_backward(dout[rows], **xs, cu_seqlens=cu_a, q_ranges=ranges)
+        out[rows] = o; lse[rows] = l; dq[rows] = g[0]
+        for acc, gi in zip(sums, g[1:]):
+            acc += gi
+    np.testing.assert_allclose(out, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, l1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dq, g1[0], rtol=1e-12, atol=1e-14)
+    for acc, ref in zip(sums, g1[1:]):
+        np.testing.assert_allclose(acc, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("SP", [1, 2, 4, 8])
+def test_zigzag_ranks_have_equal_pairs(SP):
+    """Block k of C rows holds k*C^2 + C(C+1)/2 causal pairs, so blocks r and
+    2SP-1-r together hold (2SP-1)C^2 + C(C+1) on every rank."""
+    C = 16
+    for r in range(SP):
+        ranges = [(r * C, C), ((2 * SP - 1 - r) * C, C)]
+        assert oracle.visible_pairs(2 * C, 0, None, ranges) == (2 * SP - 1) * C * C + C * (C + 1)
+
+
+def test_zero_gradient_for_keys_between_blocks():
+    # the middle sample [6, 12) lies between the two blocks: nobody sees it
+    cu = np.array([0, 6, 12, 18], np.int32)
+    ranges = [(2, 3), (14, 3)]
+    x = rand_inputs(S=18, S_loc=6, seed=63)
+    dout = np.random.default_rng(64).standard_normal((6, 2, 4))
+    _, dc, dkr, _, _ = oracle.mla_backward(dout, **x, cu_seqlens=cu, q_ranges=ranges)
+    assert np.all(dc[6:12] == 0) and np.all(dkr[6:12] == 0)
+    assert np.all(dc[5:6] == 0) and np.all(dc[17:] == 0)
+    assert np.any(dc[:5] != 0) and np.any(dc[12:17] != 0)
+
+
+def test_row_positions_rejects_wrong_total():
+    with pytest.raises(ValueError):
+        oracle.row_positions(5, 0, [(0, 2), (4, 2)])
+
+
 # ----------------------------------------------------------- gradients
-def _loss(x, dout, q_offset, cu):
-    out, _ = oracle.mla_forward(**x, q_offset=q_offset, cu_seqlens=cu)
+def _loss(x, dout, q_offset, cu, q_ranges=None):
+    out, _ = oracle.mla_forward(**x, q_offset=q_offset, cu_seqlens=cu, q_ranges=q_ranges)
     return float(np.sum(out * dout))
+
+
+def test_backward_ranges_directional_finite_differences():
+    ranges = [(1, 4), (9, 5)]
+    cu_a = np.array([0, 3, 3, 4, 10, 16], np.int32)
+    x = rand_inputs(n_h=2, d_c=8, d_rope=4, d_nope=4, d_v=6, S=16, S_loc=9, seed=33)
+    rng = np.random.default_rng(34)
+    dout = rng.standard_normal((9, 2, 6))
+    grads = oracle.mla_backward(dout, **x, cu_seqlens=cu_a, q_ranges=ranges)
+    eps = 1e-5
+    for name, g in zip(["q", "c_kv", "k_rope", "W_UK", "W_UV"], grads):
+        for _ in range(3):
+            v = rng.standard_normal(x[name].shape)
+            xp = dict(x); xp[name] = x[name] + eps * v
+            xm = dict(x); xm[name] = x[name] - eps * v
+            fd = (_loss(xp, dout, 0, cu_a, ranges) - _loss(xm, dout, 0, cu_a, ranges)) / (2 * eps)
+            an = float(np.sum(g * v))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
 
 
 GRAD_CASES = [(16, 16, 0, None), (16, 11, 5, [0, 3, 3, 4, 10, 16])]
