@@ -2,6 +2,7 @@
 one query shard (synthetic seeded inputs, resident in HBM before timing).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --sp-sweep 8 [--steps K]   (per-rank times of an 8-way split)
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: visible
 (query, key) pairs times 2*n_h*(d_qk+d_v) forward and 2*n_h*(3*d_qk+2*d_v)
@@ -159,8 +160,10 @@ def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
     t0 = time.perf_counter()
     while heads < min(max_heads, cfg.n_h) and time.perf_counter() - t0 < budget_s:
         h = [heads]
-        oracle.mla_forward(*args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h)
-        oracle.mla_backward(x["dout"], *args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h)
+        oracle.mla_forward(*args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h,
+                           q_ranges=cfg.q_ranges)
+        oracle.mla_backward(x["dout"], *args, q_offset=cfg.q_offset, cu_seqlens=cu, heads=h,
+                            q_ranges=cfg.q_ranges)
         heads += 1
     dt = time.perf_counter() - t0
     F = (flops(cfg, pairs, kn, False) + flops(cfg, pairs, kn, True)) * heads / cfg.n_h
@@ -168,6 +171,56 @@ def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
             "kind": "oracle",
             "sample": f"fp64 numpy oracle, forward+backward of heads 0..{heads - 1} of {cfg.n_h} "
                       f"(all {cfg.S_loc} rows), {dt:.1f} s"}
+
+
+def sp_sweep(base_name, world, steps, warmup):
+    """Time every rank's forward+backward of a `world`-way sequence-parallel
+    split of the workload's sequence, contiguous and zigzag, one rank after
+    another on this GPU. With all ranks running at once, a step lasts as
+    long as the slowest rank, so `max` is the split's step time."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_kv_amd as hla
+    import workloads
+
+    base = workloads.config(base_name)
+    S, n = base.S, base.S // world
+    out = {"sp_sweep": {"workload": base.name, "world": world, "S": S, "steps": steps}}
+    for sharding in ("contiguous", "zigzag"):
+        ms, pairs = [], []
+        for r in range(world):
+            if sharding == "contiguous":
+                cfg = base.with_(S_loc=n, q_offset=r * n, q_ranges=None)
+            else:
+                cfg = base.with_(S_loc=n, q_offset=0, q_ranges=workloads.zigzag_blocks(S, r, world))
+            x = workloads.make_inputs(cfg, with_dout=True)
+            a = [torch.from_numpy(x[k + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+                 for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV", "dout")]
+            dout = a.pop()
+            call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cfg.cu_seqlens(),
+                               backward=True, q_ranges=cfg.q_ranges)
+            pairs.append(hla.mla_laga_count(call.desc, call.cu)[0])
+            o, l = call.fwd(*a)
+            g = call.bwd(dout, *a, o, l)
+            for _ in range(warmup):
+                call.fwd(*a, out=o, lse=l)
+                call.bwd(dout, *a, o, l, grads=g)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                call.fwd(*a, out=o, lse=l)
+                call.bwd(dout, *a, o, l, grads=g)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - t0) * 1e3 / steps)
+            print(f"  {sharding} rank {r}: {ms[-1]:.3f} ms per step", file=sys.stderr, flush=True)
+            del call, a, dout, o, l, g
+            torch.cuda.empty_cache()
+        out["sp_sweep"][sharding] = {"ms_per_step": [round(v, 4) for v in ms],
+                                     "max_ms": round(max(ms), 4),
+                                     "mean_ms": round(sum(ms) / len(ms), 4),
+                                     "visible_pairs_per_head": pairs}
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -183,6 +236,9 @@ def main():
                          "(the scale reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two --counter-step counter csv files")
+    ap.add_argument("--sp-sweep", type=int, metavar="WORLD",
+                    help="time each rank of a WORLD-way contiguous and zigzag split of the "
+                         "workload's sequence, one after another (prints its own JSON line)")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from, args.workload), indent=1))
@@ -192,6 +248,10 @@ def main():
         print("bench.py measures one GPU's query shard: the library has no multi-GPU path "
               "(the latent all-gather is not part of it); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sp_sweep:
+        sp_sweep(args.workload, args.sp_sweep, args.steps, args.warmup)
+        return
 
     import numpy as np
     import torch
@@ -209,7 +269,8 @@ def main():
         else:
             dev[k] = torch.from_numpy(x[k]).cuda()
     a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
-    call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True)
+    call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True,
+                       q_ranges=cfg.q_ranges)
     pairs, k_lo, k_hi = hla.mla_laga_count(call.desc, call.cu)
     kn = k_hi - k_lo
     F_fwd, F_bwd = flops(cfg, pairs, kn, False), flops(cfg, pairs, kn, True)
@@ -286,6 +347,7 @@ def main():
         "config": {"workload": cfg.name, "n_h": cfg.n_h, "d_c": cfg.d_c, "d_rope": cfg.d_rope,
                    "d_nope": cfg.d_nope, "d_v": cfg.d_v, "S": cfg.S, "S_loc": cfg.S_loc,
                    "q_offset": cfg.q_offset, "packed_samples": None if cu is None else len(cu) - 1,
+                   "q_ranges": None if cfg.q_ranges is None else [list(r) for r in cfg.q_ranges],
                    "step": "forward+backward", "fast_path": call.fast,
                    "visible_pairs_per_head": pairs, "keys_needed": kn,
                    "flop_fwd": F_fwd, "flop_bwd": F_bwd},

@@ -20,11 +20,13 @@ __all__ = [
     "MLAError", "MLADesc", "load_library", "library_path", "mla_laga_fwd", "mla_laga_bwd",
     "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
     "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC",
+    "MLA_MAX_RANGES",
 ]
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC = 1
+MLA_MAX_RANGES = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -47,6 +49,7 @@ class MLADesc(ctypes.Structure):
         ("S", ctypes.c_int64), ("S_loc", ctypes.c_int64), ("q_offset", ctypes.c_int64),
         ("in_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("n_ranges", ctypes.c_int32), ("q_ranges", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -127,9 +130,19 @@ def _cu_ptr(cu: Optional[np.ndarray]):
     return None if cu is None else cu.ctypes.data_as(_I32P)
 
 
+def _host_ranges(q_ranges) -> Optional[np.ndarray]:
+    if q_ranges is None:
+        return None
+    r = np.ascontiguousarray(np.asarray(q_ranges, dtype=np.int64).reshape(-1, 2))
+    return r
+
+
 def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: torch.Tensor,
               q_offset: int = 0, cu_seqlens=None, softmax_scale: Optional[float] = None,
-              generic: bool = False) -> Tuple[MLADesc, Optional[np.ndarray]]:
+              generic: bool = False, q_ranges=None
+              ) -> Tuple[MLADesc, Optional[np.ndarray], Optional[np.ndarray]]:
+    """Descriptor plus the host arrays it points at (cu_seqlens, ranges):
+    keep those alive as long as the descriptor is used."""
     S_loc, n_h, d_qk = q.shape
     S, d_c = c_kv.shape
     d_rope = k_rope.shape[1]
@@ -142,7 +155,10 @@ def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: t
     d.in_dtype = _in_dtype(q)
     d.flags = MLA_FLAG_GENERIC if generic else 0
     d.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    return d, cu
+    rng = _host_ranges(q_ranges)
+    d.n_ranges = 0 if rng is None else len(rng)
+    d.q_ranges = None if rng is None else rng.ctypes.data_as(_I64P)
+    return d, cu, rng
 
 
 def _check_inputs(d: MLADesc, tensors):
@@ -220,9 +236,9 @@ class MLACall:
 
     def __init__(self, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
                  softmax_scale: Optional[float] = None, generic: bool = False,
-                 backward: bool = False):
-        self.desc, self.cu = make_desc(q, c_kv, k_rope, W_UV, q_offset, cu_seqlens,
-                                       softmax_scale, generic)
+                 backward: bool = False, q_ranges=None):
+        self.desc, self.cu, self.ranges = make_desc(q, c_kv, k_rope, W_UV, q_offset, cu_seqlens,
+                                                    softmax_scale, generic, q_ranges)
         _check_inputs(self.desc, _input_specs(self.desc, q, c_kv, k_rope, W_UK, W_UV))
         self.device = q.device
         self.cu_dev = None if self.cu is None else torch.from_numpy(self.cu).to(self.device)
@@ -268,17 +284,20 @@ class MLACall:
 
 
 def mla_laga_fwd(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
-                 softmax_scale: Optional[float] = None, generic: bool = False):
-    """out [S_loc,n_h,d_v] fp32 and lse [S_loc,n_h] fp32 for one query shard."""
-    call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic)
+                 softmax_scale: Optional[float] = None, generic: bool = False, q_ranges=None):
+    """out [S_loc,n_h,d_v] fp32 and lse [S_loc,n_h] fp32 for one query shard.
+    q_ranges: optional (start, length) position blocks of the rows (q_offset 0)."""
+    call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic,
+                   q_ranges=q_ranges)
     return call.fwd(q, c_kv, k_rope, W_UK, W_UV)
 
 
 def mla_laga_bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, q_offset: int = 0,
-                 cu_seqlens=None, softmax_scale: Optional[float] = None, generic: bool = False):
+                 cu_seqlens=None, softmax_scale: Optional[float] = None, generic: bool = False,
+                 q_ranges=None):
     """(dq, dc_kv, dk_rope, dW_UK, dW_UV), all fp32, gradients of sum(out*dout)."""
     call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic,
-                   backward=True)
+                   backward=True, q_ranges=q_ranges)
     d = call.desc
     _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))] +
                   _input_specs(d, q, c_kv, k_rope, W_UK, W_UV)[:1])

@@ -178,7 +178,42 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
       if (cu[k + 1] < cu[k])
         return fail(MLA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", k);
   }
+  if (d->n_ranges < 0 || d->n_ranges > MLA_MAX_RANGES)
+    return fail(MLA_ERR_INVALID_ARG, "n_ranges must be in [0, %d] (got %d)", MLA_MAX_RANGES,
+                d->n_ranges);
   Plan& P = *p;
+  P.rm = RowMap{};
+  if (d->n_ranges == 0) {
+    P.rm.n = 1;
+    P.rm.row0[1] = static_cast<int>(d->S_loc);
+    P.rm.pos0[0] = static_cast<int>(d->q_offset);
+  } else {
+    const int64_t* qr = d->q_ranges;
+    if (!qr) return fail(MLA_ERR_INVALID_ARG, "n_ranges > 0 needs q_ranges");
+    if (d->q_offset != 0) return fail(MLA_ERR_INVALID_ARG, "q_offset must be 0 when n_ranges > 0");
+    int64_t rows = 0, prev_end = 0;
+    P.rm.n = 0;
+    for (int b = 0; b < d->n_ranges; ++b) {
+      const int64_t a = qr[2 * b], n = qr[2 * b + 1];
+      if (a < 0 || n < 0 || a + n > d->S)
+        return fail(MLA_ERR_INVALID_ARG, "q_ranges[%d] = (%lld, %lld) is outside [0, S)", b,
+                    (long long)a, (long long)n);
+      if (b > 0 && a < prev_end)
+        return fail(MLA_ERR_INVALID_ARG, "q_ranges must be ascending and disjoint (block %d starts at %lld, before %lld)",
+                    b, (long long)a, (long long)prev_end);
+      prev_end = a + n;
+      if (n == 0) continue;
+      P.rm.row0[P.rm.n] = static_cast<int>(rows);
+      P.rm.pos0[P.rm.n] = static_cast<int>(a);
+      ++P.rm.n;
+      rows += n;
+    }
+    if (rows != d->S_loc)
+      return fail(MLA_ERR_INVALID_ARG, "q_ranges hold %lld rows, S_loc is %lld", (long long)rows,
+                  (long long)d->S_loc);
+    P.rm.row0[P.rm.n] = static_cast<int>(rows);
+    if (P.rm.n == 0) P.rm.n = 1;  // S_loc = 0: one empty block
+  }
   P.n_h = d->n_h; P.d_c = d->d_c; P.d_rope = d->d_rope; P.d_nope = d->d_nope; P.d_v = d->d_v;
   P.d_qk = d->d_nope + d->d_rope; P.n_seqs = d->n_seqs;
   P.S = d->S; P.S_loc = d->S_loc; P.q_offset = d->q_offset;
@@ -190,8 +225,10 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(P.d_qk));
   if (!(P.scale < INFINITY)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (P.S_loc > 0) {
-    P.key_lo = seg_lo_host(cu, P.n_seqs, P.q_offset);
-    P.key_hi = P.q_offset + P.S_loc;
+    // positions increase with the row: the first row has the lowest sample
+    // start, the last row the highest position
+    P.key_lo = seg_lo_host(cu, P.n_seqs, rm_pos(P.rm, 0));
+    P.key_hi = rm_pos(P.rm, static_cast<int>(P.S_loc - 1)) + 1;
   } else {
     P.key_lo = P.key_hi = 0;
   }
@@ -199,7 +236,7 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   P.Kpad = align_up(P.Kn, kKeyTile);
   int64_t pairs = 0;
   for (int64_t i = 0; i < P.S_loc; ++i) {
-    const int64_t pos = P.q_offset + i;
+    const int64_t pos = rm_pos(P.rm, static_cast<int>(i));
     pairs += pos - seg_lo_host(cu, P.n_seqs, pos) + 1;
   }
   P.visible_pairs = pairs;

@@ -36,7 +36,7 @@ constexpr int kMaxOrderTiles = 2048;
 // qorder[0 .. n_qt) / korder[0 .. n_kt) = query tiles (256 rows) / key tiles
 // (128 workspace keys) of a packed call by decreasing number of visible
 // (row, key) pairs; korder may be null. n_qt, n_kt <= kMaxOrderTiles.
-mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, int64_t q_offset,
+mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, const RowMap& rm,
                              int64_t key_lo, int64_t Kn, int n_qt, int n_kt, int* qorder,
                              int* korder, hipStream_t st);
 

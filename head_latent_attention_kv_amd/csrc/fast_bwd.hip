@@ -55,7 +55,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
                 const float* __restrict__ out, const float* __restrict__ lse,
                 const int32_t* __restrict__ cu, float* __restrict__ D, _Float16* __restrict__ Qn,
                 _Float16* __restrict__ dOn, uint32_t* __restrict__ info, int n_h, int n_seqs,
-                int64_t S_loc, int64_t S_pad, int64_t q_offset) {
+                int64_t S_loc, int64_t S_pad, RowMap rm) {
   const int h = blockIdx.y;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -77,8 +77,9 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
       const bool ok = i < S_loc;
       blk[r] = __float_as_uint(ok ? lse[i * n_h + h] * kLog2e : 0.f);
       blk[32 + r] = __float_as_uint(v);
-      blk[64 + r] = ok ? static_cast<uint32_t>(seg_lo_dev(cu, n_seqs, q_offset + i)) : 0x7fffffffu;
-      blk[96 + r] = ok ? static_cast<uint32_t>(q_offset + i) : 0xffffffffu;
+      const int pos = rm_pos(rm, static_cast<int>(i));
+      blk[64 + r] = ok ? static_cast<uint32_t>(seg_lo_dev(cu, n_seqs, pos)) : 0x7fffffffu;
+      blk[96 + r] = ok ? static_cast<uint32_t>(pos) : 0xffffffffu;
     }
   }
   // q then dout, 16 bytes per thread
@@ -145,7 +146,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
                     const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
                     _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
                     float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
-                    int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+                    RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
   constexpr int BYTES = kDK ? SK_BYTES : SV_BYTES;
   constexpr int INFO = kDK ? SK_INFO : SV_INFO;
   constexpr int DON_ROW = kDK ? DONK_ROW : DONV_ROW;
@@ -178,7 +179,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
 
   // query rows that see any key of the workgroup: from the first row at or
   // past its first key to the last row whose sample starts by its last key
-  const int i_begin = max(gk_min - q_offset, 0);
+  const int i_begin = rm_rows_below(rm, gk_min);
   int i_end = S_loc;
   if (n_seqs > 0) {
     // first sample start after gk_max (none: S): rows from there on see nothing here
@@ -187,7 +188,7 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
       const int mid = (lo_i + hi_i) >> 1;
       if (cu[mid] <= gk_max) lo_i = mid; else hi_i = mid;
     }
-    if (lo_i + 1 <= n_seqs) i_end = min(i_end, cu[lo_i + 1] - q_offset);
+    if (lo_i + 1 <= n_seqs) i_end = rm_rows_below(rm, cu[lo_i + 1]);
   }
   const int qb_begin = (i_begin / QB) * QB;
   const int nq = i_end > qb_begin ? (i_end - qb_begin + QB - 1) / QB : 0;
@@ -260,9 +261,10 @@ attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict_
       const int q0 = qb + 32 * mt;
       const float* rinfo = reinterpret_cast<const float*>(base + INFO + mt * 512);
       const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 64);
-      // positions of the sub-block's rows: q_offset + q0 ..; rows past S_loc have p = -1
-      const int p_first = q_offset + q0;
-      const int p_last = q_offset + min(q0 + 32, S_loc) - 1;
+      // first and last position of the sub-block's rows (positions increase
+      // with the row; rows past S_loc hold position -1)
+      const int p_first = iinfo[32];
+      const int p_last = iinfo[31 + max(min(32, S_loc - q0), 1)];
       const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
       if (skip) continue;
       const bool full = q0 + 32 <= S_loc && p_first >= gw_max && iinfo[31] <= gw_min;
@@ -426,7 +428,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                      const int* __restrict__ korder,
                      _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
                      float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
-                     int q_offset, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+                     RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 4 * 2 * 2048];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -445,7 +447,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
 
   // query rows that see any key of the workgroup: from the first row at or
   // past its first key to the last row whose sample starts by its last key
-  const int i_begin = max(gk_min - q_offset, 0);
+  const int i_begin = rm_rows_below(rm, gk_min);
   int i_end = S_loc;
   if (n_seqs > 0) {
     // first sample start after gk_max (none: S): rows from there on see nothing here
@@ -454,7 +456,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
       const int mid = (lo_i + hi_i) >> 1;
       if (cu[mid] <= gk_max) lo_i = mid; else hi_i = mid;
     }
-    if (lo_i + 1 <= n_seqs) i_end = min(i_end, cu[lo_i + 1] - q_offset);
+    if (lo_i + 1 <= n_seqs) i_end = rm_rows_below(rm, cu[lo_i + 1]);
   }
   const int qb_begin = (i_begin / QB) * QB;
   const int nq = i_end > qb_begin ? (i_end - qb_begin + QB - 1) / QB : 0;
@@ -543,9 +545,10 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         char* xs = xslot + mt * 2048;          // sub-block parity: buffer mt
         const float* rinfo = reinterpret_cast<const float*>(base + P_INFO + mt * 512);
         const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 64);
-        // positions of the sub-block's rows: q_offset + q0 ..; rows past S_loc have p = -1
-        const int p_first = q_offset + q0;
-        const int p_last = q_offset + min(q0 + 32, S_loc) - 1;
+        // first and last position of the sub-block's rows (positions increase
+        // with the row; rows past S_loc hold position -1)
+        const int p_first = iinfo[32];
+        const int p_last = iinfo[31 + max(min(32, S_loc - q0), 1)];
         // the same for both waves of a pair (same keys, same rows)
         const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
         half8 pf[2];
@@ -712,11 +715,10 @@ static_assert(D_V % 1024 == 0 && D_BYTES % 1024 == 0, "dq stage layout");
 
 __global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
-                   const float* __restrict__ lse, const float* __restrict__ D,
-                   const _Float16* __restrict__ Kfull, const _Float16* __restrict__ Vkm,
-                   const int32_t* __restrict__ cu, const int* __restrict__ qorder,
-                   float* __restrict__ dq, int n_h, int n_seqs, int S_loc, int S_pad, int q_offset,
-                   int key_lo, int Kpad, int n_qt, float scale, float scale_log2) {
+                   const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
+                   const _Float16* __restrict__ Vkm, const int* __restrict__ qorder,
+                   float* __restrict__ dq, int n_h, int S_loc, int S_pad, int key_lo, int Kpad,
+                   int n_qt, float scale, float scale_log2) {
   constexpr int NP = (D_PIECES + 7) / 8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * D_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -730,14 +732,21 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wq0 = q0 + 32 * w;
   const int i = wq0 + lr;
   const bool valid = i < S_loc;
-  const int p = valid ? q_offset + i : -1;
-  const int lo = valid ? static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + i)) : 0;
-  const float L2 = valid ? lse[static_cast<int64_t>(i) * n_h + h] * kLog2e : 0.f;
-  const float Di = valid ? D[static_cast<int64_t>(h) * S_pad + i] : 0.f;
+  // the rows' lse*log2(e), D, sample start and position, as the backward
+  // prep stored them (the wave's 32 rows are one info block). Positions
+  // increase with the row, so a row range's extremes sit at its ends.
+  const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / 32) * 128;
   const bool wave_live = wq0 < S_loc;
-  const int wp_min = q_offset + wq0, wp_max = q_offset + min(S_loc - 1, wq0 + 31);
-  const int wlo_min = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_min)) : 0;
-  const int wlo_max = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_max)) : 0;
+  const uint32_t* blk = info_h + (wq0 >> 5) * 128;
+  const int n_last = wave_live ? min(S_loc - 1 - wq0, 31) : 0;  // the wave's last valid row
+  const float L2 = valid ? __uint_as_float(blk[lr]) : 0.f;
+  const float Di = valid ? __uint_as_float(blk[32 + lr]) : 0.f;
+  const int lo = valid ? static_cast<int>(blk[64 + lr]) : 0;
+  const int p = valid ? static_cast<int>(blk[96 + lr]) : -1;
+  const int wp_min = wave_live ? static_cast<int>(blk[96]) : 0;
+  const int wp_max = wave_live ? static_cast<int>(blk[96 + n_last]) : -1;
+  const int wlo_min = wave_live ? static_cast<int>(blk[64]) : 0;
+  const int wlo_max = wave_live ? static_cast<int>(blk[64 + n_last]) : 0;
 
   half8 qf[12], df[8];
 #pragma unroll
@@ -762,8 +771,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 
   const int i_last = min(S_loc - 1, q0 + QW - 1);
-  const int kb_begin = ((static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + q0)) - key_lo) / KS) * KS;
-  const int kb_end = q_offset + i_last + 1 - key_lo;
+  const int kb_begin = ((static_cast<int>(info_h[(q0 >> 5) * 128 + 64]) - key_lo) / KS) * KS;
+  const int kb_end = static_cast<int>(info_h[(i_last >> 5) * 128 + 96 + (i_last & 31)]) + 1 - key_lo;
   const int nblk = (kb_end - kb_begin + KS - 1) / KS;
 
   const _Float16* Kh = Kfull + static_cast<int64_t>(h) * Kpad * DQK;
@@ -952,7 +961,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   float* dKr = reinterpret_cast<float*>(at(L.dKrope));
   uint32_t* info = reinterpret_cast<uint32_t*>(at(L.info));
   const int S_loc = static_cast<int>(p.S_loc), Sp = static_cast<int>(S_pad),
-            q_off = static_cast<int>(p.q_offset), key_lo = static_cast<int>(p.key_lo),
+            key_lo = static_cast<int>(p.key_lo),
             Kpad = static_cast<int>(p.Kpad);
   mla_status s;
 
@@ -974,7 +983,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(S_pad / 64), p.n_h), dim3(256),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
                        out, lse, cu_dev, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
-                       S_pad, p.q_offset);
+                       S_pad, p.rm);
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
@@ -985,7 +994,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     if (p.n_seqs > 0 && n_qt <= kMaxOrderTiles && n_kt <= kMaxOrderTiles) {
       qorder = reinterpret_cast<int*>(at(L.order));
       korder = qorder + n_qt;
-      if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kn, n_qt, n_kt,
+      if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.rm, p.key_lo, p.Kn, n_qt, n_kt,
                                  qorder, bwd_paired() ? korder : nullptr, st)) != MLA_OK)
         return s;
       if (!bwd_paired()) korder = nullptr;
@@ -996,7 +1005,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
                        st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
-                       Sp, q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+                       Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   } else {
     const int n_kt = static_cast<int>(p.Kpad / KW);
     const unsigned grid = static_cast<unsigned>(n_kt * p.n_h);
@@ -1004,14 +1013,14 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
       KernelTimer kt("attn_bwd_dk", st);
       hipLaunchKernelGGL(attn_bwd_dkv_kernel<true>, dim3(grid), dim3(512), 0, st, Qn, dOn,
                          info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
-                         q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+                         p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
     }
     if ((s = check_launch("attention backward dK")) != MLA_OK) return s;
     {
       KernelTimer kt("attn_bwd_dv", st);
       hipLaunchKernelGGL(attn_bwd_dkv_kernel<false>, dim3(grid), dim3(512), 0, st, Qn, dOn,
                          info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
-                         q_off, key_lo, Kpad, n_kt, p.scale, scale_log2);
+                         p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
     }
   }
   if ((s = check_launch("attention backward dV")) != MLA_OK) return s;
@@ -1020,8 +1029,8 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     KernelTimer kt("attn_bwd_dq", st);
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                        0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       lse, D, Kfull, Vkm, cu_dev, qorder, dq, p.n_h, p.n_seqs, S_loc, Sp, q_off,
-                       key_lo, Kpad, n_qt, p.scale, scale_log2);
+                       info, Kfull, Vkm, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt, p.scale,
+                       scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(NW * 64)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfull,
                 const _Float16* __restrict__ Vt, const int32_t* __restrict__ cu,
                 const int* __restrict__ order, float* __restrict__ out, float* __restrict__ lse,
-                int n_h, int n_seqs, int S_loc, int q_offset, int key_lo, int Kpad, int n_qt,
+                int n_h, int n_seqs, int S_loc, RowMap rm, int key_lo, int Kpad, int n_qt,
                 float scale_log2) {
   static_assert(NT * NW * 32 == FQ, "workgroup covers 256 query rows");
   constexpr int NP = (STAGE_PIECES + NW - 1) / NW;  // DMA pieces per wave and stage
@@ -84,24 +84,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
   const int q0 = qt * FQ;
   const int wq0 = q0 + NT * 32 * w;
 
-  // this lane's query columns; rows past S_loc see nothing
+  // this lane's query columns; rows past S_loc see nothing. Positions
+  // increase with the row, so a row range's extreme positions and sample
+  // starts sit at its ends.
   int p[NT], lo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int i = wq0 + 32 * nt + lr;
-    p[nt] = i < S_loc ? q_offset + i : -1;
-    lo[nt] = i < S_loc ? static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + i)) : 0;
+    p[nt] = i < S_loc ? rm_pos(rm, i) : -1;
+    lo[nt] = i < S_loc ? static_cast<int>(seg_lo_dev(cu, n_seqs, p[nt])) : 0;
   }
   const bool wave_live = wq0 < S_loc;
   const int wi_last = min(S_loc - 1, wq0 + NT * 32 - 1);
-  const int wp_min = q_offset + wq0, wp_max = q_offset + wi_last;
+  const int wp_min = rm_pos(rm, wq0), wp_max = rm_pos(rm, wi_last);
   const int wlo_min = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_min)) : 0;
   const int wlo_max = wave_live ? static_cast<int>(seg_lo_dev(cu, n_seqs, wp_max)) : 0;
 
   // key blocks (workspace rows) the workgroup's rows can see
   const int i_last = min(S_loc - 1, q0 + FQ - 1);
-  const int kb_begin = ((static_cast<int>(seg_lo_dev(cu, n_seqs, q_offset + q0)) - key_lo) / FK) * FK;
-  const int kb_end = q_offset + i_last + 1 - key_lo;
+  const int kb_begin = ((static_cast<int>(seg_lo_dev(cu, n_seqs, rm_pos(rm, q0))) - key_lo) / FK) * FK;
+  const int kb_end = rm_pos(rm, i_last) + 1 - key_lo;
   const int nblk = (kb_end - kb_begin + FK - 1) / FK;
 
   // DMA: piece I (wave instruction) fills stage bytes [1024 I, 1024 I + 1024),
@@ -367,22 +369,21 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   int* order = nullptr;
   if (p.n_seqs > 0 && n_qt <= kMaxOrderTiles) {
     order = reinterpret_cast<int*>(ws + L.order);
-    if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kn, n_qt, 0,
+    if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.rm, p.key_lo, p.Kn, n_qt, 0,
                                order, nullptr, st)) != MLA_OK)
       return s;
   }
-  const int S_loc = static_cast<int>(p.S_loc), q_off = static_cast<int>(p.q_offset),
-            key_lo = static_cast<int>(p.key_lo), Kpad = static_cast<int>(p.Kpad);
+  const int S_loc = static_cast<int>(p.S_loc), key_lo = static_cast<int>(p.key_lo), Kpad = static_cast<int>(p.Kpad);
   {
     KernelTimer kt("attn_fwd", st);
     if (attn_fwd_variant() == 2)
       hipLaunchKernelGGL((attn_fwd_kernel<2, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                          st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
-                         p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
+                         p.n_seqs, S_loc, p.rm, key_lo, Kpad, n_qt, scale_log2);
     else
       hipLaunchKernelGGL((attn_fwd_kernel<1, 8>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
                          st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
-                         p.n_seqs, S_loc, q_off, key_lo, Kpad, n_qt, scale_log2);
+                         p.n_seqs, S_loc, p.rm, key_lo, Kpad, n_qt, scale_log2);
   }
   return check_launch("attention forward");
 }

@@ -271,13 +271,13 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
 // Longest-processing-time order of the attention work tiles of a packed
 // (varlen) call, one workgroup of 1024 threads. A query tile holds 256 rows;
 // its cost is the number of (row, key) pairs its rows see, sum over rows of
-// p - seg_lo(p) + 1 (p = q_offset + i). A key tile holds 128 workspace keys;
-// its cost is the number of rows that see each key k (global key_lo + t):
-// rows with max(k, q_offset) <= p < min(end of k's sample, q_offset + S_loc).
+// p - seg_lo(p) + 1 (p the row's position). A key tile holds 128 workspace
+// keys; its cost is the number of rows that see each key k (global
+// key_lo + t): rows with k <= p < end of k's sample.
 // qorder / korder receive the tile indices by decreasing cost (ties: later
 // query tiles first, earlier key tiles first); korder may be null.
 __global__ void __launch_bounds__(1024)
-tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, int q_offset, int key_lo,
+tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, RowMap rm, int key_lo,
                   int Kn, int n_qt, int n_kt, int* __restrict__ qorder, int* __restrict__ korder) {
   __shared__ unsigned long long cq[kMaxOrderTiles], ck[kMaxOrderTiles];
   const int tid = threadIdx.x;
@@ -285,7 +285,7 @@ tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, int q_o
   for (int t = tid; t < n_kt; t += 1024) ck[t] = 0;
   __syncthreads();
   for (int i = tid; i < S_loc; i += 1024) {
-    const int pos = q_offset + i;
+    const int pos = rm_pos(rm, i);
     atomicAdd(&cq[i >> 8], static_cast<unsigned long long>(pos - seg_lo_dev(cu, n_seqs, pos) + 1));
   }
   if (korder != nullptr) {
@@ -298,8 +298,8 @@ tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, int q_o
         if (cu[mid] <= k) lo_i = mid; else hi_i = mid;
       }
       const int end = lo_i + 1 <= n_seqs ? cu[lo_i + 1] : 0x7fffffff;
-      const int first = max(k, q_offset), last = min(end, q_offset + S_loc);
-      if (last > first) atomicAdd(&ck[t >> 7], static_cast<unsigned long long>(last - first));
+      const int seen = rm_rows_below(rm, end) - rm_rows_below(rm, k);
+      if (seen > 0) atomicAdd(&ck[t >> 7], static_cast<unsigned long long>(seen));
     }
   }
   __syncthreads();
@@ -477,14 +477,14 @@ mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, i
   return check_launch(name);
 }
 
-mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, int64_t q_offset,
+mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, const RowMap& rm,
                              int64_t key_lo, int64_t Kn, int n_qt, int n_kt, int* qorder,
                              int* korder, hipStream_t st) {
   if (n_qt > kMaxOrderTiles || n_kt > kMaxOrderTiles)
     return fail(MLA_ERR_UNSUPPORTED, "tile order: more than %d tiles", kMaxOrderTiles);
   KernelTimer kt("tile_order", st);
   hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(1024), 0, st, cu, n_seqs,
-                     static_cast<int>(S_loc), static_cast<int>(q_offset), static_cast<int>(key_lo),
+                     static_cast<int>(S_loc), rm, static_cast<int>(key_lo),
                      static_cast<int>(Kn), n_qt, n_kt, qorder, korder);
   return check_launch("tile order");
 }

@@ -57,7 +57,7 @@ template <bool BF16>
 __global__ void g_attn_fwd(const void* __restrict__ q, const float* __restrict__ K,
                            const float* __restrict__ V, const int32_t* __restrict__ cu,
                            float* __restrict__ out, float* __restrict__ lse, int n_h, int d_qk,
-                           int d_v, int n_seqs, int64_t S_loc, int64_t q_offset, int64_t key_lo,
+                           int d_v, int n_seqs, int64_t S_loc, RowMap rm, int64_t key_lo,
                            int64_t Kn, float scale) {
   extern __shared__ float smem[];
   float* sQ = smem;                     // [kRows][d_qk]
@@ -72,7 +72,7 @@ __global__ void g_attn_fwd(const void* __restrict__ q, const float* __restrict__
   const int c1 = min(d_v, c0 + slice);
   const int64_t i = i0 + r;
   const bool valid = i < S_loc;
-  const int64_t p = q_offset + i;
+  const int64_t p = rm_pos(rm, static_cast<int>(i));
   const int64_t lo = valid ? seg_lo_dev(cu, n_seqs, p) : 0;
   const int64_t hi = valid ? p : -1;  // invalid rows see nothing
 
@@ -82,8 +82,9 @@ __global__ void g_attn_fwd(const void* __restrict__ q, const float* __restrict__
   }
   // key range of the workgroup, in workspace rows
   const int64_t i_last = min(S_loc - 1, i0 + kRows - 1);
-  const int64_t j_begin = seg_lo_dev(cu, n_seqs, q_offset + i0) - key_lo;
-  const int64_t j_end = q_offset + i_last + 1 - key_lo;
+  // (positions increase with the row: the ends of the row range bound it)
+  const int64_t j_begin = seg_lo_dev(cu, n_seqs, rm_pos(rm, static_cast<int>(i0))) - key_lo;
+  const int64_t j_end = rm_pos(rm, static_cast<int>(i_last)) + 1 - key_lo;
 
   float m = -INFINITY, l = 0.f;
   float o[kMaxSlice];
@@ -142,7 +143,7 @@ __global__ void g_attn_bwd_dq(const void* __restrict__ q, const void* __restrict
                               const float* __restrict__ K, const float* __restrict__ V,
                               const float* __restrict__ lse, const float* __restrict__ D,
                               const int32_t* __restrict__ cu, float* __restrict__ dq, int n_h,
-                              int d_qk, int d_v, int n_seqs, int64_t S_loc, int64_t q_offset,
+                              int d_qk, int d_v, int n_seqs, int64_t S_loc, RowMap rm,
                               int64_t key_lo, int64_t Kn, float scale) {
   extern __shared__ float smem[];
   float* sQ = smem;                    // [kRows][d_qk]
@@ -158,7 +159,7 @@ __global__ void g_attn_bwd_dq(const void* __restrict__ q, const void* __restrict
   const int c1 = min(d_qk, c0 + slice);
   const int64_t i = i0 + r;
   const bool valid = i < S_loc;
-  const int64_t p = q_offset + i;
+  const int64_t p = rm_pos(rm, static_cast<int>(i));
   const int64_t lo = valid ? seg_lo_dev(cu, n_seqs, p) : 0;
   const int64_t hi = valid ? p : -1;
   const float L = valid ? lse[i * n_h + h] : 0.f;
@@ -173,8 +174,9 @@ __global__ void g_attn_bwd_dq(const void* __restrict__ q, const void* __restrict
     sO[e] = ii < S_loc ? load_in<BF16>(dout, (ii * n_h + h) * d_v + e % d_v) : 0.f;
   }
   const int64_t i_last = min(S_loc - 1, i0 + kRows - 1);
-  const int64_t j_begin = seg_lo_dev(cu, n_seqs, q_offset + i0) - key_lo;
-  const int64_t j_end = q_offset + i_last + 1 - key_lo;
+  // (positions increase with the row: the ends of the row range bound it)
+  const int64_t j_begin = seg_lo_dev(cu, n_seqs, rm_pos(rm, static_cast<int>(i0))) - key_lo;
+  const int64_t j_end = rm_pos(rm, static_cast<int>(i_last)) + 1 - key_lo;
 
   float g[kMaxSlice];
 #pragma unroll
@@ -218,7 +220,7 @@ __global__ void g_attn_bwd_dkdv(const void* __restrict__ q, const void* __restri
                                 const float* __restrict__ lse, const float* __restrict__ D,
                                 const int32_t* __restrict__ cu, float* __restrict__ dK,
                                 float* __restrict__ dV, int n_h, int d_qk, int d_v, int n_seqs,
-                                int64_t S_loc, int64_t q_offset, int64_t key_lo, int64_t Kn,
+                                int64_t S_loc, RowMap rm, int64_t key_lo, int64_t Kn,
                                 float scale) {
   extern __shared__ float smem[];
   constexpr int kQ = 16;                 // query rows staged per step
@@ -229,6 +231,7 @@ __global__ void g_attn_bwd_dkdv(const void* __restrict__ q, const void* __restri
   float* sL = sO + kQ * d_v;             // [kQ]
   float* sD = sL + kQ;                   // [kQ]
   int64_t* sLo = reinterpret_cast<int64_t*>(sD + kQ);  // [kQ]
+  int64_t* sP = sLo + kQ;                // [kQ] row positions
   const int h = blockIdx.y;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRows;  // workspace row
   const int r = threadIdx.x % kRows;
@@ -255,11 +258,10 @@ __global__ void g_attn_bwd_dkdv(const void* __restrict__ q, const void* __restri
   // sample starts past the block's last key see none of it (seg_lo grows with p)
   const int64_t j_first = key_lo + t0;
   const int64_t j_last = key_lo + min(Kn - 1, t0 + kRows - 1);
-  int64_t i_begin = j_first - q_offset;
-  if (i_begin < 0) i_begin = 0;
+  const int64_t i_begin = rm_rows_below(rm, j_first);
   for (int64_t ib = i_begin; ib < S_loc; ib += kQ) {
     __syncthreads();
-    if (seg_lo_dev(cu, n_seqs, q_offset + ib) > j_last) break;  // uniform
+    if (seg_lo_dev(cu, n_seqs, rm_pos(rm, static_cast<int>(ib))) > j_last) break;  // uniform
     for (int e = threadIdx.x; e < kQ * d_qk; e += blockDim.x) {
       const int64_t ii = ib + e / d_qk;
       sQ[e] = ii < S_loc ? load_in<BF16>(q, (ii * n_h + h) * d_qk + e % d_qk) : 0.f;
@@ -273,13 +275,14 @@ __global__ void g_attn_bwd_dkdv(const void* __restrict__ q, const void* __restri
       const bool ok = ii < S_loc;
       sL[threadIdx.x] = ok ? lse[ii * n_h + h] : 0.f;
       sD[threadIdx.x] = ok ? D[ii * n_h + h] : 0.f;
-      sLo[threadIdx.x] = ok ? seg_lo_dev(cu, n_seqs, q_offset + ii) : INT64_MAX;
+      sLo[threadIdx.x] = ok ? seg_lo_dev(cu, n_seqs, rm_pos(rm, static_cast<int>(ii))) : INT64_MAX;
+      sP[threadIdx.x] = ok ? rm_pos(rm, static_cast<int>(ii)) : -1;
     }
     __syncthreads();
     if (!valid) continue;
     for (int qq = 0; qq < kQ; ++qq) {
       const int64_t ii = ib + qq;
-      const int64_t p = q_offset + ii;
+      const int64_t p = sP[qq];
       if (ii >= S_loc || j > p || j < sLo[qq]) continue;
       float s = 0.f;
       for (int d = 0; d < d_qk; ++d) s += sQ[qq * d_qk + d] * sK[r * d_qk + d];
@@ -425,7 +428,7 @@ mla_status generic_fwd_t(const Plan& p, const void* q, const void* c_kv, const v
   {
     KernelTimer kt("plain_attn_fwd", st);
     hipLaunchKernelGGL(g_attn_fwd<BF16>, grid, dim3(kRows * kSlices), lds, st, q, K, V, cu, out,
-                       lse, p.n_h, p.d_qk, p.d_v, p.n_seqs, p.S_loc, p.q_offset, p.key_lo, p.Kn,
+                       lse, p.n_h, p.d_qk, p.d_v, p.n_seqs, p.S_loc, p.rm, p.key_lo, p.Kn,
                        p.scale);
   }
   return check_launch("plain attention forward");
@@ -464,7 +467,7 @@ mla_status generic_bwd_t(const Plan& p, const void* dout, const void* q, const v
     {
       KernelTimer kt("plain_attn_bwd_dq", st);
       hipLaunchKernelGGL(g_attn_bwd_dq<BF16>, grid, dim3(kRows * kSlices), lds, st, q, dout, K, V,
-                         lse, D, cu, dq, p.n_h, p.d_qk, p.d_v, p.n_seqs, p.S_loc, p.q_offset,
+                         lse, D, cu, dq, p.n_h, p.d_qk, p.d_v, p.n_seqs, p.S_loc, p.rm,
                          p.key_lo, p.Kn, p.scale);
     }
     if (mla_status s = check_launch("plain backward dq"); s != MLA_OK) return s;
@@ -472,14 +475,14 @@ mla_status generic_bwd_t(const Plan& p, const void* dout, const void* q, const v
   {
     constexpr int kQ = 16;
     const size_t lds = sizeof(float) * (kRows * (p.d_qk + p.d_v) + kQ * (p.d_qk + p.d_v) +
-                                        2 * kQ) + sizeof(int64_t) * kQ;
+                                        2 * kQ) + sizeof(int64_t) * 2 * kQ;
     if (mla_status s = allow_lds(g_attn_bwd_dkdv<BF16>, lds); s != MLA_OK) return s;
     dim3 grid(static_cast<unsigned>((p.Kn + kRows - 1) / kRows), p.n_h);
     {
       KernelTimer kt("plain_attn_bwd_dkdv", st);
       hipLaunchKernelGGL(g_attn_bwd_dkdv<BF16>, grid, dim3(kRows * kSlices), lds, st, q, dout, K,
                          V, lse, D, cu, dK, dV, p.n_h, p.d_qk, p.d_v, p.n_seqs, p.S_loc,
-                         p.q_offset, p.key_lo, p.Kn, p.scale);
+                         p.rm, p.key_lo, p.Kn, p.scale);
     }
     if (mla_status s = check_launch("plain backward dK/dV"); s != MLA_OK) return s;
   }

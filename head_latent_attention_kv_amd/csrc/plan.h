@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "mla_laga.h"
 
 namespace mla {
@@ -21,6 +22,7 @@ constexpr int kKeyTile = 256;  // key tile of the backward's key-outer kernels; 
 struct Plan {
   int n_h, d_c, d_rope, d_nope, d_v, d_qk, n_seqs;
   int64_t S, S_loc, q_offset;
+  RowMap rm;      // local row -> global position (the non-empty position blocks)
   bool bf16;
   bool fast;      // forward runs the MFMA path
   bool fast_bwd;  // backward runs the MFMA path

@@ -20,7 +20,11 @@
  * Row i sits at global position p = q_offset + i and sees keys j with
  * seg_lo(p) <= j <= p: seg_lo(p) = 0 for one causal sequence, else the start
  * of the packed sample holding p (block-diagonal causal mask of fixed-token
- * packing, Libra review page, "Axiom ledger"). q's rope part and k_rope come
+ * packing, Libra review page, "Axiom ledger"). A shard may instead hold
+ * several position blocks (zigzag or striped sharding, which evens out
+ * causal work across ranks; Libra review page, Related Work beside
+ * Fig. 15): its rows are then the blocks laid end to end and p is read off
+ * that concatenation (mla_laga_desc.q_ranges). q's rope part and k_rope come
  * already rotated. The backward computes the gradients of sum(out * dout).
  *
  * Conventions for every entry point
@@ -66,6 +70,9 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 /* Force the plain fp32 path even where the fast path applies. */
 #define MLA_FLAG_GENERIC 1
 
+/* Most position blocks one shard may hold (mla_laga_desc.n_ranges). */
+#define MLA_MAX_RANGES 16
+
 typedef struct {
   int32_t n_h;      /* heads                                                  */
   int32_t d_c;      /* latent width                                           */
@@ -79,6 +86,17 @@ typedef struct {
   int32_t in_dtype; /* mla_dtype of the inputs                                */
   int32_t flags;    /* MLA_FLAG_* bits                                        */
   float softmax_scale; /* <= 0: 1/sqrt(d_nope + d_rope)                       */
+  /* Position blocks of the local rows. n_ranges = 0: one block, rows at
+   * q_offset .. q_offset + S_loc - 1. 1 <= n_ranges <= MLA_MAX_RANGES:
+   * q_ranges (host memory, read during the call only) holds n_ranges
+   * (start, length) int64 pairs; rows are the blocks in that order, so row
+   * i of block b (rows counted from the blocks before it) sits at
+   * start_b + i. Blocks must be ascending and disjoint (start_b >= start_{b-1}
+   * + length_{b-1}), lie in [0, S), and their lengths (0 allowed) must sum
+   * to S_loc; q_offset must then be 0. A zigzag rank r of R holds blocks r
+   * and 2R-1-r of S/(2R) positions each.                                     */
+  int32_t n_ranges;
+  const int64_t* q_ranges;
 } mla_laga_desc;
 
 /*

@@ -70,6 +70,83 @@ def test_counts_edge_cases(S, S_loc, q_off, cu):
         assert (lo, hi) == oracle.key_range(S_loc, q_off, cu_a)
 
 
+def with_ranges(d, ranges):
+    """Point the descriptor at (start, length) blocks; returns the array that
+    must stay alive while it is used."""
+    arr = np.ascontiguousarray(np.asarray(ranges, np.int64).reshape(-1, 2))
+    d.n_ranges = len(arr)
+    d.q_ranges = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    d.S_loc = int(arr[:, 1].sum())
+    d.q_offset = 0
+    return arr
+
+
+RANGE_COUNT_CASES = [
+    (16384, workloads.zigzag_blocks(16384, 0, 8), None),
+    (16384, workloads.zigzag_blocks(16384, 7, 8), None),
+    (600, [(5, 120), (300, 200)], [0, 1, 1, 130, 131, 400, 600]),
+    (700, [(10, 150), (470, 200)], [0, 200, 450, 700]),    # a sample nobody sees
+    (50, [(0, 0), (3, 1), (4, 0), (49, 1)], None),          # empty and one-row blocks
+]
+
+
+@pytest.mark.parametrize("S,ranges,cu", RANGE_COUNT_CASES)
+def test_counts_with_ranges_match_oracle(S, ranges, cu):
+    cfg = workloads.config("tiny_f32").with_(S=S)
+    d, _ = desc_for(cfg)
+    keep = with_ranges(d, ranges)
+    cu_a = None if cu is None else np.array(cu, np.int32)
+    d.n_seqs = 0 if cu is None else len(cu) - 1
+    pairs, lo, hi = hla.mla_laga_count(d, cu_a)
+    S_loc = int(keep[:, 1].sum())
+    rl = [tuple(r) for r in keep.tolist()]
+    assert pairs == oracle.visible_pairs(S_loc, 0, cu_a, rl)
+    assert (lo, hi) == oracle.key_range(S_loc, 0, cu_a, rl)
+
+
+def test_zigzag_ranks_balance_pairs():
+    per_rank = []
+    for r in range(8):
+        d, _ = desc_for(workloads.config("tiny_f32").with_(S=16384))
+        keep = with_ranges(d, workloads.zigzag_blocks(16384, r, 8))
+        per_rank.append(hla.mla_laga_count(d, None)[0])
+    assert len(set(per_rank)) == 1
+    d, _ = desc_for(workloads.config("h128_s16k_shard"))
+    contiguous_last = hla.mla_laga_count(d, None)[0]
+    assert contiguous_last > 1.8 * per_rank[0]
+
+
+def test_invalid_ranges_rejected_on_host():
+    E = hla.MLA_ERR_INVALID_ARG
+    cfg = workloads.config("tiny_f32").with_(S=100)
+    cases = [
+        [(50, 10), (20, 10)],          # descending
+        [(10, 20), (25, 10)],          # overlapping
+        [(-1, 5)],                     # before 0
+        [(95, 10)],                    # past S
+        [(10, -2), (20, 4)],           # negative length
+    ]
+    for ranges in cases:
+        d, _ = desc_for(cfg)
+        keep = with_ranges(d, ranges)
+        bad(E, hla.mla_laga_fwd_workspace_size, d, None)
+    d, _ = desc_for(cfg)
+    keep = with_ranges(d, [(0, 10), (40, 10)])
+    d.S_loc = 21                                            # rows do not add up
+    assert "S_loc" in bad(E, hla.mla_laga_count, d, None)
+    d.S_loc = 20
+    d.q_offset = 3                                          # q_offset with ranges
+    assert "q_offset" in bad(E, hla.mla_laga_count, d, None)
+    d.q_offset = 0
+    d.q_ranges = None                                       # NULL blocks
+    bad(E, hla.mla_laga_count, d, None)
+    d, _ = desc_for(cfg)
+    keep = with_ranges(d, [(2 * k, 1) for k in range(hla.MLA_MAX_RANGES + 1)])
+    bad(E, hla.mla_laga_count, d, None)
+    keep = with_ranges(d, [(2 * k, 1) for k in range(hla.MLA_MAX_RANGES)])
+    assert hla.mla_laga_count(d, None)[0] == sum(2 * k + 1 for k in range(hla.MLA_MAX_RANGES))
+
+
 def test_workspace_linear_in_rows_and_heads():
     # the rebuilt K/V dominate the workspace: affine in the key count and in n_h
     base = workloads.config("h128_s16k_shard")

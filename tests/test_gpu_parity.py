@@ -24,10 +24,17 @@ DSV3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
 GRADS = ("dq", "dc_kv", "dk_rope", "dW_UK", "dW_UV")
 
 
-def small(name, n_h, S, S_loc, q_offset, cu=None, backward=True, seed=3):
+def small(name, n_h, S, S_loc, q_offset, cu=None, backward=True, seed=3, q_ranges=None):
+    if q_ranges is not None:
+        S_loc, q_offset = sum(n for _, n in q_ranges), 0
     cfg = workloads.MLAConfig(name, n_h=n_h, S=S, S_loc=S_loc, q_offset=q_offset, dtype="bf16",
-                              backward=backward, seed=seed, **DSV3)
+                              backward=backward, seed=seed, q_ranges=q_ranges, **DSV3)
     return cfg, (None if cu is None else np.array(cu, np.int32))
+
+
+def positions(cfg):
+    """Oracle keyword arguments that place the rows (one block or several)."""
+    return dict(q_offset=cfg.q_offset, q_ranges=cfg.q_ranges)
 
 
 # With one visible key a row's softmax weight is exactly 1, so dS = P (dP - D)
@@ -43,6 +50,14 @@ SMALL = [
     small("one_token", 1, 1, 1, 0),
     small("last_row_only", 2, 257, 1, 256),
     small("varlen_len1_and_empty", 2, 520, 520, 0, cu=[0, 1, 1, 2, 258, 258, 259, 520]),
+    # several position blocks; tiles straddle block ends
+    small("blocks_ragged", 2, 1000, 0, 0, q_ranges=((37, 150), (400, 230), (900, 100))),
+    small("blocks_varlen", 2, 600, 0, 0, cu=[0, 1, 1, 130, 131, 400, 600],
+          q_ranges=((5, 120), (300, 200))),
+    # the middle sample lies between the blocks: its keys get zero gradients
+    small("blocks_unseen_sample", 2, 700, 0, 0, cu=[0, 200, 450, 700],
+          q_ranges=((10, 150), (470, 200))),
+    small("zigzag_r1_of_4", 2, 1024, 0, 0, q_ranges=workloads.zigzag_blocks(1024, 1, 4)),
 ]
 
 
@@ -51,7 +66,8 @@ def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None):
     if dout_override is not None:
         dev["dout"] = dout_override
     call = hla.MLACall(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
-                       q_offset=cfg.q_offset, cu_seqlens=cu, generic=generic, backward=backward)
+                       q_offset=cfg.q_offset, cu_seqlens=cu, generic=generic, backward=backward,
+                       q_ranges=cfg.q_ranges)
     out, lse = call.fwd(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
     res = {"out": out, "lse": lse, "fast": call.fast}
     if backward:
@@ -72,10 +88,10 @@ def test_small_fwd_bwd_elementwise(cfg, cu, generic):
     announce(f"small {cfg.name} generic={generic} n_h={cfg.n_h} S={cfg.S} S_loc={cfg.S_loc} q_off={cfg.q_offset}")
     x = workloads.make_inputs(cfg, with_dout=True)
     g = run(cfg, x, cu, generic=generic, backward=True)
-    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu)
+    ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, **positions(cfg))
     check("out", g["out"], ro)
     check("lse", g["lse"], rl)
-    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, **positions(cfg))
     for name, ref in zip(GRADS, rg):
         if name in VANISHING.get(cfg.name, ()):
             assert np.abs(ref).max() < 1e-12
@@ -119,7 +135,7 @@ def test_h128_s16k_shard_forward_sampled_heads(heads):
     check("lse", g["lse"][:, heads], rl)
 
 
-@pytest.mark.parametrize("name", ["h128_s8k_bwd", "h128_varlen64k"])
+@pytest.mark.parametrize("name", ["h128_s8k_bwd", "h128_varlen64k", "h128_s16k_zigzag_r0"])
 def test_full_size_backward_sampled_heads(name):
     cfg = workloads.config(name)
     cu = cfg.cu_seqlens()
@@ -130,24 +146,25 @@ def test_full_size_backward_sampled_heads(name):
     dz[:, heads] = x["dout"][:, heads]
     x0 = dict(x, dout=dz, dout_bits=workloads.f32_to_bf16_bits(dz))
     g = run(cfg, x0, cu, backward=True)
-    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu, heads=heads)
+    ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, heads=heads, **positions(cfg))
     check("out", g["out"][:, heads], ro)
     check("lse", g["lse"][:, heads], rl)
-    rg = oracle.mla_backward(dz, *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu, heads=heads)
+    rg = oracle.mla_backward(dz, *oracle_args(x), cu_seqlens=cu, heads=heads, **positions(cfg))
     for nm, ref in zip(GRADS, rg):
         check(nm, g[nm], ref)
 
     announce(f"{name} fwd+bwd, full dout; dq and weight blocks of heads {heads}")
     g = run(cfg, x, cu, backward=True)
-    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, cu_seqlens=cu,
-                             heads=heads)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, heads=heads,
+                             **positions(cfg))
     check("dq", g["dq"][:, heads], rg[0][:, heads])
     cols_k = np.concatenate([np.arange(h * 128, (h + 1) * 128) for h in heads])
     check("dW_UK", g["dW_UK"][:, cols_k], rg[3][:, cols_k])
     check("dW_UV", g["dW_UV"][:, cols_k], rg[4][:, cols_k])
 
 
-@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER + ["h128_s16k_zigzag_r0",
+                                                           "h128_s16k_zigzag_r7"])
 def test_mask_probe_exact_counts(name):
     """q = 0: every visible score is exactly 0, so exp(lse) counts the visible
     keys of each row; it must equal the oracle's integer count exactly."""
@@ -158,10 +175,10 @@ def test_mask_probe_exact_counts(name):
     dev = to_device(x, cfg)
     q0 = torch.zeros_like(dev["q"])
     call = hla.MLACall(q0, dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
-                       q_offset=cfg.q_offset, cu_seqlens=cu)
+                       q_offset=cfg.q_offset, cu_seqlens=cu, q_ranges=cfg.q_ranges)
     _, lse = call.fwd(q0, dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
     counts = np.rint(np.exp(lse.double().cpu().numpy())).astype(np.int64)
-    lo, hi = oracle.visible_range(cfg.S_loc, cfg.q_offset, cu)
+    lo, hi = oracle.visible_range(cfg.S_loc, cfg.q_offset, cu, cfg.q_ranges)
     expect = (hi - lo + 1)[:, None]
     bad = np.argwhere(counts != expect)
     assert bad.size == 0, f"{len(bad)} rows with wrong visible-key count, first {bad[:3]}"
@@ -184,6 +201,40 @@ def test_shard_concatenation_identity(generic):
         outs.append(g["out"]); lses.append(g["lse"])
     o, l = np.concatenate(outs), np.concatenate(lses)
     assert np.array_equal(o, full["out"]) and np.array_equal(l, full["lse"])
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["default", "plain"])
+def test_zigzag_concatenation_identity(generic):
+    """Four zigzag ranks (blocks r and 7-r of eight) reproduce the single-rank
+    call row for row, bit for bit, and their latent and weight gradients sum
+    to the single-rank gradients (LAGA abstract: equivalence across
+    sequence-parallel degrees)."""
+    cfg = workloads.MLAConfig("zz", n_h=4, S=2048, S_loc=2048, q_offset=0, dtype="bf16",
+                              backward=True, **DSV3)
+    announce(f"zigzag identity generic={generic}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    full = run(cfg, x, generic=generic, backward=True)
+    out = np.full_like(full["out"], np.nan)
+    lse = np.full_like(full["lse"], np.nan)
+    dq = np.full_like(full["dq"], np.nan)
+    sums = {k: np.zeros_like(full[k], dtype=np.float64) for k in GRADS[1:]}
+    for r in range(4):
+        blocks = workloads.zigzag_blocks(2048, r, 4)
+        rows = np.concatenate([np.arange(a, a + n) for a, n in blocks])
+        c = cfg.with_(S_loc=len(rows), q_ranges=blocks)
+        xr = dict(x)
+        for k in ("q", "dout"):
+            xr[k] = x[k][rows]
+            xr[k + "_bits"] = x[k + "_bits"][rows]
+        g = run(c, xr, generic=generic, backward=True)
+        out[rows], lse[rows], dq[rows] = g["out"], g["lse"], g["dq"]
+        for k in sums:
+            sums[k] += g[k]
+    assert np.array_equal(out, full["out"]) and np.array_equal(lse, full["lse"])
+    check("dq", dq, full["dq"], max_abs=1e-5, mean_rel=1e-6)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x))
+    for k, ref in zip(GRADS[1:], rg[1:]):
+        check(k, sums[k], ref)
 
 
 def test_forward_backward_deterministic():

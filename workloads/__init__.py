@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -40,6 +40,7 @@ __all__ = [
     "lognormal_lengths",
     "cu_seqlens_from_lengths",
     "make_inputs",
+    "zigzag_blocks",
 ]
 
 
@@ -63,6 +64,9 @@ class MLAConfig:
     varlen_sigma: Optional[float] = None
     varlen_cap: Optional[int] = None
     seed: int = 0
+    # several position blocks instead of [q_offset, q_offset + S_loc): a
+    # tuple of (start, length); q_offset is then 0
+    q_ranges: Optional[Tuple[Tuple[int, int], ...]] = None
 
     @property
     def d_qk(self) -> int:
@@ -80,6 +84,16 @@ class MLAConfig:
 
 
 _DSV3 = dict(d_c=512, d_rope=64, d_nope=128, d_v=128)
+
+
+def zigzag_blocks(S: int, rank: int, world: int) -> Tuple[Tuple[int, int], ...]:
+    """Zigzag sequence-parallel shard: of 2*world equal position blocks, rank
+    r holds blocks r and 2*world-1-r, which evens out causal work (Libra
+    review page, Related Work beside Fig. 15: ring schemes arrange shards
+    against causal imbalance)."""
+    C = S // (2 * world)
+    return ((rank * C, C), ((2 * world - 1 - rank) * C, C))
+
 
 CONFIGS: Dict[str, MLAConfig] = {
     # tiny fp32 case, all queries local
@@ -100,6 +114,15 @@ CONFIGS: Dict[str, MLAConfig] = {
                                 varlen_median=2048, varlen_sigma=1.0,
                                 varlen_cap=32768, **_DSV3),
 }
+
+# further parity and measurement cases beyond the five configurations:
+# zigzag ranks of the 16384-long sequence over 8 ranks. Rank 0 holds blocks
+# 0 and 15 (it rebuilds K/V for every latent row); every rank sees the same
+# number of pairs.
+for _r in (0, 7):
+    CONFIGS[f"h128_s16k_zigzag_r{_r}"] = MLAConfig(
+        f"h128_s16k_zigzag_r{_r}", n_h=128, S=16384, S_loc=2048, q_offset=0, dtype="bf16",
+        backward=True, q_ranges=zigzag_blocks(16384, _r, 8), **_DSV3)
 
 # the five configurations, in the order they are listed with the method's targets
 CONFIG_ORDER: List[str] = ["tiny_f32", "h16_s4k", "h128_s16k_shard",
