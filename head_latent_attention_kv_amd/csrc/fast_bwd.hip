@@ -845,6 +845,9 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           half8 fa[QPF + 1];
           #pragma unroll
           for (int i = 0; i < QPF; ++i) fa[i] = frag(i);
+          // raised priority over the S / dP chain: the SIMD's other wave
+          // fills its gaps with its own VALU work
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int k = 0; k < 20; ++k) {
             if (k + QPF < 20) fa[(k + QPF) % (QPF + 1)] = frag(k + QPF);
@@ -853,6 +856,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         half8 dsf[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -204,6 +204,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
         half8 fa[FPF + 1];
 #pragma unroll
         for (int i = 0; i < FPF; ++i) fa[i] = *reinterpret_cast<const half8*>(skm + 32 * i);
+        // the score products run at raised wave priority, so that the SIMD's
+        // other wave fills the gaps of this dependent chain with its softmax
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 12; ++kk) {
           if (kk + FPF < 12) fa[(kk + FPF) % (FPF + 1)] = *reinterpret_cast<const half8*>(skm + 32 * (kk + FPF));
@@ -211,6 +214,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
           for (int nt = 0; nt < NT; ++nt) s[nt] = mfma_f16(fa[kk % (FPF + 1)], qf[nt][kk], s[nt]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (need_mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
