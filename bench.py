@@ -3,6 +3,7 @@ one query shard (synthetic seeded inputs, resident in HBM before timing).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --sp-sweep 8 [--steps K]   (per-rank times of an 8-way split)
+    python bench.py --decode decode_h128_b64_l8k   (absorbed decode over the latent cache)
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: visible
 (query, key) pairs times 2*n_h*(d_qk+d_v) forward and 2*n_h*(3*d_qk+2*d_v)
@@ -223,6 +224,66 @@ def sp_sweep(base_name, world, steps, warmup):
     print(json.dumps(out), flush=True)
 
 
+def decode_bench(name, steps, warmup):
+    """Time the decode path (absorbed form over the latent cache) on a decode
+    batch; prints its own JSON line. Algorithmic work per cached row and
+    head: 2 (576 + 512) FLOP for the scores and the latent-weighted sum; the
+    dominant kernel streams each cached row (1152 bytes in bf16) once."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_kv_amd as hla
+    import workloads
+
+    cfg = workloads.config(name)
+    cu = cfg.cu_seqlens()
+    x = workloads.make_inputs(cfg, with_dout=False)
+    a = [torch.from_numpy(x[k + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+         for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    call = hla.MLADecodeCall(*a, cu)
+    out, lse = call(*a)
+    for _ in range(warmup):
+        call(*a, out=out, lse=lse)
+    torch.cuda.synchronize()
+    hla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call(*a, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = {}
+    for kname in hla.timing_names():
+        tot, n = hla.timing_read(kname)
+        kern[kname] = {"ms_per_launch": round(tot / max(n, 1), 4),
+                       "launches_per_step": n / steps}
+    hla.timing_enable(False)
+    keys = int(cu[-1])
+    n_h, B = cfg.n_h, cfg.S_loc
+    f_attn = 2 * n_h * (576 + 512) * keys
+    f_proj = 2 * B * n_h * 128 * 512 * 2
+    cache_bytes = keys * 1152
+    t_attn = kern.get("decode_attn", {}).get("ms_per_launch")
+    roofline = None
+    if t_attn:
+        gbs = cache_bytes / (t_attn / 1e3) / 1e9
+        roofline = {"kernel": "decode_attn", "bound": "hbm", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": None, "ms_per_launch": t_attn,
+                    "tflops": round(f_attn / (t_attn / 1e3) / 1e12, 2),
+                    "mfma_tflops_executed": round(f_attn * (2 * 576 + 512) / (576 + 512)
+                                                  / (t_attn / 1e3) / 1e12, 2)}
+    res = {"metric": "MLA absorbed decode step (latent cache), TFLOP/s",
+           "value": round((f_attn + f_proj) / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name, "n_h": n_h, "batch": B, "cached_rows": keys,
+                      "longest": int(max(cfg.seq_lens)), "flop": f_attn + f_proj,
+                      "cache_bytes": cache_bytes},
+           "cache_gbs": round(cache_bytes / (ms / 1e3) / 1e9, 1),
+           "roofline": roofline, "kernels": kern}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +297,9 @@ def main():
                          "(the scale reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two --counter-step counter csv files")
+    ap.add_argument("--decode", metavar="NAME",
+                    help="time the absorbed decode path on a decode batch "
+                         "(decode_h128_b64_l8k, decode_h128_b32_mixed); prints its own JSON line")
     ap.add_argument("--sp-sweep", type=int, metavar="WORLD",
                     help="time each rank of a WORLD-way contiguous and zigzag split of the "
                          "workload's sequence, one after another (prints its own JSON line)")
@@ -249,6 +313,9 @@ def main():
               "(the latent all-gather is not part of it); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.decode:
+        decode_bench(args.decode, args.steps, args.warmup)
+        return
     if args.sp_sweep:
         sp_sweep(args.workload, args.sp_sweep, args.steps, args.warmup)
         return

@@ -20,7 +20,8 @@ __all__ = [
     "MLAError", "MLADesc", "load_library", "library_path", "mla_laga_fwd", "mla_laga_bwd",
     "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
     "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC",
-    "MLA_MAX_RANGES",
+    "MLA_MAX_RANGES", "MLADecodeDesc", "MLADecodeCall", "mla_laga_decode",
+    "mla_laga_decode_workspace_size",
 ]
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
@@ -53,11 +54,20 @@ class MLADesc(ctypes.Structure):
     ]
 
 
+class MLADecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_h", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+        ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("S", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _DESCP = ctypes.POINTER(MLADesc)
+_DDESCP = ctypes.POINTER(MLADecodeDesc)
 
 EXPORTED = {
     "mla_laga_fwd_workspace_size": (ctypes.c_int, [_DESCP, _I32P, ctypes.POINTER(ctypes.c_size_t)]),
@@ -67,6 +77,9 @@ EXPORTED = {
     "mla_laga_bwd": (ctypes.c_int, [_DESCP, _P, _P, _P, _P, _P, _P, _I32P, _P, _P, _P,
                                     _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_laga_count": (ctypes.c_int, [_DESCP, _I32P, _I64P, _I64P, _I64P]),
+    "mla_laga_decode_workspace_size": (ctypes.c_int, [_DDESCP, _I32P, ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_laga_decode": (ctypes.c_int, [_DDESCP, _P, _P, _P, _P, _P, _I32P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
     "mla_laga_uses_fast_path": (ctypes.c_int, [_DESCP]),
     "mla_laga_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "mla_laga_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), _I64P]),
@@ -302,3 +315,65 @@ def mla_laga_bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, q_offset: int = 0,
     _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))] +
                   _input_specs(d, q, c_kv, k_rope, W_UK, W_UV)[:1])
     return call.bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse)
+
+
+# ------------------------------------------------------------------ decode
+def make_decode_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor,
+                     W_UV: torch.Tensor, cu_seqlens,
+                     softmax_scale: Optional[float] = None) -> Tuple[MLADecodeDesc, np.ndarray]:
+    batch, n_h, d_qk = q.shape
+    S, d_c = c_kv.shape
+    d_rope = k_rope.shape[1]
+    cu = _host_cu(cu_seqlens)
+    d = MLADecodeDesc()
+    d.n_h, d.d_c, d.d_rope = n_h, d_c, d_rope
+    d.d_nope, d.d_v = d_qk - d_rope, W_UV.shape[1] // n_h
+    d.batch, d.S = batch, S
+    d.in_dtype = _in_dtype(q)
+    d.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    return d, cu
+
+
+def mla_laga_decode_workspace_size(desc: MLADecodeDesc, cu: np.ndarray) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mla_laga_decode_workspace_size(ctypes.byref(desc), _cu_ptr(cu),
+                                                          ctypes.byref(n)))
+    return n.value
+
+
+class MLADecodeCall:
+    """One decode batch's shapes, prepared once: one query per sequence over
+    the latent cache (c_kv, k_rope) packed by cu_seqlens."""
+
+    def __init__(self, q, c_kv, k_rope, W_UK, W_UV, cu_seqlens,
+                 softmax_scale: Optional[float] = None):
+        self.desc, self.cu = make_decode_desc(q, c_kv, k_rope, W_UV, cu_seqlens, softmax_scale)
+        d = self.desc
+        _check_inputs(d, [("q", q, (d.batch, d.n_h, d.d_nope + d.d_rope)),
+                          ("c_kv", c_kv, (d.S, d.d_c)), ("k_rope", k_rope, (d.S, d.d_rope)),
+                          ("W_UK", W_UK, (d.d_c, d.n_h * d.d_nope)),
+                          ("W_UV", W_UV, (d.d_c, d.n_h * d.d_v))])
+        self.device = q.device
+        self.cu_dev = torch.from_numpy(self.cu).to(self.device)
+        self.ws = _workspace(mla_laga_decode_workspace_size(d, self.cu), self.device)
+
+    def __call__(self, q, c_kv, k_rope, W_UK, W_UV, out=None, lse=None):
+        d = self.desc
+        if out is None:
+            out = torch.empty((d.batch, d.n_h, d.d_v), dtype=torch.float32, device=self.device)
+        if lse is None:
+            lse = torch.empty((d.batch, d.n_h), dtype=torch.float32, device=self.device)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(load_library().mla_laga_decode(
+            ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK), _ptr(W_UV),
+            _cu_ptr(self.cu), _ptr(self.cu_dev), _ptr(out), _ptr(lse), _ptr(self.ws),
+            self.ws.numel(), ctypes.c_void_p(stream)))
+        return out, lse
+
+
+def mla_laga_decode(q, c_kv, k_rope, W_UK, W_UV, cu_seqlens,
+                    softmax_scale: Optional[float] = None):
+    """out [batch,n_h,d_v] fp32 and lse [batch,n_h] fp32: one query per
+    sequence (at its last cached position) over the latent cache."""
+    return MLADecodeCall(q, c_kv, k_rope, W_UK, W_UV, cu_seqlens, softmax_scale)(
+        q, c_kv, k_rope, W_UK, W_UV)

@@ -48,6 +48,10 @@ COMMON = [
 # then copies each score tile back to VGPRs, so ask for the VGPR form there.
 DEVICE_FLAGS = {
     "fast_bwd.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+    # decode attention: the score tile and the output accumulators both in
+    # VGPRs; the AGPR form put the score chain in AGPRs next to the
+    # accumulators and spilled to scratch
+    "decode.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -245,6 +245,47 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
 
 static bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
 
+// Validate a decode call and choose its split: chunks of keys sized so that
+// the attention launch has about two workgroups per compute unit.
+static mla_status make_decode_plan(const mla_laga_decode_desc* d, const int32_t* cu, DecodePlan* p) {
+  if (!d) return fail(MLA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->n_h < 1 || d->d_c < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 0)
+    return fail(MLA_ERR_INVALID_ARG, "dims must be positive");
+  if (d->S < 1 || d->S > INT32_MAX) return fail(MLA_ERR_INVALID_ARG, "S must be in [1, 2^31)");
+  if (d->in_dtype != MLA_F32 && d->in_dtype != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "in_dtype must be MLA_F32 or MLA_BF16");
+  if (!cu) return fail(MLA_ERR_INVALID_ARG, "decode needs cu_seqlens_host");
+  if (cu[0] != 0 || cu[d->batch] != d->S)
+    return fail(MLA_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at S (got %d .. %d)", cu[0],
+                cu[d->batch]);
+  int64_t longest = 0;
+  for (int b = 0; b < d->batch; ++b) {
+    if (cu[b + 1] <= cu[b])
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d has no cached row (cu_seqlens must increase)", b);
+    longest = std::max<int64_t>(longest, cu[b + 1] - cu[b]);
+  }
+  if (d->in_dtype != MLA_BF16 || d->d_c != 512 || d->d_rope != 64 || d->d_nope != 128 ||
+      d->d_v != 128 || d->n_h % 32 != 0)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "decode takes bf16 with d_c=512, d_rope=64, d_nope=d_v=128 and n_h a multiple of 32");
+  DecodePlan& P = *p;
+  P.n_h = d->n_h;
+  P.batch = d->batch;
+  P.S = d->S;
+  P.total_keys = d->S;
+  P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(d->d_nope + d->d_rope));
+  if (!(P.scale < INFINITY)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const int64_t groups = (d->n_h + 127) / 128;
+  const int64_t target = 512;   // workgroups of the attention launch
+  int64_t chunk = (P.total_keys * groups + target - 1) / target;
+  chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);
+  chunk = std::min<int64_t>(chunk, (longest + 31) / 32 * 32);
+  P.chunk = static_cast<int>(chunk);
+  P.nch = static_cast<int>((longest + chunk - 1) / chunk);
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -356,6 +397,38 @@ mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void*
                     dW_UK, dW_UV, ws, st);
   return generic_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
                      dW_UK, dW_UV, ws, st);
+}
+
+mla_status mla_laga_decode_workspace_size(const mla_laga_decode_desc* desc, const int32_t* cu_host,
+                                           size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  DecodePlan p;
+  if (mla_status s = make_decode_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  *bytes = static_cast<size_t>(decode_layout(p).total);
+  return MLA_OK;
+}
+
+mla_status mla_laga_decode(const mla_laga_decode_desc* desc, const void* q, const void* c_kv,
+                           const void* k_rope, const void* W_UK, const void* W_UV,
+                           const int32_t* cu_host, const int32_t* cu_dev, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan p;
+  if (mla_status s = make_decode_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  const void* ptrs[] = {q, c_kv, k_rope, W_UK, W_UV, out, lse};
+  const char* names[] = {"q", "c_kv", "k_rope", "W_UK", "W_UV", "out", "lse"};
+  for (int k = 0; k < 7; ++k) {
+    if (!ptrs[k]) return fail(MLA_ERR_INVALID_ARG, "%s is NULL", names[k]);
+    if (misaligned(ptrs[k])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[k]);
+  }
+  if (!cu_dev) return fail(MLA_ERR_INVALID_ARG, "decode needs cu_seqlens_dev");
+  const int64_t need = decode_layout(p).total;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    return fail(MLA_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (static_cast<int64_t>(workspace_bytes) < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %lld", workspace_bytes,
+                (long long)need);
+  return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse,
+                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 const char* mla_laga_status_string(mla_status s) {

@@ -1,0 +1,425 @@
+// Decode in the absorbed form over the latent cache (inference only).
+//
+// The LAGA abstract describes the absorbed MLA form as the one allowed only in
+// inference decode: W_UK is folded into the query and attention runs over the
+// compressed latent itself, so no per-head K/V is ever built. One query per
+// sequence attends to all of that sequence's cached latent rows:
+//   q_lat[b,h,:] = W_UK_h q_nope[b,h,:]                (512)
+//   s_j          = scale * (q_lat . c_kv[j] + q_rope . k_rope[j])
+//   o_lat[b,h,:] = sum_j softmax(s)_j c_kv[j]          (512)
+//   out[b,h,:]   = W_UV_h^T o_lat[b,h,:]               (128)
+// which equals the explicit form for a query at the sequence's last position.
+//
+// Kernels (gfx950, fp16/bf16 MFMA with fp32 accumulation):
+//   1. head_gemm_kernel: per-head q_lat (bf16 in, fp16 out);
+//   2. decode_attn_kernel: split-KV attention. A workgroup owns one sequence,
+//      one chunk of its keys, up to 128 heads (4 waves x 32) and one half
+//      (256) of the 512 output dims. Keys and values are the same 576-wide
+//      latent rows: each 32-key block is loaded to registers, converted
+//      bf16 -> fp16 and written to one swizzled LDS tile that serves both
+//      S^T = K Q^T (row-wise fragments) and O^T += V^T P^T (transposed
+//      reads). The latent part of q_lat stays in registers, its rope part in
+//      LDS. The two halves of a
+//      chunk recompute S (a third more products than one workgroup holding
+//      all 512 dims, whose 256 accumulator registers per wave do not fit
+//      next to q_lat) and run back to back on one XCD, so the second reads
+//      the cache block from L2; the next block's loads are in flight while
+//      the current block is used;
+//   3. decode_combine_kernel: merges the chunks (max, rescaled sums), writes
+//      o_lat in fp16 and lse;
+//   4. head_gemm_kernel: per-head out = o_lat W_UV_h (fp16 in, fp32 out).
+#include <math.h>
+
+#include "fast.h"
+#include "fast_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int DC = 512;            // latent width
+constexpr int DR = 64;             // rope width
+constexpr int DL = DC + DR;        // key width in the latent space (576)
+constexpr int DB = 32;             // keys per block
+// LDS row pitch: 72 data slots of 16 bytes + 4 pad slots. 1216 = 448 + 3*256,
+// so rows fall on the banks exactly as the 448-byte swizzled rows do: both
+// row-wise and transposed 16-bit reads are conflict-free.
+constexpr int DROW = 1216;
+constexpr int DSTAGE = DB * DROW;
+constexpr int DWAVES = 4;
+constexpr int QR_ROW = DR * 2 + 16;               // q_rope LDS row pitch (odd slot count)
+constexpr int DPIECES = DB * (DL / 8);            // 16-byte pieces per block
+constexpr int DPT = DPIECES / (DWAVES * 64);      // per thread (9)
+static_assert(DPIECES % (DWAVES * 64) == 0, "pieces split evenly");
+constexpr float kTauD = 8.f;                      // lazy-rescale threshold, log2 units
+constexpr float kLn2D = 0.69314718055994530942f;
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// out[r][h][c] (at out + r*ldo + h*ho + c) = sum_k X[r][h][k] Y[c][h][k] for
+// r < R, c < C, with X[r][h][k] at X + r*ldx + h*hx + k and Y likewise.
+// One wave per 32 x 32 tile, operands straight from memory (the products
+// here are small next to the attention).
+template <typename TIn, typename TOut>
+__global__ void __launch_bounds__(64)
+head_gemm_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t hx, const TIn* __restrict__ Y,
+                 int64_t ldy, int64_t hy, TOut* __restrict__ out, int64_t ldo, int64_t ho, int R,
+                 int C, int K) {
+  typedef typename MfmaOp<TIn>::vec vec;
+  const int ct = blockIdx.x, rt = blockIdx.y, h = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+  const int r = 32 * rt + lr, c = 32 * ct + lr;
+  const TIn* xr = X + static_cast<int64_t>(r) * ldx + static_cast<int64_t>(h) * hx + 8 * lh;
+  const TIn* yr = Y + static_cast<int64_t>(c) * ldy + static_cast<int64_t>(h) * hy + 8 * lh;
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  vec zero;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zero[e] = static_cast<TIn>(0.f);
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const vec a = r < R ? *reinterpret_cast<const vec*>(xr + k0) : zero;
+    const vec b = c < C ? *reinterpret_cast<const vec*>(yr + k0) : zero;
+    acc = MfmaOp<TIn>::run(a, b, acc);
+  }
+  if (c >= C) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 32 * rt + d_row(e, lh);
+    if (row < R)
+      out[static_cast<int64_t>(row) * ldo + static_cast<int64_t>(h) * ho + c] = static_cast<TOut>(acc[e]);
+  }
+}
+
+// Split-KV attention of one chunk of one sequence's keys for up to 128 heads
+// and one half of the output dims. Partial results: opart[b][chunk][h][:] =
+// O / l (fp16; this workgroup's 256 dims) and ml[b][chunk][h] = (m, l) with
+// O = sum_j 2^(s_j scale log2e - m) c_kv[j] and l the same sum of weights;
+// chunks past the sequence's end write nothing. Work item w (of n_items =
+// nch * batch * head groups) runs as workgroups 16 (w / 8) + w % 8 (first
+// half) and that + 8 (second half): round-robin XCD assignment puts both on
+// one XCD, one after the other.
+__global__ void __launch_bounds__(DWAVES * 64)
+decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict__ q,
+                   const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_rope,
+                   const int32_t* __restrict__ cu, _Float16* __restrict__ opart,
+                   float2* __restrict__ ml, int n_h, int batch, int nch, int n_items, int chunk,
+                   float scale_log2) {
+  // two K/V stages, then q_rope of the workgroup's heads (144-byte rows)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * DSTAGE + 128 * QR_ROW];
+  const int bid = blockIdx.x;
+  const int item = ((bid >> 4) << 3) | (bid & 7), dh = (bid >> 3) & 1;
+  if (item >= n_items) return;                // whole workgroup
+  const int ch = item % nch, b = (item / nch) % batch, hg = item / (nch * batch);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lr = lane & 31, lh = lane >> 5;
+  const int s0 = cu[b], len = cu[b + 1] - s0;
+  const int k0 = ch * chunk;                 // chunk's first key, within the sequence
+  if (k0 >= len) return;                     // whole workgroup: nothing to do
+  const int k1 = min(len, k0 + chunk);
+  const int nblk = (k1 - k0 + DB - 1) / DB;
+  const int hw = hg * 128 + 32 * w;          // the wave's first head
+  const bool live = hw < n_h;                // n_h is a multiple of 32
+  const int h = hw + lr;                     // this lane's head
+
+  // staging: piece e = tid + 256 j of a block is 16 bytes of key e / 72,
+  // slot e % 72 (slots 0..63: c_kv, 64..71: k_rope); it lands in LDS slot
+  // xs_slot(key, slot) of the key's row. A block moves in three parts of
+  // three pieces per thread, spread over the products of the block before.
+  constexpr int PPART = DPT / 3;
+  static_assert(DPT % 3 == 0, "three staging parts");
+  auto load_part = [&](int blk, int part, u32x4 (&r)[PPART]) {
+    const int kb = k0 + blk * DB;            // block's first key (sequence-relative)
+    const int64_t row0 = static_cast<int64_t>(s0) + kb;
+    const uint16_t* cb = c_kv + row0 * DC;
+    const uint16_t* rb = k_rope + row0 * DR;
+#pragma unroll
+    for (int j = 0; j < PPART; ++j) {
+      const int e = tid + DWAVES * 64 * (PPART * part + j);
+      const int key = e / (DL / 8), sl = e % (DL / 8);
+      if (kb + key < k1) {
+        const uint16_t* src = sl < DC / 8 ? cb + key * DC + 8 * sl : rb + key * DR + 8 * (sl - DC / 8);
+        r[j] = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        r[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_part = [&](int st, int part, const u32x4 (&r)[PPART]) {
+    char* dst = smem + st * DSTAGE;
+#pragma unroll
+    for (int j = 0; j < PPART; ++j) {
+      const int e = tid + DWAVES * 64 * (PPART * part + j);
+      const int key = e / (DL / 8), sl = e % (DL / 8);
+      *reinterpret_cast<half8*>(dst + key * DROW + xs_slot(key, sl) * 16) = bf16x8_to_half8(r[j]);
+    }
+  };
+
+  // Q^T fragments (B operand of S^T = K Q^T): lane = head, k-slots = dims.
+  // The 512 latent dims stay in registers; the 64 rope dims are read from
+  // LDS (registers are the limit here).
+  half8 qf[DC / 16];
+  {
+    const _Float16* ql = qlat + (static_cast<int64_t>(b) * n_h + h) * DC + 8 * lh;
+#pragma unroll
+    for (int kk = 0; kk < DC / 16; ++kk) {
+      if (live) {
+        qf[kk] = *reinterpret_cast<const half8*>(ql + 16 * kk);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<_Float16>(0.f);
+      }
+    }
+    // q_rope of this lane's head: dims 8 lh + 16 j .. (j = 0..3)
+    const uint16_t* qr = q + (static_cast<int64_t>(b) * n_h + h) * 192 + 128 + 8 * lh;
+    char* qrow = smem + 2 * DSTAGE + (32 * w + lr) * QR_ROW + 16 * lh;
+#pragma unroll
+    for (int j = 0; j < DR / 16; ++j) {
+      half8 v;
+      if (live) {
+        v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(qr + 16 * j));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(0.f);
+      }
+      *reinterpret_cast<half8*>(qrow + 32 * j) = v;
+    }
+  }
+  const char* qrope = smem + 2 * DSTAGE + (32 * w + lr) * QR_ROW + 16 * lh;
+
+  // O^T accumulators: 32 heads x 256 dims (dh * 256 ..) per wave
+  constexpr int NDT = DC / 2 / 32;
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const half2v ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  const int k_r0 = xs_row_base<DROW>(swap23(lr), lh, 0);   // K rows swap23(lr)
+  const int k_r1 = xs_row_base<DROW>(swap23(lr), lh, 1);
+  const int v_t0 = xs_tr_base<DROW>(lane, 0);              // V^T transposed reads
+  const int v_t1 = xs_tr_base<DROW>(lane, 1);
+
+  u32x4 stg[PPART];
+#pragma unroll
+  for (int part = 0; part < 3; ++part) {
+    load_part(0, part, stg);
+    store_part(0, part, stg);
+  }
+  __syncthreads();   // first block and q_rope in LDS
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int st = bi & 1;
+    const bool more = bi + 1 < nblk;
+    if (more) load_part(bi + 1, 0, stg);   // in flight during the score products
+    const char* base = smem + st * DSTAGE;
+    f32x16 s;
+    if (live) {
+      // S^T rows: keys swap23(lr) of the block
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      constexpr int PF = 3;
+      auto frag = [&](int kk) {
+        return *reinterpret_cast<const half8*>(base + ((kk & 1) ? k_r1 : k_r0) + 64 * (kk >> 1));
+      };
+      half8 fa[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) fa[i] = frag(i);
+#pragma unroll
+      for (int kk = 0; kk < DL / 16; ++kk) {
+        if (kk + PF < DL / 16) fa[(kk + PF) % (PF + 1)] = frag(kk + PF);
+        const half8 qb = kk < DC / 16 ? qf[kk] : *reinterpret_cast<const half8*>(qrope + 32 * (kk - DC / 16));
+        s = mfma_f16(fa[kk % (PF + 1)], qb, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (more) {
+      store_part(st ^ 1, 0, stg);
+      load_part(bi + 1, 1, stg);
+    }
+    half8 pb[2];
+    if (live) {
+      const int kb = k0 + bi * DB;
+      if (kb + DB > k1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb + swap23(d_row(r, lh)) >= k1) s[r] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = wave_max_pair(mx) * scale_log2;
+      const bool grow = mx > m + kTauD;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      }
+      float sum = l;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        half2v pr;
+        pr[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m)));
+        pr[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], scale_log2, -m)));
+        pb[r >> 3][r & 7] = pr[0];
+        pb[r >> 3][(r & 7) + 1] = pr[1];
+        sum = __builtin_amdgcn_fdot2(pr, ones, sum, false);
+      }
+      l = sum;
+    }
+    if (more) {
+      store_part(st ^ 1, 1, stg);
+      load_part(bi + 1, 2, stg);
+    }
+    if (live) {
+      // O^T (dims x heads) += V^T (dims x keys) P^T (keys x heads)
+      // V^T fragments run PF products ahead (16 products: dim tile k % 8 of
+      // this half, keys 16 (k / 8) ..)
+      constexpr int PF = 3, NPV = 2 * NDT;
+      auto vfrag = [&](int k) {
+        const int off = 16 * (k / NDT) * DROW + 64 * (NDT * dh + k % NDT);
+        return frag_tr2(base + v_t0 + off, base + v_t1 + off);
+      };
+      half8 fv[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) fv[i] = vfrag(i);
+#pragma unroll
+      for (int k = 0; k < NPV; ++k) {
+        if (k + PF < NPV) fv[(k + PF) % (PF + 1)] = vfrag(k + PF);
+        const int dt = k % NDT;
+        o[dt] = mfma_f16(fv[k % (PF + 1)], pb[k / NDT], o[dt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (more) store_part(st ^ 1, 2, stg);
+    __syncthreads();
+  }
+
+  if (!live) return;
+  const float lt = l + __shfl_xor(l, 32, 64);
+  const float inv = 1.f / lt;
+  const int64_t slot = (static_cast<int64_t>(b) * nch + ch) * n_h + h;
+  _Float16* dst = opart + slot * DC + (DC / 2) * dh;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      half4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(o[dt][4 * g + e] * inv);
+      *reinterpret_cast<half4*>(dst + 32 * dt + 8 * g + 4 * lh) = v;
+    }
+  if (lh == 0 && dh == 0) ml[slot] = make_float2(m, lt);   // both halves hold the same
+}
+
+// o_lat[b][h][:] = sum_c w_c opart[b][c][h][:] / sum_c w_c with w_c =
+// l_c 2^(m_c - max m); lse[b][h] = ln(sum_c l_c 2^(m_c)) (natural log).
+// One workgroup of 128 threads per (head, sequence), four dims per thread.
+__global__ void __launch_bounds__(128)
+decode_combine_kernel(const _Float16* __restrict__ opart, const float2* __restrict__ ml,
+                      const int32_t* __restrict__ cu, _Float16* __restrict__ olat,
+                      float* __restrict__ lse, int n_h, int nch, int chunk) {
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int len = cu[b + 1] - cu[b];
+  const int nc = (len + chunk - 1) / chunk;
+  const int64_t base = static_cast<int64_t>(b) * nch * n_h + h;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[base + static_cast<int64_t>(c) * n_h].x);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, L = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const int64_t sl = base + static_cast<int64_t>(c) * n_h;
+    const float2 v = ml[sl];
+    const float wgt = v.y * __builtin_amdgcn_exp2f(v.x - M);
+    L += wgt;
+    const half4 x = *reinterpret_cast<const half4*>(opart + sl * DC + 4 * t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += wgt * static_cast<float>(x[e]);
+  }
+  const float inv = 1.f / L;
+  half4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<_Float16>(acc[e] * inv);
+  *reinterpret_cast<half4*>(olat + (static_cast<int64_t>(b) * n_h + h) * DC + 4 * t) = r;
+  if (t == 0) lse[static_cast<int64_t>(b) * n_h + h] = (M + __log2f(L)) * kLn2D;
+}
+
+}  // namespace
+
+DecodeLayout decode_layout(const DecodePlan& p) {
+  DecodeLayout L{};
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += align_up(bytes, kAlign);
+    return o;
+  };
+  const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
+  L.WTv = take(nk * DC * 2);
+  L.qlat = take(static_cast<int64_t>(p.batch) * p.n_h * DC * 2);
+  L.olat = take(static_cast<int64_t>(p.batch) * p.n_h * DC * 2);
+  L.opart = take(static_cast<int64_t>(p.batch) * p.nch * p.n_h * DC * 2);
+  L.ml = take(static_cast<int64_t>(p.batch) * p.nch * p.n_h * 8);
+  L.total = off;
+  return L;
+}
+
+mla_status fast_decode(const DecodePlan& p, const void* q, const void* c_kv, const void* k_rope,
+                       const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
+                       float* lse, char* ws, hipStream_t st) {
+  const DecodeLayout L = decode_layout(p);
+  _Float16* WTv = reinterpret_cast<_Float16*>(ws + L.WTv);
+  _Float16* qlat = reinterpret_cast<_Float16*>(ws + L.qlat);
+  _Float16* olat = reinterpret_cast<_Float16*>(ws + L.olat);
+  _Float16* opart = reinterpret_cast<_Float16*>(ws + L.opart);
+  float2* ml = reinterpret_cast<float2*>(ws + L.ml);
+  const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
+  const int n_h = p.n_h, B = p.batch;
+  const unsigned rtiles = static_cast<unsigned>((B + 31) / 32);
+  mla_status s;
+  // W_UV^T in fp16: [h*128 + d][c]
+  if ((s = launch_transpose(static_cast<const uint16_t*>(W_UV), nk, 0, DC, DC, nk, WTv, DC, 0,
+                            Elem::F16, 1, st, "decode_prep_w")) != MLA_OK)
+    return s;
+  {
+    // q_lat[b][h][c] = sum_d q[b][h][d] W_UK[c][h*128 + d]
+    KernelTimer kt("decode_absorb", st);
+    hipLaunchKernelGGL((head_gemm_kernel<__bf16, _Float16>), dim3(DC / 32, rtiles, n_h), dim3(64),
+                       0, st, static_cast<const __bf16*>(q), static_cast<int64_t>(n_h) * 192,
+                       int64_t(192), static_cast<const __bf16*>(W_UK), nk, int64_t(128), qlat,
+                       static_cast<int64_t>(n_h) * DC, int64_t(DC), B, DC, 128);
+  }
+  if ((s = check_launch("decode absorb")) != MLA_OK) return s;
+  {
+    KernelTimer kt("decode_attn", st);
+    const int64_t items = static_cast<int64_t>(p.nch) * B * ((n_h + 127) / 128);
+    const int64_t blocks = (items + 7) / 8 * 16;
+    if (blocks > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "decode: too many workgroups");
+    hipLaunchKernelGGL(decode_attn_kernel, dim3(static_cast<unsigned>(blocks)), dim3(DWAVES * 64), 0,
+                       st, qlat, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c_kv),
+                       static_cast<const uint16_t*>(k_rope), cu_dev, opart, ml, n_h, B, p.nch,
+                       static_cast<int>(items), p.chunk, p.scale * 1.44269504088896340736f);
+  }
+  if ((s = check_launch("decode attention")) != MLA_OK) return s;
+  {
+    KernelTimer kt("decode_combine", st);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(n_h, B), dim3(128), 0, st, opart, ml, cu_dev,
+                       olat, lse, n_h, p.nch, p.chunk);
+  }
+  if ((s = check_launch("decode combine")) != MLA_OK) return s;
+  {
+    // out[b][h][d] = sum_c o_lat[b][h][c] W_UV[c][h*128 + d]
+    KernelTimer kt("decode_outproj", st);
+    hipLaunchKernelGGL((head_gemm_kernel<_Float16, float>), dim3(128 / 32, rtiles, n_h), dim3(64), 0,
+                       st, olat, static_cast<int64_t>(n_h) * DC, int64_t(DC), WTv, int64_t(DC),
+                       int64_t(128) * DC, out, static_cast<int64_t>(n_h) * 128, int64_t(128), B, 128,
+                       DC);
+  }
+  return check_launch("decode output projection");
+}
+
+}  // namespace mla

@@ -60,6 +60,23 @@ struct BwdLayout {
   int64_t total;
 };
 
+// Decode (absorbed form over the latent cache): one query per sequence.
+struct DecodePlan {
+  int n_h, batch;
+  int64_t S;          // cache rows over all sequences
+  float scale;
+  int chunk;          // keys per split-KV workgroup (a multiple of 32)
+  int nch;            // chunks of the longest sequence
+  int64_t total_keys;
+};
+struct DecodeLayout {
+  // W_UV^T fp16 [n_h*128][512]; q_lat, o_lat fp16 [batch][n_h][512];
+  // per-chunk partials fp16 [batch][nch][n_h][512] and (max, sum) [batch][nch][n_h]
+  int64_t WTv, qlat, olat, opart, ml;
+  int64_t total;
+};
+DecodeLayout decode_layout(const DecodePlan& p);
+
 FwdLayout fwd_layout(const Plan& p, bool fast);
 inline FwdLayout fwd_layout(const Plan& p) { return fwd_layout(p, p.fast); }
 BwdLayout bwd_layout(const Plan& p);
@@ -114,6 +131,9 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
                            const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* KfullT,
                            _Float16* Vt, _Float16* Vkm, hipStream_t st);
+mla_status fast_decode(const DecodePlan& p, const void* q, const void* c_kv, const void* k_rope,
+                       const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
+                       float* lse, char* ws, hipStream_t st);
 mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
                     const void* k_rope, const void* W_UK, const void* W_UV,
                     const int32_t* cu_dev, const float* out, const float* lse, float* dq,

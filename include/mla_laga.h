@@ -154,6 +154,51 @@ mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode in the absorbed form (inference only). The LAGA abstract names the
+ * absorbed MLA form -- W_UK folded into the query, attention over the
+ * compressed latent -- as the one allowed only in inference decode; it needs
+ * no per-head K/V. One query per sequence attends to every cached latent row
+ * of its sequence (it sits at the sequence's last position, its own latent
+ * row already appended):
+ *   q_lat = W_UK_h q_nope,  s_j = scale (q_lat . c_kv[j] + q_rope . k_rope[j]),
+ *   out   = W_UV_h^T sum_j softmax(s)_j c_kv[j],  lse = ln sum_j exp(s_j)
+ * which equals the explicit form (mla_laga_fwd) for that query.
+ * Takes bf16 inputs with d_c = 512, d_rope = 64, d_nope = d_v = 128 and n_h a
+ * multiple of 32 (MLA_ERR_UNSUPPORTED otherwise).
+ */
+typedef struct {
+  int32_t n_h, d_c, d_rope, d_nope, d_v;
+  int32_t batch;       /* sequences, one query each (>= 1)                      */
+  int64_t S;           /* cached latent rows over all sequences                 */
+  int32_t in_dtype;    /* MLA_BF16                                              */
+  float softmax_scale; /* <= 0: 1/sqrt(d_nope + d_rope)                         */
+} mla_laga_decode_desc;
+
+/*
+ * cu_seqlens_host: batch+1 int32 in host memory; sequence b owns cache rows
+ * [cu[b], cu[b+1]), at least one (cu strictly increasing, cu[0] = 0,
+ * cu[batch] = S). The workspace grows with batch * n_h * (longest sequence).
+ */
+mla_status mla_laga_decode_workspace_size(const mla_laga_decode_desc* desc,
+                                           const int32_t* cu_seqlens_host, size_t* bytes);
+
+/*
+ *   q        device [batch, n_h, d_nope + d_rope] bf16 (rope part rotated)
+ *   c_kv     device [S, d_c] bf16, k_rope device [S, d_rope] bf16: the cache
+ *   W_UK, W_UV device [d_c, n_h * 128] bf16 (head-major columns)
+ *   cu_seqlens_host / cu_seqlens_dev: the same batch+1 values, host and device
+ *   out      device [batch, n_h, d_v] float32 (written)
+ *   lse      device [batch, n_h] float32, natural log (written)
+ *   workspace device, >= mla_laga_decode_workspace_size bytes, 256-byte aligned.
+ * Conventions as for mla_laga_fwd.
+ */
+mla_status mla_laga_decode(const mla_laga_decode_desc* desc, const void* q, const void* c_kv,
+                           const void* k_rope, const void* W_UK, const void* W_UV,
+                           const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Host-side counts used for FLOP accounting: visible (query, key) pairs per
  * head, and the half-open latent row range [key_lo, key_hi) the shard needs.
  * Attention cost grows with the visible pairs, i.e. with the sum of squared

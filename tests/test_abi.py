@@ -207,3 +207,28 @@ def test_null_and_misaligned_pointers_rejected_before_launch(lib):
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4):
         assert lib.mla_laga_status_string(s).startswith(b"MLA_")
+
+
+def decode_desc(n_h=128, batch=4, S=100, d_c=512, d_rope=64, d_nope=128, d_v=128, dtype=None):
+    d = hla.MLADecodeDesc()
+    d.n_h, d.d_c, d.d_rope, d.d_nope, d.d_v = n_h, d_c, d_rope, d_nope, d_v
+    d.batch, d.S = batch, S
+    d.in_dtype = hla.MLA_BF16 if dtype is None else dtype
+    d.softmax_scale = 0.0
+    return d
+
+
+def test_decode_validation_and_workspace():
+    cu = np.array([0, 10, 11, 60, 100], np.int32)
+    ws = hla.mla_laga_decode_workspace_size(decode_desc(), cu)
+    assert ws > 128 * 128 * 512 * 2            # at least W_UV^T in fp16
+    longer = np.array([0, 10, 11, 60, 100000], np.int32)
+    assert hla.mla_laga_decode_workspace_size(decode_desc(S=100000), longer) > ws
+    E, U = hla.MLA_ERR_INVALID_ARG, hla.MLA_ERR_UNSUPPORTED
+    bad(E, hla.mla_laga_decode_workspace_size, decode_desc(batch=0), np.array([0], np.int32))
+    bad(E, hla.mla_laga_decode_workspace_size, decode_desc(), np.array([0, 10, 10, 60, 100], np.int32))
+    bad(E, hla.mla_laga_decode_workspace_size, decode_desc(), np.array([0, 10, 11, 60, 99], np.int32))
+    bad(E, hla.mla_laga_decode_workspace_size, decode_desc(), None)
+    bad(U, hla.mla_laga_decode_workspace_size, decode_desc(d_c=256), cu)
+    bad(U, hla.mla_laga_decode_workspace_size, decode_desc(n_h=48), cu)
+    bad(U, hla.mla_laga_decode_workspace_size, decode_desc(dtype=hla.MLA_F32), cu)

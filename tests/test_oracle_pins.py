@@ -388,3 +388,21 @@ def test_flops_headline_shard():
     assert oracle.visible_pairs(2048, 14336) == pairs == 31_458_304
     assert f == 2 * 128 * 320 * pairs + 2 * 128 * 512 * 256 * 16384
     assert abs(f / 1e12 - 3.127) < 1e-3
+
+
+def test_decode_batch_absorbed_equals_explicit():
+    """A decode batch (one query per packed sequence, at its last position)
+    computed in the absorbed form equals the explicit form (LAGA abstract:
+    the absorbed form is a reformulation, used for decode)."""
+    lens = [1, 4, 9, 2]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    last = [(int(cu[b + 1]) - 1, 1) for b in range(len(lens))]
+    x = rand_inputs(n_h=3, S=int(cu[-1]), S_loc=len(lens), seed=71)
+    o1, l1 = oracle.mla_forward(**x, cu_seqlens=cu, q_ranges=last)
+    o2, l2 = oracle.mla_forward_absorbed(**x, cu_seqlens=cu, q_ranges=last)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-13)
+    # the one-key sequence attends to its own row only: out = V of that row
+    c = x["c_kv"][0]
+    for h in range(3):
+        np.testing.assert_allclose(o1[0, h], c @ x["W_UV"][:, 4 * h:4 * (h + 1)], rtol=1e-12)

@@ -41,6 +41,9 @@ __all__ = [
     "cu_seqlens_from_lengths",
     "make_inputs",
     "zigzag_blocks",
+    "decode_config",
+    "lognormal_count",
+    "DECODE_CONFIGS",
 ]
 
 
@@ -67,6 +70,8 @@ class MLAConfig:
     # several position blocks instead of [q_offset, q_offset + S_loc): a
     # tuple of (start, length); q_offset is then 0
     q_ranges: Optional[Tuple[Tuple[int, int], ...]] = None
+    # explicit sample lengths (packed samples; overrides the lognormal draw)
+    seq_lens: Optional[Tuple[int, ...]] = None
 
     @property
     def d_qk(self) -> int:
@@ -76,6 +81,8 @@ class MLAConfig:
         return dataclasses.replace(self, **kw)
 
     def cu_seqlens(self) -> Optional[np.ndarray]:
+        if self.seq_lens is not None:
+            return cu_seqlens_from_lengths(self.seq_lens)
         if self.varlen_median is None:
             return None
         lens = lognormal_lengths(self.S, self.varlen_median, self.varlen_sigma,
@@ -123,6 +130,8 @@ for _r in (0, 7):
     CONFIGS[f"h128_s16k_zigzag_r{_r}"] = MLAConfig(
         f"h128_s16k_zigzag_r{_r}", n_h=128, S=16384, S_loc=2048, q_offset=0, dtype="bf16",
         backward=True, q_ranges=zigzag_blocks(16384, _r, 8), **_DSV3)
+
+
 
 # the five configurations, in the order they are listed with the method's targets
 CONFIG_ORDER: List[str] = ["tiny_f32", "h16_s4k", "h128_s16k_shard",
@@ -224,3 +233,33 @@ def make_inputs(cfg: MLAConfig, seed: Optional[int] = None,
     if cu is not None:
         out["cu_seqlens"] = cu
     return out
+
+def decode_config(name: str, n_h: int, lens, seed: int = 0) -> MLAConfig:
+    """Decode batch: one query per sequence, at the last position of its
+    cached latent rows (the packed cache holds the sequences end to end).
+    The query rows are those last positions, so the oracle reads them as
+    one-row position blocks."""
+    lens = tuple(int(x) for x in lens)
+    cu = cu_seqlens_from_lengths(lens)
+    last = tuple((int(cu[b + 1]) - 1, 1) for b in range(len(lens)))
+    return MLAConfig(name, n_h=n_h, S=int(cu[-1]), S_loc=len(lens), q_offset=0, dtype="bf16",
+                     seq_lens=lens, q_ranges=last, seed=seed, **_DSV3)
+
+
+def lognormal_count(count: int, median: int, sigma: float, cap: int, seed: int = 0) -> List[int]:
+    """`count` lengths clip(round(exp(ln(median) + sigma z)), 1, cap), z drawn
+    one at a time from a fresh default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    mu = math.log(median)
+    return [max(1, min(cap, int(round(math.exp(mu + sigma * float(rng.standard_normal()))))))
+            for _ in range(count)]
+
+
+# decode batches (absorbed form over the latent cache): 64 sequences of 8192
+# cached rows, and 32 sequences of long-tailed lengths (median 4096)
+DECODE_CONFIGS: Dict[str, MLAConfig] = {
+    "decode_h128_b64_l8k": decode_config("decode_h128_b64_l8k", 128, [8192] * 64),
+    "decode_h128_b32_mixed": decode_config("decode_h128_b32_mixed", 128,
+                                           lognormal_count(32, 4096, 1.0, 32768, seed=0)),
+}
+CONFIGS.update(DECODE_CONFIGS)
