@@ -420,6 +420,14 @@ constexpr int P_NPW = (P_PIECES + 7) / 8;      // 7 per wave
 constexpr int P_XCH = 2 * P_BYTES;             // P slots: [pair][buffer] x 2 KiB
 static_assert(P_DON >= QB * XS_ROW && P_INFO - P_DON >= QB * PD_ROW && P_BYTES - P_INFO >= QB * 16,
               "paired dK/dV stage layout");
+// dKV^T staging tile after the loop: 256 dims x 128 keys, rows padded to 136
+// halves (272 bytes, an odd number of 16-byte slots)
+constexpr int T_PITCH = 136;
+// ... then dKr rows: 128 keys x 64 floats, padded to 68 (272 bytes); then
+// dKV rows: 128 keys x 256 halves, padded to 264 (528 bytes, odd slot count)
+constexpr int R_PITCH = 68, K_PITCH = 264;
+static_assert(256 * T_PITCH * 2 + 128 * R_PITCH * 4 <= 2 * P_BYTES + 4 * 2 * 2048 &&
+              128 * K_PITCH * 2 <= 2 * P_BYTES + 4 * 2 * 2048, "staging tiles fit the LDS");
 
 __global__ void __launch_bounds__(512)
 attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
@@ -669,33 +677,67 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
       __syncthreads();
     }
 
-    // write: lane = key t, registers = dims (four consecutive per group)
-    const int64_t t = tw + lr;
-    const int64_t nk = static_cast<int64_t>(n_h) * 128;
+    // write: lane = key t, registers = dims (four consecutive per group).
+    // Every output leaves through LDS in whole rows: first dKV^T (one dim,
+    // the workgroup's 128 keys = 256 bytes per row) together with the fp32
+    // rope part of dK (dKr: 128 keys x 64 floats, one contiguous 32 KiB
+    // block), then dKV row-major (one key, 2 x 256 bytes).
     const int nacc = kA ? 4 : 6;
+    const int64_t nk = static_cast<int64_t>(n_h) * 128;
+    const int key = 32 * pi + lr;                           // key within the workgroup
+    const float sc = kA ? 1.f : scale;
+    _Float16* tile = reinterpret_cast<_Float16*>(smem);     // [256 dims][T_PITCH] (free after the loop)
+    float* rtile = reinterpret_cast<float*>(smem + 256 * T_PITCH * 2);   // [128 keys][R_PITCH]
   #pragma unroll
     for (int mt = 0; mt < 6; ++mt) {
       if (mt >= nacc) break;
   #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3
-        const float sc = kA ? 1.f : scale;
-        const float v0 = acc[mt][4 * g] * sc, v1 = acc[mt][4 * g + 1] * sc,
-                    v2 = acc[mt][4 * g + 2] * sc, v3 = acc[mt][4 * g + 3] * sc;
         if (d < 128) {
-          const int64_t col = (kA ? nk : 0) + static_cast<int64_t>(h) * 128 + d;
-          const half4 hv = {static_cast<_Float16>(v0), static_cast<_Float16>(v1),
-                            static_cast<_Float16>(v2), static_cast<_Float16>(v3)};
-          *reinterpret_cast<half4*>(dKV + t * (2 * nk) + col) = hv;
-          dKVT[(col + 0) * Kpad + t] = hv[0];
-          dKVT[(col + 1) * Kpad + t] = hv[1];
-          dKVT[(col + 2) * Kpad + t] = hv[2];
-          dKVT[(col + 3) * Kpad + t] = hv[3];
+          const int r = (kA ? 128 : 0) + d;       // tile row of dim d
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) tile[(r + e) * T_PITCH + key] = static_cast<_Float16>(acc[mt][4 * g + e] * sc);
         } else {
-          const f32x4 fv = {v0, v1, v2, v3};
-          *reinterpret_cast<f32x4*>(dKr + (static_cast<int64_t>(h) * Kpad + t) * 64 + (d - 128)) = fv;
+          const f32x4 fv = {acc[mt][4 * g] * sc, acc[mt][4 * g + 1] * sc, acc[mt][4 * g + 2] * sc,
+                            acc[mt][4 * g + 3] * sc};
+          *reinterpret_cast<f32x4*>(rtile + key * R_PITCH + (d - 128)) = fv;
         }
       }
+    }
+    __syncthreads();   // both roles' rows written
+    // dKV^T rows h*128 + d (dK_nope) and nk + h*128 + d (dV), keys t0 .. t0+127
+    for (int e = tid; e < 256 * 16; e += 512) {
+      const int r = e >> 4, c = e & 15;
+      const int64_t col = (r < 128 ? 0 : nk) + static_cast<int64_t>(h) * 128 + (r & 127);
+      *reinterpret_cast<u32x4*>(dKVT + col * Kpad + t0 + 8 * c) =
+          *reinterpret_cast<const u32x4*>(tile + r * T_PITCH + 8 * c);
+    }
+    // dKr[h][t0 .. t0+127][64]: contiguous
+    float* kr = dKr + (static_cast<int64_t>(h) * Kpad + t0) * 64;
+    for (int e = tid; e < 128 * 16; e += 512) {
+      const int k = e >> 4, c = e & 15;
+      *reinterpret_cast<f32x4*>(kr + k * 64 + 4 * c) = *reinterpret_cast<const f32x4*>(rtile + k * R_PITCH + 4 * c);
+    }
+    __syncthreads();   // the tiles are read; reuse the space row-major
+    _Float16* rows = reinterpret_cast<_Float16*>(smem);     // [128 keys][K_PITCH]: dK_nope | dV
+  #pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * mt + 8 * g + 4 * lh;
+        const half4 hv = {static_cast<_Float16>(acc[mt][4 * g] * sc), static_cast<_Float16>(acc[mt][4 * g + 1] * sc),
+                          static_cast<_Float16>(acc[mt][4 * g + 2] * sc), static_cast<_Float16>(acc[mt][4 * g + 3] * sc)};
+        *reinterpret_cast<half4*>(rows + key * K_PITCH + (kA ? 128 : 0) + d) = hv;
+      }
+    }
+    __syncthreads();
+    // dKV[t0 + k][h*128 ..] (dK_nope) and [nk + h*128 ..] (dV): 2 x 256 bytes per key
+    for (int e = tid; e < 128 * 32; e += 512) {
+      const int k = e >> 5, c = e & 31;   // c < 16: dK_nope, else dV
+      const int64_t col = (c < 16 ? 0 : nk) + static_cast<int64_t>(h) * 128 + 8 * (c & 15);
+      *reinterpret_cast<u32x4*>(dKV + (t0 + k) * (2 * nk) + col) =
+          *reinterpret_cast<const u32x4*>(rows + k * K_PITCH + 8 * c);
     }
   };
   if (role_a) run(std::true_type());
