@@ -32,6 +32,13 @@ def small(name, n_h, S, S_loc, q_offset, cu=None, backward=True, seed=3, q_range
     return cfg, (None if cu is None else np.array(cu, np.int32))
 
 
+def small_dc(name, d_c, n_h, S, S_loc, q_offset, cu=None):
+    """Fast path at another latent width (d_c a multiple of 64)."""
+    cfg = workloads.MLAConfig(name, n_h=n_h, d_c=d_c, d_rope=64, d_nope=128, d_v=128, S=S,
+                              S_loc=S_loc, q_offset=q_offset, dtype="bf16", backward=True, seed=4)
+    return cfg, (None if cu is None else np.array(cu, np.int32))
+
+
 def positions(cfg):
     """Oracle keyword arguments that place the rows (one block or several)."""
     return dict(q_offset=cfg.q_offset, q_ranges=cfg.q_ranges)
@@ -58,6 +65,12 @@ SMALL = [
     small("blocks_unseen_sample", 2, 700, 0, 0, cu=[0, 200, 450, 700],
           q_ranges=((10, 150), (470, 200))),
     small("zigzag_r1_of_4", 2, 1024, 0, 0, q_ranges=workloads.zigzag_blocks(1024, 1, 4)),
+    # the most position blocks a call takes, over packed samples
+    small("sixteen_blocks", 2, 2000, 0, 0, cu=[0, 3, 400, 401, 1250, 2000],
+          q_ranges=tuple((125 * k + 11 * (k % 3), 1 + 6 * k) for k in range(16))),
+    # other latent widths on the fast path
+    small_dc("d_c_256", 256, 3, 700, 333, 367),
+    small_dc("d_c_1024", 1024, 2, 600, 450, 150, cu=[0, 1, 1, 130, 131, 400, 600]),
 ]
 
 
