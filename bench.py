@@ -45,8 +45,8 @@ def kernel_flops(name, cfg, pairs, kn):
     (640 per visible pair and head forward, 1664 backward, plus the
     up-projection of the needed keys) over the kernels, each product once:
     the backward's S = Q K^T and dP = dO V^T go to the dK/dV kernel; the dQ
-    kernel recomputes them (and, on the split path, the dV kernel S), and
-    the backward's K/V rebuild launches recompute the up-projection."""
+    kernel recomputes them, and the backward's K/V rebuild launches
+    recompute the up-projection."""
     d_qk = cfg.d_nope + cfg.d_rope
     up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
     per_pair = lambda d: 2 * cfg.n_h * d * pairs  # noqa: E731
@@ -57,10 +57,7 @@ def kernel_flops(name, cfg, pairs, kn):
         "plain_attn_fwd": (per_pair(d_qk + cfg.d_v),) * 2,
         # paired dK/dV: S, dP, dV += P^T dO, dK += dS^T Q (each once)
         "attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
-        # split dK/dV launches: dK: S, dP, dK += dS^T Q;  dV: dV += P^T dO (S
-        # recomputed);  dQ: dQ = dS K (S and dP recomputed)
-        "attn_bwd_dk": (per_pair(2 * d_qk + cfg.d_v),) * 2,
-        "attn_bwd_dv": (per_pair(cfg.d_v), per_pair(d_qk + cfg.d_v)),
+        # dQ: dQ = dS K (S and dP recomputed)
         "attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
         "plain_attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
         "plain_attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
@@ -78,8 +75,6 @@ CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")
 COUNTED_KERNELS = {
     "attn_fwd_kernel": ("attn_fwd", ["fast_fwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
-    "attn_bwd_dkv_kernelILb1": ("attn_bwd_dk", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
-    "attn_bwd_dkv_kernelILb0": ("attn_bwd_dv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dq_kernel": ("attn_bwd_dq", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"

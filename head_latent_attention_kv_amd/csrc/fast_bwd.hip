@@ -6,17 +6,18 @@
 //   prep      D = rowsum(dout * out); q and dout to fp16, per head,
 //             row-major [row][dim]
 //   rebuild   K_nope and V again (fp16), in the layouts the kernels read
-//   dK, dV    key-outer, two launches: each wave owns 32 keys and steps
-//             over query rows; S = Q K^T lands with lanes on keys, so P and
-//             dS feed dV^T += dO^T P and dK^T += Q^T dS from registers.
+//   dK, dV    key-outer, one launch of paired waves: a pair owns 32 keys
+//             and steps over query rows; S = Q K^T lands with lanes on keys
+//             and, with the query rows loaded in swap23 order, P and dS are
+//             already the k-operands of dV^T += dO^T P and dK^T += Q^T dS.
 //   dq        query-outer: each wave owns 32 rows (two waves per SIMD); S^T,
 //             dP^T per lane = row, dQ^T += K^T dS^T. No atomics: the result
 //             is deterministic.
 //   GEMMs     dc_kv = [dK_nope | dV] [W_UK | W_UV]^T,  dW = c_kv^T [dK_nope | dV]
 //   reduce    dk_rope = sum over heads of the per-head rope-key gradients
 //
-// Query/key tiles are DMA-filled (global_load_lds) into padded LDS rows and
-// double-buffered, as in the forward.
+// Query/key tiles are DMA-filled (global_load_lds) into swizzled LDS rows
+// and double-buffered, as in the forward.
 #include <math.h>
 #include <stdlib.h>
 
@@ -104,297 +105,8 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
   }
 }
 
-// ------------------------------------------------------------------ dK, dV
-// Key-outer, in two launches: one accumulates dK (S, dP, dS, then Q^T dS),
-// the other dV (S, P, then dO^T P). Computing S twice costs 12 of every 52
-// products, but it keeps each wave's live registers (its keys' K and V rows,
-// 96 or 64 accumulators) within 256, so two waves share each SIMD and one's
-// softmax overlaps the other's MFMAs. A workgroup owns 256 keys (8 waves x
-// 32) and steps over query blocks of 64 rows (two sub-blocks of 32).
-//
-// S = Q K^T lands with lanes on keys and registers on query rows; with the
-// query rows loaded in swap23 order, register j of the fp16 P (or dS) pair
-// ks holds query 16 ks + 8 lh + j, which is the k-slot order of the next
-// product's B operand, so P and dS feed dV^T += dO^T P and dK^T += Q^T dS
-// without leaving registers.
-//
-// LDS tiles carry a 16-byte pad per row (row strides of 25, 17 or 9 sixteen-
-// byte slots, all odd): the 16 lanes served together then hit 16 different
-// slots of the 64 banks, and fragment addresses are a per-lane base plus a
-// compile-time offset. Tile regions start on 1 KiB boundaries so each DMA
-// wave instruction (1 KiB) lies in one region.
-constexpr int KW = 256;     // keys per workgroup (8 waves x 32)
-constexpr int QB = 64;      // query rows per step
-// Row strides: Q 448 B, swizzled (read row-wise and, in the dK launch,
-// transposed); dO 272 B where it is read row-wise (dP = dO V^T in the dK
-// launch) and 320 B where it is read transposed (dV^T += dO^T P): a
-// transposed read of rows 256 or 272 B apart runs at half rate.
-constexpr int QN_ROW = XS_ROW, DONK_ROW = DV * 2 + 16, DONV_ROW = DV * 2 + 64;  // 448, 272, 320
-// stage (bytes): Qn [64 rows] | dOn [64 rows] | row info. Q^T and dO^T
-// fragments (the A operands of dK^T and dV^T) are transposed reads of them.
-constexpr int S_QN = 0, S_DON = 28 * 1024;
-constexpr int SK_INFO = 45 * 1024, SK_BYTES = 46 * 1024;
-constexpr int SV_INFO = 48 * 1024, SV_BYTES = 49 * 1024;
-static_assert(S_DON >= QB * QN_ROW && SK_INFO - S_DON >= QB * DONK_ROW &&
-              SK_BYTES - SK_INFO >= QB * 16, "dK stage layout");
-static_assert(SV_INFO - S_DON >= QB * DONV_ROW && SV_BYTES - SV_INFO >= QB * 16, "dV stage layout");
-
-template <bool kDK>
-__global__ void __launch_bounds__(512)
-attn_bwd_dkv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
-                    const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
-                    const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
-                    _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
-                    float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
-                    RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
-  constexpr int BYTES = kDK ? SK_BYTES : SV_BYTES;
-  constexpr int INFO = kDK ? SK_INFO : SV_INFO;
-  constexpr int DON_ROW = kDK ? DONK_ROW : DONV_ROW;
-  constexpr int PIECES = BYTES / 1024;          // DMA wave instructions per stage
-  constexpr int NPW = (PIECES + 7) / 8;         // per wave
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BYTES];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const int lr = lane & 31, lh = lane >> 5;
-  int h, kt;
-  work_item(blockIdx.x, n_h, n_kt, &h, &kt);
-  const int t0 = kt * KW;                     // workspace key row of the workgroup
-  const int tw = t0 + 32 * w;                 // this wave's first key
-  const int gkey = key_lo + tw + lr;          // this lane's key (global)
-  const int gk_min = key_lo + t0, gk_max = key_lo + t0 + KW - 1;
-  const int gw_min = key_lo + tw, gw_max = gw_min + 31;
-
-  // this lane's key row of K (and, for dK, of V) as MFMA B fragments
-  half8 kf[12], vf[kDK ? 8 : 1];
-  {
-    const _Float16* kr = Kfull + (static_cast<int64_t>(h) * Kpad + tw + lr) * DQK + 8 * lh;
-#pragma unroll
-    for (int kk = 0; kk < 12; ++kk) kf[kk] = *reinterpret_cast<const half8*>(kr + 16 * kk);
-    if constexpr (kDK) {
-      const _Float16* vr = Vkm + (static_cast<int64_t>(h) * Kpad + tw + lr) * DV + 8 * lh;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) vf[kk] = *reinterpret_cast<const half8*>(vr + 16 * kk);
-    }
-  }
-
-  // query rows that see any key of the workgroup: from the first row at or
-  // past its first key to the last row whose sample starts by its last key
-  const int i_begin = rm_rows_below(rm, gk_min);
-  int i_end = S_loc;
-  if (n_seqs > 0) {
-    // first sample start after gk_max (none: S): rows from there on see nothing here
-    int lo_i = 0, hi_i = n_seqs + 1;
-    while (hi_i - lo_i > 1) {
-      const int mid = (lo_i + hi_i) >> 1;
-      if (cu[mid] <= gk_max) lo_i = mid; else hi_i = mid;
-    }
-    if (lo_i + 1 <= n_seqs) i_end = rm_rows_below(rm, cu[lo_i + 1]);
-  }
-  const int qb_begin = (i_begin / QB) * QB;
-  const int nq = i_end > qb_begin ? (i_end - qb_begin + QB - 1) / QB : 0;
-
-  // DMA: per-lane source offsets (elements) relative to the region's first
-  // row qb; a region's pad slots reload a valid element and are never read
-  const _Float16* Qn_h = Qn + static_cast<int64_t>(h) * S_pad * DQK;
-  const _Float16* dOn_h = dOn + static_cast<int64_t>(h) * S_pad * DV;
-  const uint32_t* info_h = info + static_cast<int64_t>(h) * (S_pad / 32) * 128;
-  int doff[NPW];
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) {
-    const int o = (w * NPW + j) * 1024 + lane * 16;
-    int off = 0;
-    if (o < S_DON) {   // swizzled Q rows; pad slots 24..27 reload slot 0
-      const int row = min(o / QN_ROW, QB - 1), ph = (o % QN_ROW) >> 4;
-      off = row * DQK + (ph < DQK / 8 ? xs_slot(row, ph) : 0) * 8;
-    } else if (o >= INFO) {
-      off = min((o - INFO) >> 2, 2 * 128 - 4);   // 4-byte elements, 128 per 32 rows
-    } else {
-      const int oo = o - S_DON, row = min(oo / DON_ROW, QB - 1), pc = min((oo % DON_ROW) >> 4, DV / 8 - 1);
-      off = row * DV + pc * 8;
-    }
-    doff[j] = off;
-  }
-  auto issue = [&](int qb, int st) {
-    char* sbase = smem + st * BYTES;
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) {
-      const int I = w * NPW + j;   // wave-uniform region choice
-      if (I < PIECES) {
-        // wave-uniform base plus an unsigned 32-bit lane offset in bytes
-        // (the scalar-base form of the load); the offset is opaque to the
-        // optimizer, so it cannot hoist one 64-bit address per piece
-        uint32_t off = static_cast<uint32_t>(doff[j]) * (I * 1024 >= INFO ? 4u : 2u);
-        asm volatile("" : "+v"(off));
-        const char* ub;
-        if (I * 1024 < S_DON) ub = reinterpret_cast<const char*>(Qn_h + static_cast<int64_t>(qb) * DQK);
-        else if (I * 1024 >= INFO) ub = reinterpret_cast<const char*>(info_h + (qb / 32) * 128);
-        else ub = reinterpret_cast<const char*>(dOn_h + static_cast<int64_t>(qb) * DV);
-        lds_dma16(ub + off, sbase + I * 1024);
-      }
-    }
-  };
-
-  constexpr int NACC = kDK ? 6 : 4;   // 32-dim tiles of dK^T (192) or dV^T (128)
-  f32x16 acc[NACC];
-#pragma unroll
-  for (int a = 0; a < NACC; ++a)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
-
-  const int qrow = swap23(lr);   // A-operand row loaded by this lane
-  const int a_qn0 = S_QN + xs_row_base(qrow, lh, 0), a_qn1 = S_QN + xs_row_base(qrow, lh, 1);
-  const int a_don = S_DON + qrow * DON_ROW + lh * 16;
-  // Q^T (dK) or dO^T (dV) fragments: transposed reads of the row tiles
-  const int a_t0 = kDK ? S_QN + xs_tr_base(lane, 0) : S_DON + tr_lane_offset(lane, DON_ROW);
-  const int a_t1 = kDK ? S_QN + xs_tr_base(lane, 1) : 0;
-
-  if (nq > 0) issue(qb_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int b = 0; b < nq; ++b) {
-    const int st = b & 1;
-    const int qb = qb_begin + b * QB;
-    if (b + 1 < nq) issue(qb + QB, st ^ 1);
-    const char* base = smem + st * BYTES;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int q0 = qb + 32 * mt;
-      const float* rinfo = reinterpret_cast<const float*>(base + INFO + mt * 512);
-      const int32_t* iinfo = reinterpret_cast<const int32_t*>(rinfo + 64);
-      // first and last position of the sub-block's rows (positions increase
-      // with the row; rows past S_loc hold position -1)
-      const int p_first = iinfo[32];
-      const int p_last = iinfo[31 + max(min(32, S_loc - q0), 1)];
-      const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
-      if (skip) continue;
-      const bool full = q0 + 32 <= S_loc && p_first >= gw_max && iinfo[31] <= gw_min;
-      // S = Q K^T (12 steps)
-      f32x16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      {
-        auto frag = [&](int k) {
-          return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_qn1 : a_qn0) + mt * 32 * QN_ROW + 64 * (k >> 1));
-        };
-        half8 fa[3];
-        fa[0] = frag(0);
-        fa[1] = frag(1);
-#pragma unroll
-        for (int k = 0; k < 12; ++k) {
-          if (k + 2 < 12) fa[(k + 2) % 3] = frag(k + 2);
-          s = mfma_f16(fa[k % 3], kf[k], s);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (!full) {
-        // rows that do not see this lane's key get weight 0 (score -> -inf)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = swap23(d_row(4 * g, lh));
-          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(iinfo + r0);
-          const u32x4 p4 = *reinterpret_cast<const u32x4*>(iinfo + 32 + r0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (gkey < static_cast<int>(lo4[e]) || gkey > static_cast<int>(p4[e])) s[4 * g + e] = -INFINITY;
-        }
-      }
-      // P = exp2(S scale log2e - lse log2e). Register r holds row
-      // swap23(d_row(r, lh)); groups of 4 are consecutive rows. The dV launch
-      // feeds P (fp16) on; the dK launch computes dP = dO V^T and then
-      // dS = P (dP - D) from the fp32 P.
-      half8 bf[2];
-      if constexpr (kDK) {
-        f32x16 dp;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dp[e] = 0.f;
-        auto frag = [&](int k) {
-          return *reinterpret_cast<const half8*>(base + a_don + mt * 32 * DON_ROW + 32 * k);
-        };
-        half8 fa[3];
-        fa[0] = frag(0);
-        fa[1] = frag(1);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k + 2 < 8) fa[(k + 2) % 3] = frag(k + 2);
-          dp = mfma_f16(fa[k % 3], vf[k], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
-          const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e]));
-            bf[r >> 3][r & 7] = static_cast<_Float16>(pr * (dp[r] - Dd[e]));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 L = *reinterpret_cast<const f32x4*>(rinfo + swap23(d_row(4 * g, lh)));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            bf[r >> 3][r & 7] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -L[e])));
-          }
-        }
-      }
-      // acc^T (dims x keys) += A^T (dims x rows) . bf (rows x keys), rows as k-slots
-      {
-        constexpr int NM = 2 * NACC;
-        auto frag = [&](int k) {
-          const int ks = k / NACC, dm = k % NACC;
-          // dims 32 dm + lr, rows 32 mt + 16 ks + 8 lh + j
-          if constexpr (kDK) {
-            const int o = (32 * mt + 16 * ks) * QN_ROW + 64 * dm;
-            return frag_tr2(base + a_t0 + o, base + a_t1 + o);
-          } else {
-            return frag_tr<DONV_ROW>(base + a_t0 + (32 * mt + 16 * ks) * DONV_ROW + 32 * dm * 2);
-          }
-        };
-        half8 fa[3];
-        fa[0] = frag(0);
-        fa[1] = frag(1);
-#pragma unroll
-        for (int k = 0; k < NM; ++k) {
-          if (k + 2 < NM) fa[(k + 2) % 3] = frag(k + 2);
-          acc[k % NACC] = mfma_f16(fa[k % 3], bf[k / NACC], acc[k % NACC]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  // write: lane = key t, registers = dims (four consecutive per group)
-  const int64_t t = tw + lr;
-  const int64_t nk = static_cast<int64_t>(n_h) * 128;
-#pragma unroll
-  for (int mt = 0; mt < NACC; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3
-      const float sc = kDK ? scale : 1.f;
-      const float v0 = acc[mt][4 * g] * sc, v1 = acc[mt][4 * g + 1] * sc,
-                  v2 = acc[mt][4 * g + 2] * sc, v3 = acc[mt][4 * g + 3] * sc;
-      if (d < 128) {
-        const int64_t col = (kDK ? 0 : nk) + static_cast<int64_t>(h) * 128 + d;
-        const half4 hv = {static_cast<_Float16>(v0), static_cast<_Float16>(v1),
-                          static_cast<_Float16>(v2), static_cast<_Float16>(v3)};
-        *reinterpret_cast<half4*>(dKV + t * (2 * nk) + col) = hv;
-        dKVT[(col + 0) * Kpad + t] = hv[0];
-        dKVT[(col + 1) * Kpad + t] = hv[1];
-        dKVT[(col + 2) * Kpad + t] = hv[2];
-        dKVT[(col + 3) * Kpad + t] = hv[3];
-      } else {
-        const f32x4 fv = {v0, v1, v2, v3};
-        *reinterpret_cast<f32x4*>(dKr + (static_cast<int64_t>(h) * Kpad + t) * 64 + (d - 128)) = fv;
-      }
-    }
-}
+// ------------------------------------------------------------------ shared by dK/dV and dQ
+constexpr int QB = 64;      // query rows per step of the key-outer kernel
 
 // ------------------------------------------------------------------ dK + dV, paired waves
 // One launch for dK and dV without computing S twice. A workgroup owns 128
@@ -966,15 +678,6 @@ zero_rows_kernel(float* __restrict__ p, int64_t n) {
     p[e] = 0.f;
 }
 
-// dK and dV in one paired launch (default) or two (MLA_LAGA_BWD_SPLIT=1).
-bool bwd_paired() {
-  static const bool v = [] {
-    const char* e = getenv("MLA_LAGA_BWD_SPLIT");
-    return !(e && atoi(e) == 1);
-  }();
-  return v;
-}
-
 unsigned grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   return static_cast<unsigned>(g < 1 ? 1 : (g > 16384 ? 16384 : g));
@@ -1041,35 +744,18 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
       qorder = reinterpret_cast<int*>(at(L.order));
       korder = qorder + n_qt;
       if ((s = launch_tile_order(cu_dev, p.n_seqs, p.S_loc, p.rm, p.key_lo, p.Kn, n_qt, n_kt,
-                                 qorder, bwd_paired() ? korder : nullptr, st)) != MLA_OK)
+                                 qorder, korder, st)) != MLA_OK)
         return s;
-      if (!bwd_paired()) korder = nullptr;
     }
   }
-  if (bwd_paired()) {
+  {
     const int n_kt = static_cast<int>(p.Kpad / PW);
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
                        st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
                        Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
-  } else {
-    const int n_kt = static_cast<int>(p.Kpad / KW);
-    const unsigned grid = static_cast<unsigned>(n_kt * p.n_h);
-    {
-      KernelTimer kt("attn_bwd_dk", st);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<true>, dim3(grid), dim3(512), 0, st, Qn, dOn,
-                         info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
-                         p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
-    }
-    if ((s = check_launch("attention backward dK")) != MLA_OK) return s;
-    {
-      KernelTimer kt("attn_bwd_dv", st);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<false>, dim3(grid), dim3(512), 0, st, Qn, dOn,
-                         info, Kfull, Vkm, cu_dev, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc, Sp,
-                         p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
-    }
   }
-  if ((s = check_launch("attention backward dV")) != MLA_OK) return s;
+  if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
     KernelTimer kt("attn_bwd_dq", st);

@@ -63,9 +63,9 @@ __device__ __forceinline__ void work_item(int bid, int n_h, int n_qt, const int*
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // NT: 32-row query tiles per wave; NW: waves per workgroup (NT*NW*32 = 256).
-// NT = 2 keeps 64 rows per wave (half the LDS reads per MFMA, one wave per
-// SIMD); NT = 1 fits two waves per SIMD, which lets one wave's softmax run
-// while the other's MFMAs do.
+// Only NT = 1, NW = 8 is built: two waves per SIMD let one wave's softmax run
+// while the other's MFMAs do. NT = 2 (64 rows per wave, half the LDS reads
+// per MFMA, one wave per SIMD) measured slower.
 template <int NT, int NW>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfull,
@@ -74,6 +74,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
                 int n_h, int n_seqs, int S_loc, RowMap rm, int key_lo, int Kpad, int n_qt,
                 float scale_log2) {
   static_assert(NT * NW * 32 == FQ, "workgroup covers 256 query rows");
+  static_assert(NT == 1, "only the 32-row-per-wave form is built");
   constexpr int NP = (STAGE_PIECES + NW - 1) / NW;  // DMA pieces per wave and stage
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_B];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -292,17 +293,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
   }
 }
 
-// Which attention tiling to launch: 1 = 32 rows per wave, two waves per SIMD
-// (default), 2 = 64 rows per wave, one wave per SIMD. MLA_LAGA_ATTN_VARIANT
-// overrides it.
-int attn_fwd_variant() {
-  static const int v = [] {
-    const char* e = getenv("MLA_LAGA_ATTN_VARIANT");
-    return e ? atoi(e) : 1;
-  }();
-  return v;
-}
-
 }  // namespace
 
 // Rebuild per-head keys and values from the latent (MFMA GEMMs), in the
@@ -380,14 +370,9 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   const int S_loc = static_cast<int>(p.S_loc), key_lo = static_cast<int>(p.key_lo), Kpad = static_cast<int>(p.Kpad);
   {
     KernelTimer kt("attn_fwd", st);
-    if (attn_fwd_variant() == 2)
-      hipLaunchKernelGGL((attn_fwd_kernel<2, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
-                         p.n_seqs, S_loc, p.rm, key_lo, Kpad, n_qt, scale_log2);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<1, 8>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
-                         st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
-                         p.n_seqs, S_loc, p.rm, key_lo, Kpad, n_qt, scale_log2);
+    hipLaunchKernelGGL((attn_fwd_kernel<1, 8>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
+                       st, static_cast<const uint16_t*>(q), Kfull, Vt, cu_dev, order, out, lse, p.n_h,
+                       p.n_seqs, S_loc, p.rm, key_lo, Kpad, n_qt, scale_log2);
   }
   return check_launch("attention forward");
 }
