@@ -279,6 +279,37 @@ def decode_bench(name, steps, warmup):
     print(json.dumps(res), flush=True)
 
 
+def device_info(torch):
+    """Compute units and the maximum shader clock of GPU 0, and the dense
+    fp16/bf16 MFMA peak they imply (4096 FLOP per clock per CU). The clock
+    comes from rocminfo; null when it cannot be read."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "max_sclk_mhz": None, "peak_tflops_derived": None}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        gpu = False
+        for line in txt.splitlines():
+            if "Name:" in line and "gfx" in line:
+                gpu = True
+            if gpu and "Max Clock Freq. (MHz):" in line:
+                info["max_sclk_mhz"] = int(line.split(":")[1].split()[0])
+                break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    if info["max_sclk_mhz"]:
+        info["peak_tflops_derived"] = round(info["cus"] * info["max_sclk_mhz"] * 1e6 * 4096 / 1e12, 1)
+    return info
+
+
+def spread(v):
+    """Median, min and 90th percentile of a list of times (ms)."""
+    import numpy as np
+    return {"ms_median": round(float(np.median(v)), 4), "ms_min": round(float(min(v)), 4),
+            "ms_p90": round(float(np.percentile(v, 90)), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +318,8 @@ def main():
     ap.add_argument("--workload", default="h128_s16k_shard")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps timed after a 512 MiB write that evicts the caches")
     ap.add_argument("--counter-step", action="store_true",
                     help="run one warm-up and one step, then a plain 512 MiB device copy "
                          "(the scale reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -399,6 +432,23 @@ def main():
         for f in ("ms_per_launch", "ms_per_step"):
             k[f] = round(k[f], 4)
 
+    # cold caches: a 512 MiB write (twice the last-level cache) before each
+    # step, outside the timed events
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        cev = []
+        for i in range(args.cold_steps):
+            flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            cev.append((e0, e1))
+        torch.cuda.synchronize()
+        cold = spread([e0.elapsed_time(e1) for e0, e1 in cev])
+        del flush
+
     med = lambda v: float(np.median(v))  # noqa: E731
     value = (F_fwd + F_bwd) / (step_ms / 1e3) / 1e12
     res = {
@@ -414,12 +464,13 @@ def main():
                    "visible_pairs_per_head": pairs, "keys_needed": kn,
                    "flop_fwd": F_fwd, "flop_bwd": F_bwd},
         "frac_peak": round(value / PEAK_TFLOPS, 4),
-        "fwd": {"ms_median": round(med(fwd_ms), 4), "ms_min": round(min(fwd_ms), 4),
-                "tflops": round(F_fwd / (med(fwd_ms) / 1e3) / 1e12, 2),
+        "fwd": {**spread(fwd_ms), "tflops": round(F_fwd / (med(fwd_ms) / 1e3) / 1e12, 2),
                 "frac_peak": round(F_fwd / (med(fwd_ms) / 1e3) / 1e12 / PEAK_TFLOPS, 4)},
-        "bwd": {"ms_median": round(med(bwd_ms), 4), "ms_min": round(min(bwd_ms), 4),
-                "tflops": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12, 2),
+        "bwd": {**spread(bwd_ms), "tflops": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12, 2),
                 "frac_peak": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12 / PEAK_TFLOPS, 4)},
+        "step_events": spread([f + b for f, b in zip(fwd_ms, bwd_ms)]),
+        "step_cold_caches": cold,
+        "device": device_info(torch),
         "roofline": roofline,
         "kernels": kern,
         "cpu_baseline": None,

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MLAError", "MLADesc", "load_library", "library_path", "mla_laga_fwd", "mla_laga_bwd",
     "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
-    "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC",
+    "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC", "MLA_FLAG_RECOMPUTE_DQ",
     "MLA_MAX_RANGES", "MLADecodeDesc", "MLADecodeCall", "mla_laga_decode",
     "mla_laga_decode_workspace_size",
 ]
@@ -27,6 +27,7 @@ __all__ = [
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC = 1
+MLA_FLAG_RECOMPUTE_DQ = 2
 MLA_MAX_RANGES = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -152,10 +153,11 @@ def _host_ranges(q_ranges) -> Optional[np.ndarray]:
 
 def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: torch.Tensor,
               q_offset: int = 0, cu_seqlens=None, softmax_scale: Optional[float] = None,
-              generic: bool = False, q_ranges=None
+              generic: bool = False, q_ranges=None, recompute_dq: bool = False
               ) -> Tuple[MLADesc, Optional[np.ndarray], Optional[np.ndarray]]:
     """Descriptor plus the host arrays it points at (cu_seqlens, ranges):
-    keep those alive as long as the descriptor is used."""
+    keep those alive as long as the descriptor is used. recompute_dq sets
+    MLA_FLAG_RECOMPUTE_DQ (dQ without the stored-dS workspace)."""
     S_loc, n_h, d_qk = q.shape
     S, d_c = c_kv.shape
     d_rope = k_rope.shape[1]
@@ -166,7 +168,7 @@ def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: t
     d.n_seqs = 0 if cu is None else len(cu) - 1
     d.S, d.S_loc, d.q_offset = S, S_loc, int(q_offset)
     d.in_dtype = _in_dtype(q)
-    d.flags = MLA_FLAG_GENERIC if generic else 0
+    d.flags = (MLA_FLAG_GENERIC if generic else 0) | (MLA_FLAG_RECOMPUTE_DQ if recompute_dq else 0)
     d.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
     rng = _host_ranges(q_ranges)
     d.n_ranges = 0 if rng is None else len(rng)
@@ -249,9 +251,9 @@ class MLACall:
 
     def __init__(self, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
                  softmax_scale: Optional[float] = None, generic: bool = False,
-                 backward: bool = False, q_ranges=None):
+                 backward: bool = False, q_ranges=None, recompute_dq: bool = False):
         self.desc, self.cu, self.ranges = make_desc(q, c_kv, k_rope, W_UV, q_offset, cu_seqlens,
-                                                    softmax_scale, generic, q_ranges)
+                                                    softmax_scale, generic, q_ranges, recompute_dq)
         _check_inputs(self.desc, _input_specs(self.desc, q, c_kv, k_rope, W_UK, W_UV))
         self.device = q.device
         self.cu_dev = None if self.cu is None else torch.from_numpy(self.cu).to(self.device)
@@ -307,10 +309,11 @@ def mla_laga_fwd(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None
 
 def mla_laga_bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, q_offset: int = 0,
                  cu_seqlens=None, softmax_scale: Optional[float] = None, generic: bool = False,
-                 q_ranges=None):
-    """(dq, dc_kv, dk_rope, dW_UK, dW_UV), all fp32, gradients of sum(out*dout)."""
+                 q_ranges=None, recompute_dq: bool = False):
+    """(dq, dc_kv, dk_rope, dW_UK, dW_UV), all fp32, gradients of sum(out*dout).
+    recompute_dq: compute dQ without the stored-dS workspace."""
     call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic,
-                   backward=True, q_ranges=q_ranges)
+                   backward=True, q_ranges=q_ranges, recompute_dq=recompute_dq)
     d = call.desc
     _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))] +
                   _input_specs(d, q, c_kv, k_rope, W_UK, W_UV)[:1])

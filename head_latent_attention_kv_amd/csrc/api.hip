@@ -112,6 +112,7 @@ BwdLayout bwd_layout(const Plan& p) {
     return o;
   };
   L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = L.order = -1;
+  L.dS = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
     const int64_t S_pad = align_up(p.S_loc, 64);
@@ -131,6 +132,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
                             gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
     L.order = take(4 * ((p.S_loc + 255) / 256 + p.Kpad / 128));
+    if (p.ds_store) L.dS = take(p.n_h * p.Kpad * S_pad * 2);
     L.f.total = -1;
   } else {
     L.f = fwd_layout(p, false);
@@ -234,6 +236,8 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   }
   P.Kn = P.key_hi - P.key_lo;
   P.Kpad = align_up(P.Kn, kKeyTile);
+  P.ds_store = P.fast_bwd && !(d->flags & MLA_FLAG_RECOMPUTE_DQ) &&
+               P.n_h * P.Kpad * align_up(P.S_loc, 64) * 2 <= kMaxStoredDsBytes;
   int64_t pairs = 0;
   for (int64_t i = 0; i < P.S_loc; ++i) {
     const int64_t pos = rm_pos(P.rm, static_cast<int>(i));

@@ -128,7 +128,7 @@ constexpr int PF = 4;                          // fragment reads in flight ahead
 constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
 constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
 constexpr int P_PIECES = P_BYTES / 1024;       // 49
-constexpr int P_NPW = (P_PIECES + 7) / 8;      // 7 per wave
+constexpr int P_NPW = (P_PIECES + 3) / 4;      // 13 per A wave (only A waves issue the DMA)
 constexpr int P_XCH = 2 * P_BYTES;             // P slots: [pair][buffer] x 2 KiB
 static_assert(P_DON >= QB * XS_ROW && P_INFO - P_DON >= QB * PD_ROW && P_BYTES - P_INFO >= QB * 16,
               "paired dK/dV stage layout");
@@ -147,8 +147,9 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                      const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
                      const int* __restrict__ korder,
                      _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
-                     float* __restrict__ dKr, int n_h, int n_seqs, int S_loc, int S_pad,
-                     RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+                     float* __restrict__ dKr, _Float16* __restrict__ dS, int n_h, int n_seqs,
+                     int S_loc, int S_pad, RowMap rm, int key_lo, int Kpad, int n_kt, float scale,
+                     float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 4 * 2 * 2048];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -216,7 +217,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         if (I * 1024 < P_DON) ub = reinterpret_cast<const char*>(Qn_h + static_cast<int64_t>(qb) * DQK);
         else if (I * 1024 < P_INFO) ub = reinterpret_cast<const char*>(dOn_h + static_cast<int64_t>(qb) * DV);
         else ub = reinterpret_cast<const char*>(info_h + (qb / 32) * 128);
-        lds_dma16(ub + off, sbase + I * 1024);
+        lds_dma16(ub, off, sbase + I * 1024);
       }
     }
   };
@@ -251,13 +252,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     const int a_t0 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 0) : P_QN + xs_tr_base<XS_ROW>(lane, 0);
     const int a_t1 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 1) : P_QN + xs_tr_base<XS_ROW>(lane, 1);
 
-    if (nq > 0) issue(qb_begin, 0);
+    if (kA && nq > 0) issue(qb_begin, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int b = 0; b < nq; ++b) {
       const int st = b & 1;
       const int qb = qb_begin + b * QB;
-      if (b + 1 < nq) issue(qb + QB, st ^ 1);
+      if (kA && b + 1 < nq) issue(qb + QB, st ^ 1);
       const char* base = smem + st * P_BYTES;
   #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -334,8 +335,11 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             }
           }
         }
-        // P(t) visible to B; every wave, every sub-block
-        __syncthreads();
+        // P(t) visible to B; every wave, every sub-block. Only LDS is waited
+        // for: the DMA of the next block keeps running (a __syncthreads()
+        // would wait for it here).
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
         // ---- phase 2: A accumulates dV^T; B forms dS and accumulates dK^T
         if (!skip) {
           if constexpr (kA) {
@@ -367,6 +371,14 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                 dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
               }
             }
+            if (dS != nullptr) {
+              // dS^T block of (key tile, 32-row block): [128 keys][32 rows];
+              // this lane's key, rows 16 ks + 8 lh .. + 7 (dsf[ks])
+              _Float16* db = dS + ((((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (q0 >> 5)) * 128 +
+                                    32 * pi + lr) * 32 + 8 * lh);
+              *reinterpret_cast<half8*>(db) = dsf[0];
+              *reinterpret_cast<half8*>(db + 16) = dsf[1];
+            }
             // dK^T (dims x keys) += Q^T (dims x rows) . dS (rows x keys)
             auto frag = [&](int k) {
               const int ks = k / 6, dm = k % 6;
@@ -385,8 +397,12 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
           }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // A waves issued the DMA of the next block and wait for it; B waves
+      // wait for their LDS accesses only, so that their dS stores, still
+      // in flight, do not hold the barrier
+      if constexpr (kA) __builtin_amdgcn_s_waitcnt(0);
+      else __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
     }
 
     // write: lane = key t, registers = dims (four consecutive per group).
@@ -559,7 +575,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                                                                       : Vh + static_cast<int64_t>(kb) * DV);
         uint32_t off = static_cast<uint32_t>(doff[j]) * 2u;
         asm volatile("" : "+v"(off));
-        lds_dma16(ub + off, base + I * 1024);
+        lds_dma16(ub, off, base + I * 1024);
       }
     }
   };
@@ -656,6 +672,182 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 }
 
+// ------------------------------------------------------------------ dQ from the stored dS
+// dQ = scale dS K, reading the dS^T blocks that the dK/dV kernel wrote
+// ([key tile][32-row block][128 keys][32 rows], fp16) instead of recomputing
+// S and dP: 24 products per wave and 64 keys instead of 64. Eight waves of 32
+// rows (two per SIMD) as in the recomputing kernel. Per step of 64 keys the
+// K tile (swizzled rows, read transposed for K^T; double-buffered, mostly L2
+// hits) is shared, and each wave streams its own 64 x 32 dS^T block (64-byte
+// rows, read transposed: lane = row, eight consecutive keys, the B operand
+// of dQ^T += K^T dS^T) through a ring of three buffers, two steps ahead:
+// dS is the kernel's HBM stream. Pairs that no row sees were never written;
+// they are masked to 0 here.
+constexpr int E_KST = KS * K_ROW;                     // one K stage (28 KiB)
+constexpr int E_DS0 = 2 * E_KST, E_DST = 8 * KS * 64;  // dS stages: 8 waves x 4 KiB
+constexpr int E_BYTES = E_DS0 + 3 * E_DST;
+constexpr int E_KPIECES = E_KST / 1024;                // 28
+static_assert(E_KST % 1024 == 0 && E_BYTES <= 160 * 1024, "dq-from-dS LDS layout");
+
+// s_waitcnt vmcnt(n) (n = 0 or 4) with lgkmcnt(0): the gfx9 encoding
+// (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+__device__ __forceinline__ void wait_vm_lgkm(bool four) {
+  if (four) __builtin_amdgcn_s_waitcnt(0x0074);
+  else __builtin_amdgcn_s_waitcnt(0x0070);
+}
+
+__global__ void __launch_bounds__(512)
+attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
+                      const _Float16* __restrict__ dS, const int* __restrict__ qorder,
+                      float* __restrict__ dq, int n_h, int S_loc, int S_pad, int key_lo, int Kpad,
+                      int n_qt, float scale) {
+  __shared__ __attribute__((aligned(1024))) char smem[E_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lr = lane & 31, lh = lane >> 5;
+  int h, qt;
+  work_item(blockIdx.x, n_h, n_qt, &h, &qt);
+  qt = qorder != nullptr ? qorder[qt] : n_qt - 1 - qt;
+  const int q0 = qt * QW;
+  const int wq0 = q0 + 32 * w;
+  const int i = wq0 + lr;
+  const bool valid = i < S_loc;
+  const int n_rb = S_pad / 32;
+  const uint32_t* info_h = info + static_cast<int64_t>(h) * n_rb * 128;
+  const bool wave_live = wq0 < S_loc;
+  const uint32_t* blk = info_h + min(wq0 >> 5, n_rb - 1) * 128;
+  const int n_last = wave_live ? min(S_loc - 1 - wq0, 31) : 0;  // the wave's last valid row
+  const int lo = valid ? static_cast<int>(blk[64 + lr]) : 0;
+  const int p = valid ? static_cast<int>(blk[96 + lr]) : -1;
+  const int wp_min = wave_live ? static_cast<int>(blk[96]) : 0;
+  const int wp_max = wave_live ? static_cast<int>(blk[96 + n_last]) : -1;
+  const int wlo_min = wave_live ? static_cast<int>(blk[64]) : 0;
+  const int wlo_max = wave_live ? static_cast<int>(blk[64 + n_last]) : 0;
+
+  const int i_last = min(S_loc - 1, q0 + QW - 1);
+  const int kb_begin = ((static_cast<int>(info_h[(q0 >> 5) * 128 + 64]) - key_lo) / KS) * KS;
+  const int kb_end = static_cast<int>(info_h[(i_last >> 5) * 128 + 96 + (i_last & 31)]) + 1 - key_lo;
+  const int nblk = (kb_end - kb_begin + KS - 1) / KS;
+
+  const _Float16* Kh = Kfull + static_cast<int64_t>(h) * Kpad * DQK;
+  // this wave's dS^T rows (32-row block, clamped for rows past S_pad)
+  const _Float16* dSw = dS + (static_cast<int64_t>(h) * (Kpad / 128) * n_rb + min((q0 >> 5) + w, n_rb - 1)) * (128 * 32);
+  // K pieces of this wave: w, w + 8, w + 16, w + 24 (< 28); per-lane offsets
+  // (elements) of the swizzled rows, pad slots reloading slot 0
+  int kdoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int o = (w + 8 * j) * 1024 + lane * 16;
+    const int row = min(o / K_ROW, KS - 1), ph = (o % K_ROW) >> 4;
+    kdoff[j] = row * DQK + (ph < DQK / 8 ? xs_slot(row, ph) : 0) * 8;
+  }
+  auto issue_k = [&](int kb, int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int I = w + 8 * j;   // wave-uniform
+      if (I < E_KPIECES) {
+        uint32_t off = static_cast<uint32_t>(kdoff[j]) * 2u;
+        asm volatile("" : "+v"(off));
+        lds_dma16(Kh + static_cast<int64_t>(kb) * DQK, off, smem + st * E_KST + I * 1024);
+      }
+    }
+  };
+  // this wave's dS^T block of step kb: keys kb .. kb + 63 of key tile
+  // kb / 128, 64 bytes each, contiguous (4 pieces)
+  auto issue_ds = [&](int kb, int st) {
+    const char* src = reinterpret_cast<const char*>(dSw + (static_cast<int64_t>(kb >> 7) * n_rb * 128 + (kb & 127)) * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t off = static_cast<uint32_t>(c * 1024 + lane * 16);
+      asm volatile("" : "+v"(off));
+      lds_dma16(src, off, smem + E_DS0 + st * E_DST + w * 4096 + c * 1024);
+    }
+  };
+
+  f32x16 acc[6];
+#pragma unroll
+  for (int a = 0; a < 6; ++a)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
+  // K^T fragments: transposed reads of the K tile; dS^T fragments:
+  // transposed reads of this wave's block (64-byte rows)
+  const int a_kt0 = xs_tr_base(lane, 0), a_kt1 = xs_tr_base(lane, 1);
+  const int a_ds = E_DS0 + w * 4096 + tr_lane_offset(lane, 64);
+
+  // Before step b's products: K(b) and dS(b) landed in every wave. A wave's
+  // loads complete in issue order, so with dS(b + 1) issued after K(b), at
+  // most its 4 pieces may stay outstanding; the barrier then shows the
+  // other waves' pieces, and that every wave is done with the stages the
+  // next issues refill.
+  if (nblk > 0) {
+    issue_k(kb_begin, 0);
+    issue_ds(kb_begin, 0);
+    if (nblk > 1) issue_ds(kb_begin + KS, 1);
+    wait_vm_lgkm(nblk > 1);
+    asm volatile("s_barrier" ::: "memory");
+  }
+  int dst_ = 0;   // dS stage of step b
+  for (int b = 0; b < nblk; ++b) {
+    const int kb = kb_begin + b * KS;
+    if (b + 1 < nblk) issue_k(kb + KS, (b + 1) & 1);
+    if (b + 2 < nblk) issue_ds(kb + 2 * KS, dst_ == 0 ? 2 : dst_ - 1);
+    const int g0 = key_lo + kb;
+    const bool skip = !wave_live || g0 > wp_max || g0 + KS - 1 < wlo_min;
+    if (!skip) {
+      const bool need_mask = !(g0 >= wlo_max && g0 + KS - 1 <= wp_min);
+      const char* kbase = smem + (b & 1) * E_KST;
+      const char* dbase = smem + dst_ * E_DST;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        // dS^T fragment of k-step ksl: row lr, keys 32 mt + 16 ksl + 8 lh + j
+        half8 dsf[2];
+#pragma unroll
+        for (int ksl = 0; ksl < 2; ++ksl) {
+          dsf[ksl] = frag_tr<64>(dbase + a_ds + (32 * mt + 16 * ksl) * 64);
+          if (need_mask) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int key = g0 + 32 * mt + 16 * ksl + 8 * lh + j;
+              if (key < lo || key > p) dsf[ksl][j] = static_cast<_Float16>(0.f);
+            }
+          }
+        }
+        // K^T fragment: dims 32dm + lr, keys 32mt + 16ksl + 8lh + j (transposed read)
+        auto frag = [&](int k) {
+          const int ksl = k / 6, dm = k % 6;
+          const int o = (32 * mt + 16 * ksl) * K_ROW + 64 * dm;
+          return frag_tr2(kbase + a_kt0 + o, kbase + a_kt1 + o);
+        };
+        half8 fa[QPF + 1];
+#pragma unroll
+        for (int ii = 0; ii < QPF; ++ii) fa[ii] = frag(ii);
+#pragma unroll
+        for (int k = 0; k < 12; ++k) {
+          if (k + QPF < 12) fa[(k + QPF) % (QPF + 1)] = frag(k + QPF);
+          acc[k % 6] = mfma_f16(fa[k % (QPF + 1)], dsf[k / 6], acc[k % 6]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (b + 1 < nblk) {
+      wait_vm_lgkm(b + 2 < nblk);
+      asm volatile("s_barrier" ::: "memory");
+    }
+    dst_ = dst_ == 2 ? 0 : dst_ + 1;
+  }
+  if (valid) {
+    float* dst = dq + (static_cast<int64_t>(i) * n_h + h) * DQK;
+#pragma unroll
+    for (int dm = 0; dm < 6; ++dm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[dm][4 * g] * scale, acc[dm][4 * g + 1] * scale,
+                         acc[dm][4 * g + 2] * scale, acc[dm][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dst + 32 * dm + 8 * g + 4 * lh) = v;
+      }
+  }
+}
+
 // dk_rope[key_lo + t][r] = sum_h dKr[h][t][r] for t < Kn; other rows 0.
 __global__ void __launch_bounds__(256)
 reduce_rope_kernel(const float* __restrict__ dKr, float* __restrict__ dk_rope, int n_h,
@@ -709,6 +901,8 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   _Float16* dKVT = reinterpret_cast<_Float16*>(at(L.dV));
   float* dKr = reinterpret_cast<float*>(at(L.dKrope));
   uint32_t* info = reinterpret_cast<uint32_t*>(at(L.info));
+  // stored dS: the dK/dV kernel writes it, the dQ kernel reads it
+  _Float16* dS = p.ds_store ? reinterpret_cast<_Float16*>(at(L.dS)) : nullptr;
   const int S_loc = static_cast<int>(p.S_loc), Sp = static_cast<int>(S_pad),
             key_lo = static_cast<int>(p.key_lo),
             Kpad = static_cast<int>(p.Kpad);
@@ -752,17 +946,22 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     const int n_kt = static_cast<int>(p.Kpad / PW);
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
-                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, p.n_h, p.n_seqs, S_loc,
-                       Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, dS, p.n_h,
+                       p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
     KernelTimer kt("attn_bwd_dq", st);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
-                       0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       info, Kfull, Vkm, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt, p.scale,
-                       scale_log2);
+    if (dS != nullptr)
+      hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
+                         0, st, info, Kfull, dS, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
+                         p.scale);
+    else
+      hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
+                         0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
+                         info, Kfull, Vkm, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt, p.scale,
+                         scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0

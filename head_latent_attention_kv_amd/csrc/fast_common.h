@@ -112,10 +112,19 @@ __device__ __forceinline__ half8 frag_tr2(const char* p0, const char* p1) {
   return half8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
 }
 
-// One wave instruction of global_load_lds (16 bytes per lane): lane l's 16
-// bytes land at lds_dst + 16 l, so the wave fills 1 KiB of LDS contiguously.
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+// One wave instruction of global_load_lds (16 bytes per lane) in its
+// scalar-base form: lane l reads base + off_l (base wave-uniform, off_l a
+// 32-bit byte offset) and its 16 bytes land at lds_dst + 16 l, so the wave
+// fills 1 KiB of LDS contiguously (lds_dst wave-uniform, in M0). It is
+// issued through inline asm so that the compiler does not track it: the
+// compiler waits for every outstanding LDS DMA before a transposed LDS read
+// (ds_read_b64_tr_b16), which would serialise each next-tile prefetch with
+// the current tile's products. Callers therefore wait for the DMA
+// themselves (s_waitcnt vmcnt, then a barrier) before reading what it wrote.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, char* lds_dst) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds_dst)));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ float wave_max_pair(float x) {

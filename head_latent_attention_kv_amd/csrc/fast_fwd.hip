@@ -139,7 +139,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
         // bytes (the scalar-base form of the load)
         uint32_t off = static_cast<uint32_t>(dsrc[j]) * 2u;
         asm volatile("" : "+v"(off));
-        lds_dma16(reinterpret_cast<const char*>(I * 1024 < K_TILE_B ? kbase : vbase) + off, dst + I * 1024);
+        lds_dma16(I * 1024 < K_TILE_B ? kbase : vbase, off, dst + I * 1024);
       }
     }
   };

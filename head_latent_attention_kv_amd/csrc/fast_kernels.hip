@@ -123,7 +123,7 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
       // 64-bit address per piece is hoisted
       uint32_t off = static_cast<uint32_t>(doff[j]) * static_cast<uint32_t>(sizeof(InT));
       asm volatile("" : "+v"(off));
-      lds_dma16(s0 + off, dst + j * 1024);
+      lds_dma16(s0, off, dst + j * 1024);
     }
   };
 

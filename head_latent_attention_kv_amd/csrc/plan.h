@@ -26,6 +26,7 @@ struct Plan {
   bool bf16;
   bool fast;      // forward runs the MFMA path
   bool fast_bwd;  // backward runs the MFMA path
+  bool ds_store;  // fast backward: dK/dV stores dS, dQ reads it (no recompute)
   float scale;
   // latent rows the shard needs: [key_lo, key_hi), Kn of them
   int64_t key_lo, key_hi, Kn, Kpad;
@@ -57,8 +58,13 @@ struct BwdLayout {
   // fast path, packed calls: query-tile then key-tile order (int32
   // [ceil(S_loc / 256) + Kpad / 128])
   int64_t order;
+  // fast path with stored dS: fp16 [n_h][Kpad / 128][S_pad / 32][128 keys][32 rows]
+  int64_t dS;
   int64_t total;
 };
+
+// Largest stored-dS buffer the fast backward uses (bytes).
+constexpr int64_t kMaxStoredDsBytes = int64_t(32) << 30;
 
 // Decode (absorbed form over the latent cache): one query per sequence.
 struct DecodePlan {

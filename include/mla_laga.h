@@ -69,6 +69,13 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 /* Force the plain fp32 path even where the fast path applies. */
 #define MLA_FLAG_GENERIC 1
+/* Fast backward: compute dQ by recomputing the scores and dP per query tile
+ * instead of reading dS back from the workspace. The stored-dS form needs
+ * n_h * Kpad * S_pad * 2 bytes more workspace (Kpad = needed keys rounded up
+ * to 256, S_pad = S_loc rounded up to 64; 8.6 GB at n_h = 128, 16384 keys,
+ * 2048 rows) and is used unless this flag is set or that buffer would pass
+ * 32 GiB. Both give the same gradients up to fp16 rounding order. */
+#define MLA_FLAG_RECOMPUTE_DQ 2
 
 /* Most position blocks one shard may hold (mla_laga_desc.n_ranges). */
 #define MLA_MAX_RANGES 16

@@ -160,6 +160,24 @@ def test_workspace_linear_in_rows_and_heads():
     assert h2 - h1 == h3 - h2 and h2 > h1
 
 
+def test_stored_ds_workspace():
+    """The fast backward keeps dS (fp16, n_h x Kpad x S_pad) unless
+    MLA_FLAG_RECOMPUTE_DQ is set or that buffer would pass 32 GiB."""
+    base = workloads.config("h128_s16k_shard")
+    d, cu = desc_for(base)
+    with_ds = hla.mla_laga_bwd_workspace_size(d, cu)
+    d.flags = hla.MLA_FLAG_RECOMPUTE_DQ
+    without = hla.mla_laga_bwd_workspace_size(d, cu)
+    # Kpad = 16384 keys, S_pad = 2048 rows
+    assert with_ds - without == 128 * 16384 * 2048 * 2
+    # a shape whose dS would need more than 32 GiB falls back by itself
+    big = base.with_(S=131072, S_loc=8192, q_offset=131072 - 8192)
+    d, cu = desc_for(big)
+    auto = hla.mla_laga_bwd_workspace_size(d, cu)
+    d.flags = hla.MLA_FLAG_RECOMPUTE_DQ
+    assert hla.mla_laga_bwd_workspace_size(d, cu) == auto
+
+
 def bad(status, fn, *args):
     with pytest.raises(hla.MLAError) as e:
         fn(*args)

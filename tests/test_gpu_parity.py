@@ -74,13 +74,13 @@ SMALL = [
 ]
 
 
-def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None):
+def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None, recompute_dq=False):
     dev = to_device(x, cfg)
     if dout_override is not None:
         dev["dout"] = dout_override
     call = hla.MLACall(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
                        q_offset=cfg.q_offset, cu_seqlens=cu, generic=generic, backward=backward,
-                       q_ranges=cfg.q_ranges)
+                       q_ranges=cfg.q_ranges, recompute_dq=recompute_dq)
     out, lse = call.fwd(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
     res = {"out": out, "lse": lse, "fast": call.fast}
     if backward:
@@ -95,12 +95,14 @@ def oracle_args(x):
     return [x[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
 
 
-@pytest.mark.parametrize("generic", [False, True], ids=["default", "plain"])
+# default: the fast path with dQ read from the stored dS; recompute_dq: the
+# fast path with dQ recomputing S and dP; plain: the fp32 path
+@pytest.mark.parametrize("path", ["default", "recompute_dq", "plain"])
 @pytest.mark.parametrize("cfg,cu", SMALL, ids=[c.name for c, _ in SMALL])
-def test_small_fwd_bwd_elementwise(cfg, cu, generic):
-    announce(f"small {cfg.name} generic={generic} n_h={cfg.n_h} S={cfg.S} S_loc={cfg.S_loc} q_off={cfg.q_offset}")
+def test_small_fwd_bwd_elementwise(cfg, cu, path):
+    announce(f"small {cfg.name} path={path} n_h={cfg.n_h} S={cfg.S} S_loc={cfg.S_loc} q_off={cfg.q_offset}")
     x = workloads.make_inputs(cfg, with_dout=True)
-    g = run(cfg, x, cu, generic=generic, backward=True)
+    g = run(cfg, x, cu, generic=path == "plain", backward=True, recompute_dq=path == "recompute_dq")
     ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, **positions(cfg))
     check("out", g["out"], ro)
     check("lse", g["lse"], rl)
@@ -150,6 +152,7 @@ def test_h128_s16k_shard_forward_sampled_heads(heads):
 
 @pytest.mark.parametrize("name", ["h128_s8k_bwd", "h128_varlen64k", "h128_s16k_zigzag_r0"])
 def test_full_size_backward_sampled_heads(name):
+    """Default fast path (dQ from the stored dS)."""
     cfg = workloads.config(name)
     cu = cfg.cu_seqlens()
     heads = [5, 122]
@@ -248,6 +251,22 @@ def test_zigzag_concatenation_identity(generic):
     rg = oracle.mla_backward(x["dout"], *oracle_args(x))
     for k, ref in zip(GRADS[1:], rg[1:]):
         check(k, sums[k], ref)
+
+
+@pytest.mark.parametrize("name", ["h128_s16k_shard", "h128_varlen64k"])
+def test_full_size_dq_paths_agree(name):
+    """dQ read from the stored dS and dQ recomputed per query tile, both on
+    the full-size shard, checked against the oracle on sampled heads."""
+    cfg = workloads.config(name)
+    cu = cfg.cu_seqlens()
+    heads = [3, 90]
+    x = workloads.make_inputs(cfg, with_dout=True)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, heads=heads,
+                             **positions(cfg))
+    for recompute in (False, True):
+        announce(f"{name} dq, recompute_dq={recompute}, heads {heads}")
+        g = run(cfg, x, cu, backward=True, recompute_dq=recompute)
+        check("dq", g["dq"][:, heads], rg[0][:, heads])
 
 
 def test_forward_backward_deterministic():
