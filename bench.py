@@ -45,8 +45,8 @@ def kernel_flops(name, cfg, pairs, kn):
     (640 per visible pair and head forward, 1664 backward, plus the
     up-projection of the needed keys) over the kernels, each product once:
     the backward's S = Q K^T and dP = dO V^T go to the dK/dV kernel; the dQ
-    kernel recomputes them, and the backward's K/V rebuild launches
-    recompute the up-projection."""
+    kernel either reads the dS the dK/dV kernel stored or recomputes them,
+    and the backward's K/V rebuild launches recompute the up-projection."""
     d_qk = cfg.d_nope + cfg.d_rope
     up = 2 * cfg.n_h * cfg.d_c * (cfg.d_nope + cfg.d_v) * kn
     per_pair = lambda d: 2 * cfg.n_h * d * pairs  # noqa: E731
@@ -59,6 +59,8 @@ def kernel_flops(name, cfg, pairs, kn):
         "attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
         # dQ: dQ = dS K (S and dP recomputed)
         "attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
+        # dQ = dS K from the dS the dK/dV kernel stored
+        "attn_bwd_dq_ds": (per_pair(d_qk),) * 2,
         "plain_attn_bwd_dkdv": (per_pair(2 * d_qk + 2 * cfg.d_v),) * 2,
         "plain_attn_bwd_dq": (per_pair(d_qk), per_pair(2 * d_qk + cfg.d_v)),
         # dc_kv = [dK_nope | dV] W^T and dW = c_kv^T [dK_nope | dV]: one up-projection each
@@ -76,6 +78,7 @@ COUNTED_KERNELS = {
     "attn_fwd_kernel": ("attn_fwd", ["fast_fwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dkdv_kernel": ("attn_bwd_dkdv", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
     "attn_bwd_dq_kernel": ("attn_bwd_dq", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
+    "attn_bwd_dq_ds_kernel": ("attn_bwd_dq_ds", ["fast_bwd.hip", "fast_common.h", "device_common.h"]),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 512 * 2**20

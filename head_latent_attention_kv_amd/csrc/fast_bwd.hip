@@ -371,14 +371,6 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                 dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
               }
             }
-            if (dS != nullptr) {
-              // dS^T block of (key tile, 32-row block): [128 keys][32 rows];
-              // this lane's key, rows 16 ks + 8 lh .. + 7 (dsf[ks])
-              _Float16* db = dS + ((((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (q0 >> 5)) * 128 +
-                                    32 * pi + lr) * 32 + 8 * lh);
-              *reinterpret_cast<half8*>(db) = dsf[0];
-              *reinterpret_cast<half8*>(db + 16) = dsf[1];
-            }
             // dK^T (dims x keys) += Q^T (dims x rows) . dS (rows x keys)
             auto frag = [&](int k) {
               const int ks = k / 6, dm = k % 6;
@@ -393,6 +385,16 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               if (k + PF < 12) fa[(k + PF) % (PF + 1)] = frag(k + PF);
               acc[k % 6] = mfma_f16(fa[k % (PF + 1)], dsf[k / 6], acc[k % 6]);
               __builtin_amdgcn_sched_barrier(0);
+            }
+            // after the products, so that the stores do not delay them
+            if (dS != nullptr) {
+              // dS block of (key tile, 32-row block), 8 KiB: [pair][ks][lane]
+              // x 16 bytes, lane = 32 lh + lr holding key 32 pair + lr, rows
+              // 16 ks + 8 lh .. + 7 (dsf[ks]): each store is 1 KiB contiguous
+              _Float16* db = dS + (((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (q0 >> 5)) * 4096 +
+                                   pi * 1024 + lane * 8);
+              *reinterpret_cast<half8*>(db) = dsf[0];
+              *reinterpret_cast<half8*>(db + 512) = dsf[1];
             }
           }
         }
@@ -673,14 +675,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ dQ from the stored dS
-// dQ = scale dS K, reading the dS^T blocks that the dK/dV kernel wrote
-// ([key tile][32-row block][128 keys][32 rows], fp16) instead of recomputing
+// dQ = scale dS K, reading the dS blocks that the dK/dV kernel wrote (per
+// key tile and 32-row block, 4 pairs of 32 keys x [row half ks][lane] x 16
+// bytes: lane 32 lh + lr holds key lr, rows 16 ks + 8 lh .. + 7) instead of recomputing
 // S and dP: 24 products per wave and 64 keys instead of 64. Eight waves of 32
 // rows (two per SIMD) as in the recomputing kernel. Per step of 64 keys the
 // K tile (swizzled rows, read transposed for K^T; double-buffered, mostly L2
-// hits) is shared, and each wave streams its own 64 x 32 dS^T block (64-byte
-// rows, read transposed: lane = row, eight consecutive keys, the B operand
-// of dQ^T += K^T dS^T) through a ring of three buffers, two steps ahead:
+// hits) is shared, and each wave streams its own 64-key x 32-row dS block
+// (two pairs, read transposed: lane = row, eight consecutive keys, the B
+// operand of dQ^T += K^T dS^T) through a ring of three buffers, two steps ahead:
 // dS is the kernel's HBM stream. Pairs that no row sees were never written;
 // they are masked to 0 here.
 constexpr int E_KST = KS * K_ROW;                     // one K stage (28 KiB)
@@ -752,8 +755,8 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
       }
     }
   };
-  // this wave's dS^T block of step kb: keys kb .. kb + 63 of key tile
-  // kb / 128, 64 bytes each, contiguous (4 pieces)
+  // this wave's dS of step kb: pairs (kb % 128) / 32 and the next of key
+  // tile kb / 128, 2 KiB each, contiguous (4 pieces)
   auto issue_ds = [&](int kb, int st) {
     const char* src = reinterpret_cast<const char*>(dSw + (static_cast<int64_t>(kb >> 7) * n_rb * 128 + (kb & 127)) * 32);
 #pragma unroll
@@ -769,10 +772,15 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
   for (int a = 0; a < 6; ++a)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
-  // K^T fragments: transposed reads of the K tile; dS^T fragments:
-  // transposed reads of this wave's block (64-byte rows)
+  // K^T fragments: transposed reads of the K tile. dS fragments: transposed
+  // reads of this wave's block. In a transposed read, lane q of 16-lane group
+  // g fetches keys (k) 8 (g / 2) + q / 4 and rows 16 (g % 2) + 4 (q % 4) .. + 3
+  // of a 16-key step; in the stored layout those four rows are 8 contiguous
+  // bytes at row half g % 2, lane half (q / 2) % 2, key, and 8 (q % 2); four
+  // keys further is 64 bytes on.
   const int a_kt0 = xs_tr_base(lane, 0), a_kt1 = xs_tr_base(lane, 1);
-  const int a_ds = E_DS0 + w * 4096 + tr_lane_offset(lane, 64);
+  const int a_ds = E_DS0 + w * 4096 + ((lane >> 4) & 1) * 1024 + (((lane & 15) >> 1) & 1) * 512 +
+                   (8 * (lane >> 5) + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
 
   // Before step b's products: K(b) and dS(b) landed in every wave. A wave's
   // loads complete in issue order, so with dS(b + 1) issued after K(b), at
@@ -799,11 +807,12 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
       const char* dbase = smem + dst_ * E_DST;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        // dS^T fragment of k-step ksl: row lr, keys 32 mt + 16 ksl + 8 lh + j
+        // dS fragment of k-step ksl: row lr, keys 32 mt + 16 ksl + 8 lh + j
+        // (pair mt of the step, keys 16 ksl .. of the pair)
         half8 dsf[2];
 #pragma unroll
         for (int ksl = 0; ksl < 2; ++ksl) {
-          dsf[ksl] = frag_tr<64>(dbase + a_ds + (32 * mt + 16 * ksl) * 64);
+          dsf[ksl] = frag_tr<16>(dbase + a_ds + mt * 2048 + ksl * 256);
           if (need_mask) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -952,7 +961,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
-    KernelTimer kt("attn_bwd_dq", st);
+    KernelTimer kt(dS != nullptr ? "attn_bwd_dq_ds" : "attn_bwd_dq", st);
     if (dS != nullptr)
       hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                          0, st, info, Kfull, dS, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,

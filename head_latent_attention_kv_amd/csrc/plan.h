@@ -58,7 +58,8 @@ struct BwdLayout {
   // fast path, packed calls: query-tile then key-tile order (int32
   // [ceil(S_loc / 256) + Kpad / 128])
   int64_t order;
-  // fast path with stored dS: fp16 [n_h][Kpad / 128][S_pad / 32][128 keys][32 rows]
+  // fast path with stored dS: fp16 [n_h][Kpad / 128][S_pad / 32] blocks of 8 KiB
+  // ([4 pairs of 32 keys][2 row halves][64 lanes] x 16 bytes, written by dK/dV)
   int64_t dS;
   int64_t total;
 };
