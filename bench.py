@@ -127,6 +127,8 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
     fscale = COPY_BYTES / (sum(fcopy) / len(fcopy))
     wscale = COPY_BYTES / (sum(wcopy) / len(wcopy))
     table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    # drop records taken on sources that have changed since
+    table = {k: v for k, v in table.items() if v.get("sha") == sources_sha(v.get("sources", []))}
     for frag, (timer, sources) in COUNTED_KERNELS.items():
         fk = [v for k, v in fetch.items() if frag in k]
         wk = [v for k, v in write.items() if frag in k]
