@@ -3,6 +3,7 @@ one query shard (synthetic seeded inputs, resident in HBM before timing).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --sp-sweep 8 [--steps K]   (per-rank times of an 8-way split)
+    python bench.py --memory [--workload NAME]   (activation and workspace bytes)
     python bench.py --decode decode_h128_b64_l8k   (absorbed decode over the latent cache)
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: visible
@@ -174,6 +175,87 @@ def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
                       f"(all {cfg.S_loc} rows), {dt:.1f} s"}
 
 
+def memory_report(name):
+    """Device bytes of one attention block on a query shard (prints one JSON
+    line). The LAGA figures are the caching allocator's peaks around this
+    library's calls, above the resident inputs: forward (workspace and
+    outputs), backward with the stored dS and with dQ recomputed (workspace
+    and gradients), and what stays allocated from forward to backward (out,
+    lse: the K/V rebuilt from the latent are not kept). For comparison, the
+    tensors that the other two forms of the block keep for their backward are
+    allocated (not computed) and measured the same way, in bf16:
+      explicit: per-head K = [K_nope | k_rope] and V for the keys the shard
+                attends to, and, as the smaller reading, for its own rows only;
+      absorbed: per query row and head the latent-space query (W_UK_h q_nope
+                with q_rope, 576 wide) and output (512 wide)."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_kv_amd as hla
+    import workloads
+
+    cfg = workloads.config(name)
+    x = workloads.make_inputs(cfg, with_dout=True)
+    dev = {k: torch.from_numpy(x[k + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+           for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV", "dout")}
+    a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    cu = cfg.cu_seqlens()
+    torch.cuda.synchronize()
+    inputs = torch.cuda.memory_allocated()
+
+    def peak_of(fn):
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        res = fn()
+        torch.cuda.synchronize()
+        return res, torch.cuda.max_memory_allocated() - before
+
+    def fwd_call():
+        call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, q_ranges=cfg.q_ranges)
+        out, lse = call.fwd(*a)
+        return call, out, lse
+
+    (call, out, lse), fwd_peak = peak_of(fwd_call)
+    del call
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - inputs
+    res = {"metric": "attention-block device bytes per query shard", "workload": cfg.name,
+           "config": {"n_h": cfg.n_h, "S": cfg.S, "S_loc": cfg.S_loc, "q_offset": cfg.q_offset},
+           "laga": {"forward_peak": fwd_peak, "held_forward_to_backward": held}}
+    for recompute in (False, True):
+        def bwd_call():
+            c = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, q_ranges=cfg.q_ranges,
+                            backward=True, recompute_dq=recompute)
+            g = c.bwd(dev["dout"], *a, out, lse)
+            return c, g
+        (c, g), peak = peak_of(bwd_call)
+        key = "backward_peak_recompute_dq" if recompute else "backward_peak_stored_ds"
+        res["laga"][key] = peak
+        res["laga"][key.replace("peak", "workspace")] = c.ws_bwd.numel()
+        del c, g
+    pairs, k_lo, k_hi = hla.mla_laga_count(hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu,
+                                                        q_ranges=cfg.q_ranges).desc, cu)
+    kn = k_hi - k_lo
+    d_qk = cfg.d_nope + cfg.d_rope
+
+    def held_bytes(shapes):
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        ts = [torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in shapes]
+        torch.cuda.synchronize()
+        b = torch.cuda.memory_allocated() - before
+        del ts
+        return b
+
+    res["explicit_saved_kv_all_keys"] = held_bytes([(kn, cfg.n_h, d_qk), (kn, cfg.n_h, cfg.d_v)])
+    res["explicit_saved_kv_own_rows"] = held_bytes([(cfg.S_loc, cfg.n_h, d_qk), (cfg.S_loc, cfg.n_h, cfg.d_v)])
+    res["absorbed_saved_latent_q_and_out"] = held_bytes([(cfg.S_loc, cfg.n_h, cfg.d_c + cfg.d_rope),
+                                                         (cfg.S_loc, cfg.n_h, cfg.d_c)])
+    res["keys_needed"] = kn
+    print(json.dumps(res), flush=True)
+
+
 def sp_sweep(base_name, world, steps, warmup):
     """Time every rank's forward+backward of a `world`-way sequence-parallel
     split of the workload's sequence, contiguous and zigzag, one rank after
@@ -333,6 +415,8 @@ def main():
     ap.add_argument("--decode", metavar="NAME",
                     help="time the absorbed decode path on a decode batch "
                          "(decode_h128_b64_l8k, decode_h128_b32_mixed); prints its own JSON line")
+    ap.add_argument("--memory", action="store_true",
+                    help="device bytes of the block on the workload (prints its own JSON line)")
     ap.add_argument("--sp-sweep", type=int, metavar="WORLD",
                     help="time each rank of a WORLD-way contiguous and zigzag split of the "
                          "workload's sequence, one after another (prints its own JSON line)")
@@ -348,6 +432,9 @@ def main():
 
     if args.decode:
         decode_bench(args.decode, args.steps, args.warmup)
+        return
+    if args.memory:
+        memory_report(args.workload)
         return
     if args.sp_sweep:
         sp_sweep(args.workload, args.sp_sweep, args.steps, args.warmup)
