@@ -128,7 +128,7 @@ constexpr int PF = 4;                          // fragment reads in flight ahead
 constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
 constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
 constexpr int P_PIECES = P_BYTES / 1024;       // 49
-constexpr int P_NPW = (P_PIECES + 3) / 4;      // 13 per A wave (only A waves issue the DMA)
+constexpr int P_NPW = (P_PIECES + 3) / 4;      // 13 per B wave (only B waves issue the DMA)
 constexpr int P_XCH = 2 * P_BYTES;             // P slots: [pair][buffer] x 2 KiB
 static_assert(P_DON >= QB * XS_ROW && P_INFO - P_DON >= QB * PD_ROW && P_BYTES - P_INFO >= QB * 16,
               "paired dK/dV stage layout");
@@ -150,7 +150,8 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                      float* __restrict__ dKr, _Float16* __restrict__ dS, int n_h, int n_seqs,
                      int S_loc, int S_pad, RowMap rm, int key_lo, int Kpad, int n_kt, float scale,
                      float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 4 * 2 * 2048];
+  // stages, then P slots [pair][buffer], then dS slots [pair][buffer]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 2 * 4 * 2 * 2048];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
@@ -165,6 +166,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
   const int gk_min = key_lo + t0, gk_max = key_lo + t0 + PW - 1;
   const int gw_min = key_lo + tw, gw_max = gw_min + 31;
   char* const xslot = smem + P_XCH + pi * 4096;   // this pair's two P slots
+  char* const dslot = smem + P_XCH + 4 * 4096 + pi * 4096;   // and its two dS slots
 
   // query rows that see any key of the workgroup: from the first row at or
   // past its first key to the last row whose sample starts by its last key
@@ -190,7 +192,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
   int doff[P_NPW];
 #pragma unroll
   for (int j = 0; j < P_NPW; ++j) {
-    const int o = (w * P_NPW + j) * 1024 + lane * 16;
+    const int o = ((w & 3) * P_NPW + j) * 1024 + lane * 16;
     int off = 0;
     if (o < P_DON) {
       const int row = min(o / XS_ROW, QB - 1), ph = (o % XS_ROW) >> 4;
@@ -207,7 +209,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     char* sbase = smem + st * P_BYTES;
 #pragma unroll
     for (int j = 0; j < P_NPW; ++j) {
-      const int I = w * P_NPW + j;   // wave-uniform region choice
+      const int I = (w & 3) * P_NPW + j;   // wave-uniform region choice
       if (I < P_PIECES) {
         // wave-uniform base plus an opaque unsigned 32-bit lane offset in
         // bytes (the scalar-base form of the load)
@@ -252,13 +254,28 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     const int a_t0 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 0) : P_QN + xs_tr_base<XS_ROW>(lane, 0);
     const int a_t1 = kA ? P_DON + xs_tr_base<PD_ROW>(lane, 1) : P_QN + xs_tr_base<XS_ROW>(lane, 1);
 
-    if (kA && nq > 0) issue(qb_begin, 0);
+    if (!kA && nq > 0) issue(qb_begin, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // A: the 32-row block whose dS waits in the slot (-1: none). The dS
+    // block of (key tile, 32-row block) is 8 KiB: [pair][ks][lane] x 16
+    // bytes, lane = 32 lh + lr holding key 32 pair + lr and rows 16 ks +
+    // 8 lh .. + 7, so each store writes 1 KiB contiguously.
+    int ds_q0 = -1;
+    auto store_ds = [&](int par) {
+      if (ds_q0 >= 0) {
+        const half8 v0 = *reinterpret_cast<const half8*>(dslot + par * 2048 + lane * 16);
+        const half8 v1 = *reinterpret_cast<const half8*>(dslot + par * 2048 + 1024 + lane * 16);
+        _Float16* db = dS + (((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (ds_q0 >> 5)) * 4096 +
+                             pi * 1024 + lane * 8);
+        *reinterpret_cast<half8*>(db) = v0;
+        *reinterpret_cast<half8*>(db + 512) = v1;
+      }
+    };
     for (int b = 0; b < nq; ++b) {
       const int st = b & 1;
       const int qb = qb_begin + b * QB;
-      if (kA && b + 1 < nq) issue(qb + QB, st ^ 1);
+      if (!kA && b + 1 < nq) issue(qb + QB, st ^ 1);
       const char* base = smem + st * P_BYTES;
   #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -386,26 +403,29 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               acc[k % 6] = mfma_f16(fa[k % (PF + 1)], dsf[k / 6], acc[k % 6]);
               __builtin_amdgcn_sched_barrier(0);
             }
-            // after the products, so that the stores do not delay them
+            // dS to the pair's slot for this sub-block parity; wave A stores
+            // it in the next phase 2, where it has slack
             if (dS != nullptr) {
-              // dS block of (key tile, 32-row block), 8 KiB: [pair][ks][lane]
-              // x 16 bytes, lane = 32 lh + lr holding key 32 pair + lr, rows
-              // 16 ks + 8 lh .. + 7 (dsf[ks]): each store is 1 KiB contiguous
-              _Float16* db = dS + (((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (q0 >> 5)) * 4096 +
-                                   pi * 1024 + lane * 8);
-              *reinterpret_cast<half8*>(db) = dsf[0];
-              *reinterpret_cast<half8*>(db + 512) = dsf[1];
+              *reinterpret_cast<half8*>(dslot + mt * 2048 + lane * 16) = dsf[0];
+              *reinterpret_cast<half8*>(dslot + mt * 2048 + 1024 + lane * 16) = dsf[1];
             }
           }
         }
+        if constexpr (kA) {
+          // the previous sub-block's dS (slot 1 - mt, written by B before
+          // this sub-block's barrier) to HBM, then remember this one
+          store_ds(1 - mt);
+          ds_q0 = skip || dS == nullptr ? -1 : q0;
+        }
       }
-      // A waves issued the DMA of the next block and wait for it; B waves
+      // B waves issued the DMA of the next block and wait for it; A waves
       // wait for their LDS accesses only, so that their dS stores, still
       // in flight, do not hold the barrier
-      if constexpr (kA) __builtin_amdgcn_s_waitcnt(0);
+      if constexpr (!kA) __builtin_amdgcn_s_waitcnt(0);
       else __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
     }
+    if constexpr (kA) store_ds(1);   // the last sub-block (odd parity)
 
     // write: lane = key t, registers = dims (four consecutive per group).
     // Every output leaves through LDS in whole rows: first dKV^T (one dim,
