@@ -268,8 +268,9 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         const half8 v1 = *reinterpret_cast<const half8*>(dslot + par * 2048 + 1024 + lane * 16);
         _Float16* db = dS + (((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (ds_q0 >> 5)) * 4096 +
                              pi * 1024 + lane * 8);
-        *reinterpret_cast<half8*>(db) = v0;
-        *reinterpret_cast<half8*>(db + 512) = v1;
+        // non-temporal: the dS stream then leaves the q/dO tiles in L2
+        __builtin_nontemporal_store(v0, reinterpret_cast<half8*>(db));
+        __builtin_nontemporal_store(v1, reinterpret_cast<half8*>(db + 512));
       }
     };
     for (int b = 0; b < nq; ++b) {
