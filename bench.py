@@ -147,6 +147,75 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
     return table
 
 
+# Counters of one --counter-step run, collected in two rocprofv3 --pmc passes
+# (each pass within the per-block limits of one run).
+UTIL_PASS_A = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+               "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+               "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32",
+               "GRBM_GUI_ACTIVE")
+UTIL_PASS_B = ("SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS",
+               "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY",
+               "GRBM_GUI_ACTIVE")
+
+
+def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
+    """Markdown table of per-kernel unit utilisation from the two passes.
+
+    Per kernel (summed over its dispatches): the shader clock, GRBM_GUI_ACTIVE
+    per XCD over the dispatch time; MFMA busy, SQ_VALU_MFMA_BUSY_CYCLES over
+    (active cycles x SIMDs), the counter tool's own MfmaUtil formula; the MFMA
+    rate the executed MOPS give (512 FLOP each) and its fraction of the
+    dense peak at the measured clock; LDS busy, SQ_LDS_IDX_ACTIVE over (active
+    cycles x CUs); bank-conflict cycles as a share of LDS-active cycles; and
+    the shares of wave time spent issuing VALU and LDS instructions and
+    waiting."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def load(path):
+        cnt = defaultdict(lambda: defaultdict(float))
+        dur = defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            m = re.search(r"::(\w+)(<[^(]*>)?\(", name)
+            z = re.search(r"_GLOBAL__N_1(\d+)(\w+)", name)
+            if m:
+                k = m.group(1) + (m.group(2) or "")
+            elif z:   # a mangled name: the length-prefixed identifier, then its template args
+                ln, rest = int(z.group(1)), z.group(2)
+                k = rest[:ln] + (f"<{rest[ln + 1:rest.find('E', ln)]}>" if rest[ln:ln + 1] == "I" else "")
+            else:
+                k = name.split("(")[0]
+            cnt[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            dur[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        return cnt, {k: (sum(v.values()), len(v)) for k, v in dur.items()}
+
+    A, tA = load(csv_a)
+    B, _ = load(csv_b)
+    rows = ["| kernel | launches | ms per launch | clock GHz | MFMA busy | MFMA TFLOP/s executed "
+            "| of dense peak at that clock | LDS busy | bank-conflict share | VALU issue / wave time "
+            "| LDS issue / wave time | waiting / wave time |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(A, key=lambda k: -tA[k][0]):
+        a, b = A[k], B.get(k, {})
+        t, n = tA[k]
+        if a["SQ_INSTS_VALU_MFMA_MOPS_F16"] + a["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0 and t / n < 1e-4:
+            continue
+        g = a["GRBM_GUI_ACTIVE"] / n_xcd
+        clk = g / t / 1e9
+        tf = (a["SQ_INSTS_VALU_MFMA_MOPS_F16"] + a["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512 / t / 1e12
+        wc = max(b.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        pct = lambda x: f"{100 * x:.1f}%"  # noqa: E731
+        rows.append(
+            f"| {k} | {n} | {t / n * 1e3:.3f} | {clk:.2f} | {pct(a['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * n_simd))} "
+            f"| {tf:.1f} | {pct(tf / (PEAK_TFLOPS * clk / 2.4))} | {pct(a['SQ_LDS_IDX_ACTIVE'] / (g * n_cu))} "
+            f"| {pct(a['SQ_LDS_BANK_CONFLICT'] / max(a['SQ_LDS_IDX_ACTIVE'], 1.0))} "
+            f"| {pct(a['SQ_ACTIVE_INST_VALU'] / wc)} | {pct(b.get('SQ_ACTIVE_INST_LDS', 0.0) / wc)} "
+            f"| {pct(b.get('SQ_WAIT_INST_ANY', 0.0) / wc)} |")
+    return "\n".join(rows)
+
+
 def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
     """The fp64 oracle, as it stands, on whole heads of the workload (all rows,
     forward and backward) until about `budget_s` seconds have been spent."""
@@ -410,6 +479,9 @@ def main():
     ap.add_argument("--counter-step", action="store_true",
                     help="run one warm-up and one step, then a plain 512 MiB device copy "
                          "(the scale reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--utilisation-from", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="print per-kernel MFMA/LDS/VALU utilisation from two --counter-step "
+                         "rocprofv3 --pmc runs (counters: UTIL_PASS_A, then UTIL_PASS_B)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two --counter-step counter csv files")
     ap.add_argument("--decode", metavar="NAME",
@@ -421,6 +493,9 @@ def main():
                     help="time each rank of a WORLD-way contiguous and zigzag split of the "
                          "workload's sequence, one after another (prints its own JSON line)")
     args = ap.parse_args()
+    if args.utilisation_from:
+        print(utilisation_from_counters(*args.utilisation_from))
+        return
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from, args.workload), indent=1))
         return

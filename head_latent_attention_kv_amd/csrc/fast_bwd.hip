@@ -777,12 +777,15 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
     }
   };
   // this wave's dS of step kb: pairs (kb % 128) / 32 and the next of key
-  // tile kb / 128, 2 KiB each, contiguous (4 pieces)
+  // tile kb / 128, 2 KiB each, contiguous (4 pieces). Piece c is row half
+  // c % 2 of pair c / 2; LDS chunk (lane half lh, key lr) of it holds the
+  // stored chunk of key lr ^ 4 (2 (c % 2) + lh), which spreads the rows one
+  // transposed read fetches over all 64 banks.
   auto issue_ds = [&](int kb, int st) {
     const char* src = reinterpret_cast<const char*>(dSw + (static_cast<int64_t>(kb >> 7) * n_rb * 128 + (kb & 127)) * 32);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint32_t off = static_cast<uint32_t>(c * 1024 + lane * 16);
+      uint32_t off = static_cast<uint32_t>(c * 1024 + (lane ^ (4 * (2 * (c & 1) + (lane >> 5)))) * 16);
       asm volatile("" : "+v"(off));
       lds_dma16(src, off, smem + E_DS0 + st * E_DST + w * 4096 + c * 1024);
     }
@@ -795,13 +798,15 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
     for (int e = 0; e < 16; ++e) acc[a][e] = 0.f;
   // K^T fragments: transposed reads of the K tile. dS fragments: transposed
   // reads of this wave's block. In a transposed read, lane q of 16-lane group
-  // g fetches keys (k) 8 (g / 2) + q / 4 and rows 16 (g % 2) + 4 (q % 4) .. + 3
-  // of a 16-key step; in the stored layout those four rows are 8 contiguous
-  // bytes at row half g % 2, lane half (q / 2) % 2, key, and 8 (q % 2); four
-  // keys further is 64 bytes on.
+  // g fetches keys (k) 8 (g / 2) + q / 4 (the second read: 4 keys further)
+  // and rows 16 (g % 2) + 4 (q % 4) .. + 3 of a 16-key step; those four rows
+  // are 8 contiguous bytes at row half g % 2, lane half (q / 2) % 2, the
+  // swizzled key slot, and 8 (q % 2).
   const int a_kt0 = xs_tr_base(lane, 0), a_kt1 = xs_tr_base(lane, 1);
-  const int a_ds = E_DS0 + w * 4096 + ((lane >> 4) & 1) * 1024 + (((lane & 15) >> 1) & 1) * 512 +
-                   (8 * (lane >> 5) + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
+  const int ds_hb = (lane >> 4) & 1, ds_lb = ((lane & 15) >> 1) & 1;
+  const int ds_key = 8 * (lane >> 5) + ((lane & 15) >> 2), ds_x = 4 * (2 * ds_hb + ds_lb);
+  const int a_ds0 = E_DS0 + w * 4096 + ds_hb * 1024 + ds_lb * 512 + ((ds_key ^ ds_x) * 16) + (lane & 1) * 8;
+  const int a_ds1 = E_DS0 + w * 4096 + ds_hb * 1024 + ds_lb * 512 + (((ds_key + 4) ^ ds_x) * 16) + (lane & 1) * 8;
 
   // Before step b's products: K(b) and dS(b) landed in every wave. A wave's
   // loads complete in issue order, so with dS(b + 1) issued after K(b), at
@@ -833,7 +838,7 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
         half8 dsf[2];
 #pragma unroll
         for (int ksl = 0; ksl < 2; ++ksl) {
-          dsf[ksl] = frag_tr<16>(dbase + a_ds + mt * 2048 + ksl * 256);
+          dsf[ksl] = frag_tr2(dbase + a_ds0 + mt * 2048 + ksl * 256, dbase + a_ds1 + mt * 2048 + ksl * 256);
           if (need_mask) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
