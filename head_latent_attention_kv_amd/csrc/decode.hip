@@ -301,7 +301,7 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
   }
 
   if (!live) return;
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = wave_sum_pair(l);
   const float inv = 1.f / lt;
   const int64_t slot = (static_cast<int64_t>(b) * nch + ch) * n_h + h;
   _Float16* dst = opart + slot * DC + (DC / 2) * dh;

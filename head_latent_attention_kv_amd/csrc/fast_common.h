@@ -127,9 +127,19 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, char* 
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
+// Lanes l and l ^ 32 hold the same MFMA column. v_permlane32_swap of x with
+// itself leaves x[l % 32] in the first result and x[l % 32 + 32] in the
+// second, in every lane (checked on the device), so each lane gets both
+// halves' values on the VALU, without the LDS round trip of a lane shuffle.
+// Max and sum are commutative, so every lane gets the same bits as
+// x op x[l ^ 32].
 __device__ __forceinline__ float wave_max_pair(float x) {
-  // lanes l and l ^ 32 hold the same MFMA column
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace mla

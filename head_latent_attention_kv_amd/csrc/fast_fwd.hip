@@ -274,7 +274,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float lt = l[nt] + __shfl_xor(l[nt], 32, 64);
+    const float lt = wave_sum_pair(l[nt]);
     const int i = wq0 + 32 * nt + lr;
     if (i < S_loc) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
