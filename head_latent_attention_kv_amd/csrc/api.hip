@@ -80,6 +80,38 @@ KernelTimer::~KernelTimer() {
     g_launches[slot_].name = "";
 }
 
+mla_status side_stream(SideStream* out) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream per_dev[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_HIP, "no current device for the side stream");
+  SideStream& s = per_dev[dev];
+  if (s.st == nullptr) {
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess)
+      return fail(MLA_ERR_HIP, "hipStreamCreateWithFlags failed");
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+      return fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed");
+    s = n;
+  }
+  *out = s;
+  return MLA_OK;
+}
+
+mla_status side_fork(const SideStream& s, hipStream_t main) {
+  if (hipEventRecord(s.fork, main) != hipSuccess || hipStreamWaitEvent(s.st, s.fork, 0) != hipSuccess)
+    return fail(MLA_ERR_HIP, "fork to the side stream failed");
+  return MLA_OK;
+}
+
+mla_status side_join(const SideStream& s, hipStream_t main) {
+  if (hipEventRecord(s.join, s.st) != hipSuccess || hipStreamWaitEvent(main, s.join, 0) != hipSuccess)
+    return fail(MLA_ERR_HIP, "join from the side stream failed");
+  return MLA_OK;
+}
+
 FwdLayout fwd_layout(const Plan& p, bool fast) {
   FwdLayout L{};
   int64_t off = 0;

@@ -942,28 +942,37 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
             key_lo = static_cast<int>(p.key_lo),
             Kpad = static_cast<int>(p.Kpad);
   mla_status s;
+  // The layout conversions and the row preparation do not depend on the K/V
+  // rebuild, and the dQ kernel and the rope-key reduction not on the gradient
+  // GEMMs: each such group runs on a side stream next to the other (HBM-bound
+  // work beside MFMA-bound work).
+  SideStream side;
+  if ((s = side_stream(&side)) != MLA_OK) return s;
+  const hipStream_t st2 = side.st;
+  if ((s = side_fork(side, st)) != MLA_OK) return s;
 
-  // keys (row- and column-major) and V key-major
-  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, nullptr, Vkm, st)) != MLA_OK)
-    return s;
   // [W_UK | W_UV] rows in fp16 and c_kv^T in fp16 for the gradient GEMMs
   if ((s = launch_convert(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, W16, 2 * nk,
-                          0, Elem::F16, 1, st, "prep_w16")) != MLA_OK)
+                          0, Elem::F16, 1, st2, "prep_w16")) != MLA_OK)
     return s;
   if ((s = launch_convert(static_cast<const uint16_t*>(W_UV), nk, 0, p.d_c, p.d_c, nk, W16 + nk,
-                          2 * nk, 0, Elem::F16, 1, st, "prep_w16")) != MLA_OK)
+                          2 * nk, 0, Elem::F16, 1, st2, "prep_w16")) != MLA_OK)
     return s;
   if ((s = launch_transpose(static_cast<const uint16_t*>(c_kv) + p.key_lo * p.d_c, p.d_c, 0, p.Kn,
-                            p.Kpad, p.d_c, ckvT, p.Kpad, 0, Elem::F16, 1, st, "prep_ckvT")) != MLA_OK)
+                            p.Kpad, p.d_c, ckvT, p.Kpad, 0, Elem::F16, 1, st2, "prep_ckvT")) != MLA_OK)
     return s;
   {
-    KernelTimer kt("bwd_prep", st);
+    KernelTimer kt("bwd_prep", st2);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(S_pad / 64), p.n_h), dim3(256),
-                       0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
+                       0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
                        out, lse, cu_dev, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
                        S_pad, p.rm);
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
+  // keys (row-major, with the rope key) and V key-major
+  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, nullptr, Vkm, st)) != MLA_OK)
+    return s;
+  if ((s = side_join(side, st)) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
   // packed calls: query and key tiles in longest-processing-time order
   int *qorder = nullptr, *korder = nullptr;
@@ -985,20 +994,27 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                        p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
+  if ((s = side_fork(side, st)) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
-    KernelTimer kt(dS != nullptr ? "attn_bwd_dq_ds" : "attn_bwd_dq", st);
+    KernelTimer kt(dS != nullptr ? "attn_bwd_dq_ds" : "attn_bwd_dq", st2);
     if (dS != nullptr)
       hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
-                         0, st, info, Kfull, dS, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
+                         0, st2, info, Kfull, dS, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
                          p.scale);
     else
       hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
-                         0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
+                         0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
                          info, Kfull, Vkm, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt, p.scale,
                          scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
+  {
+    KernelTimer kt("reduce_rope", st2);
+    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st2, dKr,
+                       dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
+  }
+  if ((s = check_launch("rope-key gradient reduce")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0
   float* gpart = reinterpret_cast<float*>(at(L.gpart));
   const int64_t gpart_bytes = std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
@@ -1025,12 +1041,8 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                           128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart,
                           gpart_bytes)) != MLA_OK)
     return s;
-  {
-    KernelTimer kt("reduce_rope", st);
-    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st, dKr,
-                       dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
-  }
-  return check_launch("rope-key gradient reduce");
+  if ((s = side_join(side, st)) != MLA_OK) return s;
+  return MLA_OK;
 }
 
 }  // namespace mla

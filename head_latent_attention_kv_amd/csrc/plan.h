@@ -105,6 +105,20 @@ class KernelTimer {
   hipStream_t st_;
 };
 
+// A second stream on the current device, with a fork and a join event,
+// created once per host thread and device (default priority). Work that
+// depends only on what the caller's stream has already been given runs there:
+// fork() makes it wait for the caller's stream so far, join() makes the
+// caller's stream wait for everything given to it so far. From the caller's
+// side the call still behaves as if all its work were on the caller's stream.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+mla_status side_stream(SideStream* out);
+mla_status side_fork(const SideStream& s, hipStream_t main);
+mla_status side_join(const SideStream& s, hipStream_t main);
+
 // Segment start of global position p (host version; device twin in kernels).
 inline int64_t seg_lo_host(const int32_t* cu, int n_seqs, int64_t p) {
   if (n_seqs == 0 || cu == nullptr) return 0;
