@@ -110,15 +110,21 @@ def recorded_traffic(kernel, workload):
 
 def traffic_from_counters(fetch_csv, write_csv, workload):
     """Turn two rocprofv3 --pmc csv files (FETCH_SIZE, WRITE_SIZE; KiB per
-    dispatch) of a --counter-step run into HBM bytes per launch. Each counter
-    is scaled by bytes / counter of the plain device copy in the same run."""
+    dispatch) of a --counter-step run into HBM bytes per launch of its second
+    step. Each counter is scaled by bytes / counter of the plain device copy
+    in the same run."""
     import csv
     from collections import defaultdict
 
     def per_kernel(path, counter):
+        # the run's second step only (dispatches from the last forward-attention
+        # launch on): the first step's launches also touch fresh pages and
+        # load code objects
+        rows = list(csv.DictReader(open(path)))
+        first = max([int(r["Dispatch_Id"]) for r in rows if "attn_fwd" in r["Kernel_Name"]] or [0])
         vals = defaultdict(list)
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
+        for r in rows:
+            if r["Counter_Name"] == counter and int(r["Dispatch_Id"]) >= first:
                 vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         return vals
 
@@ -168,7 +174,9 @@ def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
     dense peak at the measured clock; LDS busy, SQ_LDS_IDX_ACTIVE over (active
     cycles x CUs); bank-conflict cycles as a share of LDS-active cycles; and
     the shares of wave time spent issuing VALU and LDS instructions and
-    waiting."""
+    waiting. Only the run's second step counts (dispatches from the last
+    forward-attention launch on): the first launch of each kernel also
+    loads its code object."""
     import csv
     import re
     from collections import defaultdict
@@ -176,7 +184,11 @@ def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
     def load(path):
         cnt = defaultdict(lambda: defaultdict(float))
         dur = defaultdict(dict)
-        for r in csv.DictReader(open(path)):
+        rows = list(csv.DictReader(open(path)))
+        first = max([int(r["Dispatch_Id"]) for r in rows if "attn_fwd" in r["Kernel_Name"]] or [0])
+        for r in rows:
+            if int(r["Dispatch_Id"]) < first:
+                continue
             name = r["Kernel_Name"]
             m = re.search(r"::(\w+)(<[^(]*>)?\(", name)
             z = re.search(r"_GLOBAL__N_1(\d+)(\w+)", name)
