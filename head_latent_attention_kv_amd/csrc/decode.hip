@@ -12,19 +12,17 @@
 //
 // Kernels (gfx950, fp16/bf16 MFMA with fp32 accumulation):
 //   1. head_gemm_kernel: per-head q_lat (bf16 in, fp16 out);
-//   2. decode_attn_kernel: split-KV attention. A workgroup owns one sequence,
-//      one chunk of its keys, up to 128 heads (4 waves x 32) and one half
-//      (256) of the 512 output dims. Keys and values are the same 576-wide
-//      latent rows: each 32-key block is loaded to registers, converted
-//      bf16 -> fp16 and written to one swizzled LDS tile that serves both
-//      S^T = K Q^T (row-wise fragments) and O^T += V^T P^T (transposed
-//      reads). The latent part of q_lat stays in registers, its rope part in
-//      LDS. The two halves of a
-//      chunk recompute S (a third more products than one workgroup holding
-//      all 512 dims, whose 256 accumulator registers per wave do not fit
-//      next to q_lat) and run back to back on one XCD, so the second reads
-//      the cache block from L2; the next block's loads are in flight while
-//      the current block is used;
+//   2. decode_attn_pair_kernel: split-KV attention. A workgroup of 8 waves
+//      owns one sequence, one chunk of its keys, up to 128 heads and all 512
+//      output dims. Keys and values are the same 576-wide latent rows: each
+//      32-key block is loaded to registers, converted bf16 -> fp16 and
+//      written to one swizzled LDS tile that serves both S^T = K Q^T
+//      (row-wise fragments) and O^T += V^T P^T (transposed reads). Waves w
+//      and w + 4 share 32 heads: each holds half of q_lat's latent dims in
+//      registers, takes half of the score products, and the two partial
+//      scores are added through LDS; each then accumulates half of the
+//      output dims. The next block's loads are in flight while the current
+//      block is used;
 //   3. decode_combine_kernel: merges the chunks (max, rescaled sums), writes
 //      o_lat in fp16 and lse;
 //   4. head_gemm_kernel: per-head out = o_lat W_UV_h (fp16 in, fp32 out).
@@ -45,11 +43,7 @@ constexpr int DB = 32;             // keys per block
 // row-wise and transposed 16-bit reads are conflict-free.
 constexpr int DROW = 1216;
 constexpr int DSTAGE = DB * DROW;
-constexpr int DWAVES = 4;
 constexpr int QR_ROW = DR * 2 + 16;               // q_rope LDS row pitch (odd slot count)
-constexpr int DPIECES = DB * (DL / 8);            // 16-byte pieces per block
-constexpr int DPT = DPIECES / (DWAVES * 64);      // per thread (9)
-static_assert(DPIECES % (DWAVES * 64) == 0, "pieces split evenly");
 constexpr float kTauD = 8.f;                      // lazy-rescale threshold, log2 units
 constexpr float kLn2D = 0.69314718055994530942f;
 
@@ -90,79 +84,90 @@ head_gemm_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t hx, const TIn* 
   }
 }
 
-// Split-KV attention of one chunk of one sequence's keys for up to 128 heads
-// and one half of the output dims. Partial results: opart[b][chunk][h][:] =
-// O / l (fp16; this workgroup's 256 dims) and ml[b][chunk][h] = (m, l) with
-// O = sum_j 2^(s_j scale log2e - m) c_kv[j] and l the same sum of weights;
-// chunks past the sequence's end write nothing. Work item w (of n_items =
-// nch * batch * head groups) runs as workgroups 16 (w / 8) + w % 8 (first
-// half) and that + 8 (second half): round-robin XCD assignment puts both on
-// one XCD, one after the other.
-__global__ void __launch_bounds__(DWAVES * 64)
-decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict__ q,
-                   const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_rope,
-                   const int32_t* __restrict__ cu, _Float16* __restrict__ opart,
-                   float2* __restrict__ ml, int n_h, int batch, int nch, int n_items, int chunk,
-                   float scale_log2) {
-  // two K/V stages, then q_rope of the workgroup's heads (144-byte rows)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * DSTAGE + 128 * QR_ROW];
-  const int bid = blockIdx.x;
-  const int item = ((bid >> 4) << 3) | (bid & 7), dh = (bid >> 3) & 1;
-  if (item >= n_items) return;                // whole workgroup
+// Split-KV attention: one workgroup of 8 waves owns a chunk of one sequence's keys
+// for up to 128 heads and all 512 output dims. Waves w and w + 4 form a pair
+// for heads 32 w' .. (w' = w % 4). Wave half kh = w / 4 holds q_lat dims
+// 256 kh .. 256 kh + 255 and computes the scores over those dims and rope
+// dims 32 kh .. 32 kh + 31 (18 products per 32-key block); the two partial
+// score tiles are added through LDS (a + b is the same in either order, so
+// both waves hold the same scores and weights), and each wave then
+// accumulates its 256 output dims (16 products). A wave holding all of q_lat
+// and half of the output dims would need about 400 registers (one wave per
+// SIMD) and two workgroups that each recompute the 36 score products per
+// block (52 products per wave and block, each cache block staged twice); here
+// it is 34, one staging, and two waves per SIMD.
+constexpr int PDW = 8;                                  // waves
+constexpr int PD_QR = 2 * DSTAGE;                       // q_rope rows of the 128 heads
+constexpr int PD_XS = PD_QR + 128 * QR_ROW;             // partial scores: 8 waves x 4 KiB
+constexpr int PD_LDS = PD_XS + PDW * 4096;
+static_assert(PD_LDS <= 160 * 1024, "paired decode fits the LDS");
+constexpr int PD_PARTS = 5, PD_PPART = 1;               // staging: 5 parts of one piece per thread
+static_assert(4 * PDW * 64 == DB * (DC / 8) && PDW * 64 / 2 == DB * (DR / 8) &&
+                  DB * (DL / 8) == 4 * PDW * 64 + DB * (DR / 8),
+              "four c_kv parts of a piece per thread and a k_rope part for half the threads");
+
+__global__ void __launch_bounds__(PDW * 64)
+decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict__ q,
+                        const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_rope,
+                        const int32_t* __restrict__ cu, _Float16* __restrict__ opart,
+                        float2* __restrict__ ml, int n_h, int batch, int nch, int chunk,
+                        float scale_log2) {
+  // two K/V stages, q_rope of the 128 heads (144-byte rows), partial scores
+  __shared__ __attribute__((aligned(1024))) char smem[PD_LDS];
+  const int item = blockIdx.x;
   const int ch = item % nch, b = (item / nch) % batch, hg = item / (nch * batch);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
+  const int wp = w & 3, kh = w >> 2;
   const int s0 = cu[b], len = cu[b + 1] - s0;
-  const int k0 = ch * chunk;                 // chunk's first key, within the sequence
+  const int k0 = ch * chunk;
   if (k0 >= len) return;                     // whole workgroup: nothing to do
   const int k1 = min(len, k0 + chunk);
   const int nblk = (k1 - k0 + DB - 1) / DB;
-  const int hw = hg * 128 + 32 * w;          // the wave's first head
+  const int hw = hg * 128 + 32 * wp;         // the pair's first head
   const bool live = hw < n_h;                // n_h is a multiple of 32
-  const int h = hw + lr;                     // this lane's head
+  const int h = hw + lr;
 
-  // staging: piece e = tid + 256 j of a block is 16 bytes of key e / 72,
-  // slot e % 72 (slots 0..63: c_kv, 64..71: k_rope); it lands in LDS slot
-  // xs_slot(key, slot) of the key's row. A block moves in three parts of
-  // three pieces per thread, spread over the products of the block before.
-  constexpr int PPART = DPT / 3;
-  static_assert(DPT % 3 == 0, "three staging parts");
-  auto load_part = [&](int blk, int part, u32x4 (&r)[PPART]) {
-    const int kb = k0 + blk * DB;            // block's first key (sequence-relative)
+  // staging: parts 0..3 move c_kv pieces, thread t taking key t / 64 + 8 p,
+  // 16-byte slot t % 64; part 4 moves the k_rope pieces, thread t < 256
+  // taking key t / 8, slot 64 + t % 8. Each part reads one array from a
+  // wave-uniform base with a 32-bit lane offset; a piece lands in LDS slot
+  // xs_slot(key, slot) of its key's row.
+  const int c_key0 = tid >> 6, c_off = 8 * (tid & 63);
+  const int r_key = (tid & 255) >> 3, r_off = r_key * DR + 8 * (tid & 7);
+  auto load_part = [&](int blk, int part, u32x4 (&r)[PD_PPART]) {
+    const int kb = k0 + blk * DB;
     const int64_t row0 = static_cast<int64_t>(s0) + kb;
-    const uint16_t* cb = c_kv + row0 * DC;
-    const uint16_t* rb = k_rope + row0 * DR;
-#pragma unroll
-    for (int j = 0; j < PPART; ++j) {
-      const int e = tid + DWAVES * 64 * (PPART * part + j);
-      const int key = e / (DL / 8), sl = e % (DL / 8);
-      if (kb + key < k1) {
-        const uint16_t* src = sl < DC / 8 ? cb + key * DC + 8 * sl : rb + key * DR + 8 * (sl - DC / 8);
-        r[j] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        r[j] = u32x4{0u, 0u, 0u, 0u};
-      }
+    if (part < 4) {
+      const int key = c_key0 + 8 * part;
+      r[0] = kb + key < k1
+                 ? *reinterpret_cast<const u32x4*>(c_kv + row0 * DC + (key * DC + c_off))
+                 : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      r[0] = tid < 256 && kb + r_key < k1
+                 ? *reinterpret_cast<const u32x4*>(k_rope + row0 * DR + r_off)
+                 : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_part = [&](int st, int part, const u32x4 (&r)[PPART]) {
+  auto store_part = [&](int st, int part, const u32x4 (&r)[PD_PPART]) {
     char* dst = smem + st * DSTAGE;
-#pragma unroll
-    for (int j = 0; j < PPART; ++j) {
-      const int e = tid + DWAVES * 64 * (PPART * part + j);
-      const int key = e / (DL / 8), sl = e % (DL / 8);
-      *reinterpret_cast<half8*>(dst + key * DROW + xs_slot(key, sl) * 16) = bf16x8_to_half8(r[j]);
+    if (part < 4) {
+      const int key = c_key0 + 8 * part;
+      *reinterpret_cast<half8*>(dst + key * DROW + xs_slot(key, tid & 63) * 16) = bf16x8_to_half8(r[0]);
+    } else if (tid < 256) {
+      *reinterpret_cast<half8*>(dst + r_key * DROW + xs_slot(r_key, 64 + (tid & 7)) * 16) =
+          bf16x8_to_half8(r[0]);
     }
   };
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane = head, k-slots = dims.
-  // The 512 latent dims stay in registers; the 64 rope dims are read from
-  // LDS (registers are the limit here).
-  half8 qf[DC / 16];
+  // this wave's half of q_lat (B operand of S^T = K Q^T); the rope dims of
+  // the pair's heads go to LDS (written by the half-0 wave)
+  half8 qf[16];
   {
-    const _Float16* ql = qlat + (static_cast<int64_t>(b) * n_h + h) * DC + 8 * lh;
+    const _Float16* ql = qlat + (static_cast<int64_t>(b) * n_h + h) * DC + 256 * kh + 8 * lh;
 #pragma unroll
-    for (int kk = 0; kk < DC / 16; ++kk) {
+    for (int kk = 0; kk < 16; ++kk) {
       if (live) {
         qf[kk] = *reinterpret_cast<const half8*>(ql + 16 * kk);
       } else {
@@ -170,24 +175,24 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
         for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<_Float16>(0.f);
       }
     }
-    // q_rope of this lane's head: dims 8 lh + 16 j .. (j = 0..3)
-    const uint16_t* qr = q + (static_cast<int64_t>(b) * n_h + h) * 192 + 128 + 8 * lh;
-    char* qrow = smem + 2 * DSTAGE + (32 * w + lr) * QR_ROW + 16 * lh;
+    if (kh == 0) {
+      const uint16_t* qr = q + (static_cast<int64_t>(b) * n_h + h) * 192 + 128 + 8 * lh;
+      char* qrow = smem + PD_QR + (32 * wp + lr) * QR_ROW + 16 * lh;
 #pragma unroll
-    for (int j = 0; j < DR / 16; ++j) {
-      half8 v;
-      if (live) {
-        v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(qr + 16 * j));
-      } else {
+      for (int j = 0; j < DR / 16; ++j) {
+        half8 v;
+        if (live) {
+          v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(qr + 16 * j));
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(0.f);
+          for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(0.f);
+        }
+        *reinterpret_cast<half8*>(qrow + 32 * j) = v;
       }
-      *reinterpret_cast<half8*>(qrow + 32 * j) = v;
     }
   }
-  const char* qrope = smem + 2 * DSTAGE + (32 * w + lr) * QR_ROW + 16 * lh;
+  const char* qrope = smem + PD_QR + (32 * wp + lr) * QR_ROW + 16 * lh;
 
-  // O^T accumulators: 32 heads x 256 dims (dh * 256 ..) per wave
   constexpr int NDT = DC / 2 / 32;
   f32x16 o[NDT];
 #pragma unroll
@@ -196,14 +201,16 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
   float m = -INFINITY, l = 0.f;
   const half2v ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-  const int k_r0 = xs_row_base<DROW>(swap23(lr), lh, 0);   // K rows swap23(lr)
+  const int k_r0 = xs_row_base<DROW>(swap23(lr), lh, 0);
   const int k_r1 = xs_row_base<DROW>(swap23(lr), lh, 1);
-  const int v_t0 = xs_tr_base<DROW>(lane, 0);              // V^T transposed reads
+  const int v_t0 = xs_tr_base<DROW>(lane, 0);
   const int v_t1 = xs_tr_base<DROW>(lane, 1);
+  char* const xs_own = smem + PD_XS + w * 4096 + lane * 16;
+  const char* const xs_par = smem + PD_XS + (w ^ 4) * 4096 + lane * 16;
 
-  u32x4 stg[PPART];
+  u32x4 stg[PD_PPART];
 #pragma unroll
-  for (int part = 0; part < 3; ++part) {
+  for (int part = 0; part < PD_PARTS; ++part) {
     load_part(0, part, stg);
     store_part(0, part, stg);
   }
@@ -211,34 +218,50 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
   for (int bi = 0; bi < nblk; ++bi) {
     const int st = bi & 1;
     const bool more = bi + 1 < nblk;
-    if (more) load_part(bi + 1, 0, stg);   // in flight during the score products
+    if (more) load_part(bi + 1, 0, stg);
     const char* base = smem + st * DSTAGE;
     f32x16 s;
-    if (live) {
-      // S^T rows: keys swap23(lr) of the block
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      constexpr int PF = 3;
-      auto frag = [&](int kk) {
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    if (live) {
+      // partial S^T over this half's 18 k-steps: latent 16 kh .. 16 kh + 15,
+      // rope 32 + 2 kh, 33 + 2 kh (k-steps of 16 dims of the 576-wide row)
+      constexpr int PF = 2;
+      auto kstep = [&](int i) { return i < 16 ? 16 * kh + i : 32 + 2 * kh + (i - 16); };
+      auto frag = [&](int i) {
+        const int kk = kstep(i);
         return *reinterpret_cast<const half8*>(base + ((kk & 1) ? k_r1 : k_r0) + 64 * (kk >> 1));
       };
       half8 fa[PF + 1];
 #pragma unroll
       for (int i = 0; i < PF; ++i) fa[i] = frag(i);
 #pragma unroll
-      for (int kk = 0; kk < DL / 16; ++kk) {
-        if (kk + PF < DL / 16) fa[(kk + PF) % (PF + 1)] = frag(kk + PF);
-        const half8 qb = kk < DC / 16 ? qf[kk] : *reinterpret_cast<const half8*>(qrope + 32 * (kk - DC / 16));
-        s = mfma_f16(fa[kk % (PF + 1)], qb, s);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 18; ++i) {
+        if (i + PF < 18) fa[(i + PF) % (PF + 1)] = frag(i + PF);
+        const half8 qb = i < 16 ? qf[i] : *reinterpret_cast<const half8*>(qrope + 32 * (2 * kh + i - 16));
+        s = mfma_f16(fa[i % (PF + 1)], qb, s);
       }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(xs_own + g * 1024) = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
     }
     if (more) {
       store_part(st ^ 1, 0, stg);
       load_part(bi + 1, 1, stg);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // partial scores visible
+    if (more) {
+      store_part(st ^ 1, 1, stg);
+      load_part(bi + 1, 2, stg);
+    }
     half8 pb[2];
     if (live) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(xs_par + g * 1024);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * g + e] += v[e];
+      }
       const int kb = k0 + bi * DB;
       if (kb + DB > k1) {
 #pragma unroll
@@ -273,16 +296,14 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
       l = sum;
     }
     if (more) {
-      store_part(st ^ 1, 1, stg);
-      load_part(bi + 1, 2, stg);
+      store_part(st ^ 1, 2, stg);
+      load_part(bi + 1, 3, stg);
     }
     if (live) {
-      // O^T (dims x heads) += V^T (dims x keys) P^T (keys x heads)
-      // V^T fragments run PF products ahead (16 products: dim tile k % 8 of
-      // this half, keys 16 (k / 8) ..)
-      constexpr int PF = 3, NPV = 2 * NDT;
+      // O^T (this half's dims x heads) += V^T P^T
+      constexpr int PF = 2, NPV = 2 * NDT;
       auto vfrag = [&](int k) {
-        const int off = 16 * (k / NDT) * DROW + 64 * (NDT * dh + k % NDT);
+        const int off = 16 * (k / NDT) * DROW + 64 * (NDT * kh + k % NDT);
         return frag_tr2(base + v_t0 + off, base + v_t1 + off);
       };
       half8 fv[PF + 1];
@@ -291,12 +312,14 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
 #pragma unroll
       for (int k = 0; k < NPV; ++k) {
         if (k + PF < NPV) fv[(k + PF) % (PF + 1)] = vfrag(k + PF);
-        const int dt = k % NDT;
-        o[dt] = mfma_f16(fv[k % (PF + 1)], pb[k / NDT], o[dt]);
-        __builtin_amdgcn_sched_barrier(0);
+        o[k % NDT] = mfma_f16(fv[k % (PF + 1)], pb[k / NDT], o[k % NDT]);
       }
     }
-    if (more) store_part(st ^ 1, 2, stg);
+    if (more) {
+      store_part(st ^ 1, 3, stg);
+      load_part(bi + 1, 4, stg);
+      store_part(st ^ 1, 4, stg);
+    }
     __syncthreads();
   }
 
@@ -304,7 +327,7 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
   const float lt = wave_sum_pair(l);
   const float inv = 1.f / lt;
   const int64_t slot = (static_cast<int64_t>(b) * nch + ch) * n_h + h;
-  _Float16* dst = opart + slot * DC + (DC / 2) * dh;
+  _Float16* dst = opart + slot * DC + 256 * kh;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -314,7 +337,7 @@ decode_attn_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict
       for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(o[dt][4 * g + e] * inv);
       *reinterpret_cast<half4*>(dst + 32 * dt + 8 * g + 4 * lh) = v;
     }
-  if (lh == 0 && dh == 0) ml[slot] = make_float2(m, lt);   // both halves hold the same
+  if (lh == 0 && kh == 0) ml[slot] = make_float2(m, lt);
 }
 
 // o_lat[b][h][:] = sum_c w_c opart[b][c][h][:] / sum_c w_c with w_c =
@@ -397,12 +420,11 @@ mla_status fast_decode(const DecodePlan& p, const void* q, const void* c_kv, con
   {
     KernelTimer kt("decode_attn", st);
     const int64_t items = static_cast<int64_t>(p.nch) * B * ((n_h + 127) / 128);
-    const int64_t blocks = (items + 7) / 8 * 16;
-    if (blocks > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "decode: too many workgroups");
-    hipLaunchKernelGGL(decode_attn_kernel, dim3(static_cast<unsigned>(blocks)), dim3(DWAVES * 64), 0,
+    if (items > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "decode: too many workgroups");
+    hipLaunchKernelGGL(decode_attn_pair_kernel, dim3(static_cast<unsigned>(items)), dim3(PDW * 64), 0,
                        st, qlat, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c_kv),
-                       static_cast<const uint16_t*>(k_rope), cu_dev, opart, ml, n_h, B, p.nch,
-                       static_cast<int>(items), p.chunk, p.scale * 1.44269504088896340736f);
+                       static_cast<const uint16_t*>(k_rope), cu_dev, opart, ml, n_h, B, p.nch, p.chunk,
+                       p.scale * 1.44269504088896340736f);
   }
   if ((s = check_launch("decode attention")) != MLA_OK) return s;
   {

@@ -280,6 +280,33 @@ def test_forward_backward_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_backward_ordered_on_caller_streams():
+    """The fast backward runs part of its kernels on an internal stream, forked
+    from the caller's stream and joined back into it. Work enqueued on the
+    caller's stream right after the call (no host sync in between) must see
+    the final gradients, and calls on two other caller streams must give the
+    same bits as a call on the default stream."""
+    cfg = workloads.MLAConfig("streams", n_h=8, S=1500, S_loc=1000, q_offset=500, dtype="bf16",
+                              backward=True, **DSV3)
+    announce("backward on caller streams")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    ref = run(cfg, x, backward=True)
+    dev = to_device(x, cfg)
+    args = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    torch.cuda.synchronize()
+    copies = []
+    for s in (torch.cuda.Stream(), torch.cuda.Stream()):
+        with torch.cuda.stream(s):
+            call = hla.MLACall(*args, q_offset=cfg.q_offset, backward=True)
+            out, lse = call.fwd(*args)
+            g = call.bwd(dev["dout"], *args, out, lse)
+            copies.append([t.clone() for t in g])   # same stream, right after the call
+    torch.cuda.synchronize()
+    for got in copies:
+        for k, t in zip(GRADS, got):
+            assert np.array_equal(t.cpu().numpy(), ref[k]), k
+
+
 def test_empty_shard():
     cfg = workloads.MLAConfig("empty", n_h=2, S=64, S_loc=0, q_offset=64, dtype="bf16",
                               backward=True, **DSV3)
