@@ -433,8 +433,10 @@ def decode_bench(name, steps, warmup):
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                     "traffic": None, "ms_per_launch": t_attn,
                     "tflops": round(f_attn / (t_attn / 1e3) / 1e12, 2),
-                    "mfma_tflops_executed": round(f_attn * (2 * 576 + 512) / (576 + 512)
-                                                  / (t_attn / 1e3) / 1e12, 2)}
+                    # each score and output product runs once (the waves of a
+                    # pair split the score contraction); only the padding of a
+                    # sequence's last 32-key block is executed beyond this
+                    "mfma_tflops_executed": round(f_attn / (t_attn / 1e3) / 1e12, 2)}
     res = {"metric": "MLA absorbed decode step (latent cache), TFLOP/s",
            "value": round((f_attn + f_proj) / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s",
            "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
