@@ -96,15 +96,38 @@ head_gemm_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t hx, const TIn* 
 // SIMD) and two workgroups that each recompute the 36 score products per
 // block (52 products per wave and block, each cache block staged twice); here
 // it is 34, one staging, and two waves per SIMD.
+//
+// Staging: each 32-key block is copied raw (bf16) by LDS DMA into one of two
+// slots, two blocks ahead, so that two blocks of the cache are in flight per
+// workgroup without holding registers; all threads then convert the block
+// into the one fp16 tile the products read.
 constexpr int PDW = 8;                                  // waves
-constexpr int PD_QR = 2 * DSTAGE;                       // q_rope rows of the 128 heads
+constexpr int PD_RAW = DB * DC * 2 + DB * DR * 2;       // a raw block: c_kv rows, then k_rope rows (36 KiB)
+constexpr int PD_TILE = 2 * PD_RAW;                     // the fp16 tile
+constexpr int PD_QR = PD_TILE + DSTAGE;                 // q_rope rows of the 128 heads
 constexpr int PD_XS = PD_QR + 128 * QR_ROW;             // partial scores: 8 waves x 4 KiB
 constexpr int PD_LDS = PD_XS + PDW * 4096;
 static_assert(PD_LDS <= 160 * 1024, "paired decode fits the LDS");
-constexpr int PD_PARTS = 5, PD_PPART = 1;               // staging: 5 parts of one piece per thread
+static_assert(PD_RAW % 1024 == 0 && DC * 2 == 1024 && 8 * DR * 2 == 1024,
+              "a c_kv row, or the k_rope rows of 8 keys, per DMA wave instruction");
+constexpr int PD_PIECES = PD_RAW / 1024;                // 36: piece I = w + 8 j
 static_assert(4 * PDW * 64 == DB * (DC / 8) && PDW * 64 / 2 == DB * (DR / 8) &&
                   DB * (DL / 8) == 4 * PDW * 64 + DB * (DR / 8),
-              "four c_kv parts of a piece per thread and a k_rope part for half the threads");
+              "conversion: four c_kv pieces per thread and a k_rope piece for half the threads");
+
+// s_waitcnt vmcnt(n) for n = 0, 4, 5, other counters at their maxima (gfx9
+// encoding: vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
+  else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+__device__ __forceinline__ const uint16_t* scalar_ptr(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 __global__ void __launch_bounds__(PDW * 64)
 decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __restrict__ q,
@@ -129,35 +152,54 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
   const bool live = hw < n_h;                // n_h is a multiple of 32
   const int h = hw + lr;
 
-  // staging: parts 0..3 move c_kv pieces, thread t taking key t / 64 + 8 p,
-  // 16-byte slot t % 64; part 4 moves the k_rope pieces, thread t < 256
-  // taking key t / 8, slot 64 + t % 8. Each part reads one array from a
-  // wave-uniform base with a 32-bit lane offset; a piece lands in LDS slot
-  // xs_slot(key, slot) of its key's row.
-  const int c_key0 = tid >> 6, c_off = 8 * (tid & 63);
-  const int r_key = (tid & 255) >> 3, r_off = r_key * DR + 8 * (tid & 7);
-  auto load_part = [&](int blk, int part, u32x4 (&r)[PD_PPART]) {
+  // DMA of block blk into raw slot blk % 2: piece I (< 32) is key I's c_kv
+  // row, piece 32 + r the k_rope rows of keys 8 r .. 8 r + 7. Every wave
+  // always issues its pieces (5 for waves 0..3, 4 for waves 4..7), so that
+  // vmcnt counts stay exact: rows past the chunk read the chunk's last row
+  // instead, and the conversion writes zeros for them.
+  const int n_dma = w < PD_PIECES - 4 * PDW ? 5 : 4;
+  auto issue = [&](int blk) {
     const int kb = k0 + blk * DB;
-    const int64_t row0 = static_cast<int64_t>(s0) + kb;
-    if (part < 4) {
-      const int key = c_key0 + 8 * part;
-      r[0] = kb + key < k1
-                 ? *reinterpret_cast<const u32x4*>(c_kv + row0 * DC + (key * DC + c_off))
-                 : u32x4{0u, 0u, 0u, 0u};
-    } else {
-      r[0] = tid < 256 && kb + r_key < k1
-                 ? *reinterpret_cast<const u32x4*>(k_rope + row0 * DR + r_off)
-                 : u32x4{0u, 0u, 0u, 0u};
+    const int64_t last = static_cast<int64_t>(s0) + k1 - 1;   // the chunk's last row (>= s0)
+    char* raw = smem + (blk & 1) * PD_RAW;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int I = w + PDW * j;   // wave-uniform
+      if (I < DB) {
+        const int64_t row = min(static_cast<int64_t>(s0) + kb + I, last);
+        lds_dma16(scalar_ptr(c_kv + row * DC), lane * 16u, raw + I * 1024);
+      } else if (I < PD_PIECES) {
+        // from the sequence's first row: the lane's row, clamped to the chunk
+        const int key = min(kb + 8 * (I - DB) + (lane >> 3), k1 - 1);
+        uint32_t off = static_cast<uint32_t>(key * DR * 2 + (lane & 7) * 16);
+        asm volatile("" : "+v"(off));
+        lds_dma16(scalar_ptr(k_rope + static_cast<int64_t>(s0) * DR), off, raw + I * 1024);
+      }
     }
   };
-  auto store_part = [&](int st, int part, const u32x4 (&r)[PD_PPART]) {
-    char* dst = smem + st * DSTAGE;
-    if (part < 4) {
-      const int key = c_key0 + 8 * part;
-      *reinterpret_cast<half8*>(dst + key * DROW + xs_slot(key, tid & 63) * 16) = bf16x8_to_half8(r[0]);
-    } else if (tid < 256) {
-      *reinterpret_cast<half8*>(dst + r_key * DROW + xs_slot(r_key, 64 + (tid & 7)) * 16) =
-          bf16x8_to_half8(r[0]);
+  // raw slot blk % 2 -> fp16 tile: thread t converts key t / 64 + 8 p, slot
+  // t % 64 of c_kv (p < 4) and, for t < 256, key t / 8, rope slot t % 8; a
+  // piece lands in LDS slot xs_slot(key, slot) of its key's row, zeros past
+  // the chunk
+  auto convert = [&](int blk) {
+    const int kb = k0 + blk * DB;
+    const char* raw = smem + (blk & 1) * PD_RAW;
+    char* tile = smem + PD_TILE;
+    half8 zero;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zero[e] = static_cast<_Float16>(0.f);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 6) + 8 * p, sl = tid & 63;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + key * 1024 + sl * 16);
+      *reinterpret_cast<half8*>(tile + key * DROW + xs_slot(key, sl) * 16) =
+          kb + key < k1 ? bf16x8_to_half8(v) : zero;
+    }
+    if (tid < 256) {
+      const int key = tid >> 3, rs = tid & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + DB * 1024 + key * 128 + rs * 16);
+      *reinterpret_cast<half8*>(tile + key * DROW + xs_slot(key, 64 + rs) * 16) =
+          kb + key < k1 ? bf16x8_to_half8(v) : zero;
     }
   };
 
@@ -208,18 +250,17 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
   char* const xs_own = smem + PD_XS + w * 4096 + lane * 16;
   const char* const xs_par = smem + PD_XS + (w ^ 4) * 4096 + lane * 16;
 
-  u32x4 stg[PD_PPART];
-#pragma unroll
-  for (int part = 0; part < PD_PARTS; ++part) {
-    load_part(0, part, stg);
-    store_part(0, part, stg);
-  }
-  __syncthreads();   // first block and q_rope in LDS
+  if (nblk > 0) issue(0);
+  if (nblk > 1) issue(1);
+  // block 0 landed (loads complete in issue order, and at most block 1's
+  // pieces and the q loads above may remain), q_rope written
+  wait_vm_n(nblk > 1 ? n_dma : 0);
+  __syncthreads();
   for (int bi = 0; bi < nblk; ++bi) {
-    const int st = bi & 1;
-    const bool more = bi + 1 < nblk;
-    if (more) load_part(bi + 1, 0, stg);
-    const char* base = smem + st * DSTAGE;
+    convert(bi);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // tile ready, raw slot free
+    if (bi + 2 < nblk) issue(bi + 2);
+    const char* base = smem + PD_TILE;
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -245,15 +286,7 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4*>(xs_own + g * 1024) = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
     }
-    if (more) {
-      store_part(st ^ 1, 0, stg);
-      load_part(bi + 1, 1, stg);
-    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // partial scores visible
-    if (more) {
-      store_part(st ^ 1, 1, stg);
-      load_part(bi + 1, 2, stg);
-    }
     half8 pb[2];
     if (live) {
 #pragma unroll
@@ -295,10 +328,6 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
       }
       l = sum;
     }
-    if (more) {
-      store_part(st ^ 1, 2, stg);
-      load_part(bi + 1, 3, stg);
-    }
     if (live) {
       // O^T (this half's dims x heads) += V^T P^T
       constexpr int PF = 2, NPV = 2 * NDT;
@@ -315,11 +344,9 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
         o[k % NDT] = mfma_f16(fv[k % (PF + 1)], pb[k / NDT], o[k % NDT]);
       }
     }
-    if (more) {
-      store_part(st ^ 1, 3, stg);
-      load_part(bi + 1, 4, stg);
-      store_part(st ^ 1, 4, stg);
-    }
+    // block bi + 1 landed (block bi + 2's pieces may stay in flight); every
+    // wave is done with the tile
+    if (bi + 1 < nblk) wait_vm_n(bi + 2 < nblk ? n_dma : 0);
     __syncthreads();
   }
 
