@@ -307,6 +307,47 @@ def test_backward_ordered_on_caller_streams():
             assert np.array_equal(t.cpu().numpy(), ref[k]), k
 
 
+def test_graph_replays_match_eager():
+    """Forward and backward captured into one HIP graph (through torch) and
+    replayed: every replay, with eager work and a host synchronisation
+    between replays, gives the eager call's bits. The library enqueues no
+    memset or allocation, and the backward's side stream joins the capture
+    through its fork event and leaves it through its join event."""
+    cfg = workloads.MLAConfig("graph", n_h=8, S=1500, S_loc=1000, q_offset=500, dtype="bf16",
+                              backward=True, **DSV3)
+    announce("graph capture and replay")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    ref = run(cfg, x, backward=True)
+    dev = to_device(x, cfg)
+    args = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    call = hla.MLACall(*args, q_offset=cfg.q_offset, backward=True)
+    out, lse = call.fwd(*args)
+    grads = call.bwd(dev["dout"], *args, out, lse)   # eager: also creates the side stream
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                     # warm-up off the default stream
+        call.fwd(*args, out=out, lse=lse)
+        call.bwd(dev["dout"], *args, out, lse, grads=grads)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call.fwd(*args, out=out, lse=lse)
+        call.bwd(dev["dout"], *args, out, lse, grads=grads)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (out, lse, *grads):
+            t.fill_(7.0)                               # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref["out"])
+        assert np.array_equal(lse.cpu().numpy(), ref["lse"])
+        for k, t in zip(GRADS, grads):
+            assert np.array_equal(t.cpu().numpy(), ref[k]), k
+
+
 def test_empty_shard():
     cfg = workloads.MLAConfig("empty", n_h=2, S=64, S_loc=0, q_offset=64, dtype="bf16",
                               backward=True, **DSV3)
