@@ -408,18 +408,33 @@ def decode_bench(name, steps, warmup):
     for _ in range(warmup):
         call(*a, out=out, lse=lse)
     torch.cuda.synchronize()
+    # per-kernel breakdown in a short pass of its own (every kernel bracketed
+    # by events); the timed region brackets only the attention kernel
+    n_brk = max(1, min(5, steps))
+    hla.timing_select(None)
     hla.timing_enable(True)
+    for _ in range(n_brk):
+        call(*a, out=out, lse=lse)
+    torch.cuda.synchronize()
+    kern = {}
+    for kname in hla.timing_names():
+        tot, n = hla.timing_read(kname)
+        kern[kname] = {"ms_per_launch": round(tot / max(n, 1), 4),
+                       "launches_per_step": n / n_brk}
+    hla.timing_enable(False)
+    hla.timing_select(["decode_attn"])
+    hla.timing_enable(True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         call(*a, out=out, lse=lse)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = {}
-    for kname in hla.timing_names():
-        tot, n = hla.timing_read(kname)
-        kern[kname] = {"ms_per_launch": round(tot / max(n, 1), 4),
-                       "launches_per_step": n / steps}
+    tot, n = hla.timing_read("decode_attn")
+    if n:
+        kern["decode_attn"] = {"ms_per_launch": round(tot / n, 4), "launches_per_step": n / steps}
     hla.timing_enable(False)
+    hla.timing_select(None)
     keys = int(cu[-1])
     n_h, B = cfg.n_h, cfg.S_loc
     f_attn = 2 * n_h * (576 + 512) * keys
@@ -571,8 +586,28 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+
+    # Per-kernel breakdown: a short pass with every kernel bracketed by HIP
+    # events (each pair adds a few microseconds between launches, so this
+    # pass is not the timed one). It also names the dominant kernel.
+    n_brk = max(1, min(5, args.steps))
+    hla.timing_select(None)
+    hla.timing_enable(True)
+    for _ in range(n_brk):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in hla.timing_names():
+        tot, n = hla.timing_read(name)
+        kern[name] = {"ms_per_launch": tot / max(n, 1), "launches_per_step": n / n_brk,
+                      "ms_per_step": tot / n_brk}
+    hla.timing_enable(False)
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"]) if kern else None
+
+    # Timed region: only the dominant kernel is bracketed (for the roofline).
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    hla.timing_select([dom] if dom else None)
     hla.timing_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -587,13 +622,12 @@ def main():
     fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
     bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
     step_ms = wall * 1e3 / args.steps
-    kern = {}
-    for name in hla.timing_names():
-        tot, n = hla.timing_read(name)
-        kern[name] = {"ms_per_launch": tot / max(n, 1), "launches_per_step": n / args.steps,
-                      "ms_per_step": tot / args.steps}
+    if dom:
+        tot, n = hla.timing_read(dom)
+        kern[dom].update({"ms_per_launch": tot / max(n, 1), "ms_per_step": tot / args.steps,
+                          "launches_per_step": n / args.steps})
     hla.timing_enable(False)
-    dom = max(kern, key=lambda k: kern[k]["ms_per_step"]) if kern else None
+    hla.timing_select(None)
     roofline = None
     if dom:
         kf = kernel_flops(dom, cfg, pairs, kn)
@@ -654,6 +688,7 @@ def main():
         "device": device_info(torch),
         "roofline": roofline,
         "kernels": kern,
+        "kernels_breakdown_steps": n_brk,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

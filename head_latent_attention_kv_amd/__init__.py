@@ -83,6 +83,7 @@ EXPORTED = {
                                        ctypes.c_size_t, _P]),
     "mla_laga_uses_fast_path": (ctypes.c_int, [_DESCP]),
     "mla_laga_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "mla_laga_timing_select": (ctypes.c_int, [ctypes.c_char_p]),
     "mla_laga_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), _I64P]),
     "mla_laga_timing_names": (ctypes.c_char_p, []),
     "mla_laga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -227,6 +228,12 @@ def timing_enable(on: bool = True):
     """Bracket every library kernel with HIP events on its stream (and forget
     earlier records)."""
     _check(load_library().mla_laga_timing_enable(1 if on else 0))
+
+
+def timing_select(names=None):
+    """Bracket only the kernels named in `names` (a list; None: every kernel)."""
+    arg = None if not names else ";".join(names).encode()
+    _check(load_library().mla_laga_timing_select(arg))
 
 
 def timing_read(kernel: str) -> Tuple[float, int]:

@@ -38,6 +38,7 @@ struct TimedLaunch {
   hipEvent_t start, stop;
 };
 bool g_timing = false;
+std::string g_select;   // ";name;name;" or empty (every kernel)
 std::vector<TimedLaunch> g_launches;
 std::vector<hipEvent_t> g_event_pool;
 std::string g_names;
@@ -64,6 +65,7 @@ void release_records() {
 
 KernelTimer::KernelTimer(const char* name, hipStream_t st) : st_(st) {
   if (!g_timing) return;
+  if (!g_select.empty() && g_select.find(";" + std::string(name) + ";") == std::string::npos) return;
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return;
   if (hipEventRecord(a, st) != hipSuccess) {
@@ -488,6 +490,12 @@ mla_status mla_laga_timing_enable(int on) {
     if (!r.name.empty()) (void)hipEventSynchronize(r.stop);
   release_records();
   g_timing = on != 0;
+  return MLA_OK;
+}
+
+mla_status mla_laga_timing_select(const char* names) {
+  g_select.clear();
+  if (names != nullptr && names[0] != '\0') g_select = ";" + std::string(names) + ";";
   return MLA_OK;
 }
 

@@ -228,8 +228,13 @@ mla_status mla_laga_count(const mla_laga_desc* desc, const int32_t* cu_seqlens_h
  * duration (ms) and launch count of the kernels named `kernel` (the names
  * are listed by mla_laga_timing_names, separated by ';'). Not thread-safe:
  * enable, run and read from one host thread.
+ * mla_laga_timing_select restricts the bracketing to the kernels whose
+ * names appear in `names` (';'-separated, host string, copied); NULL or ""
+ * selects every kernel again. Each pair of events adds a few microseconds
+ * between launches, so a timed run brackets only the kernels it reports.
  */
 mla_status mla_laga_timing_enable(int on);
+mla_status mla_laga_timing_select(const char* names);
 mla_status mla_laga_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 const char* mla_laga_timing_names(void);
 
