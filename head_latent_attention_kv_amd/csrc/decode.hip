@@ -15,14 +15,13 @@
 //   2. decode_attn_pair_kernel: split-KV attention. A workgroup of 8 waves
 //      owns one sequence, one chunk of its keys, up to 128 heads and all 512
 //      output dims. Keys and values are the same 576-wide latent rows: each
-//      32-key block is loaded to registers, converted bf16 -> fp16 and
-//      written to one swizzled LDS tile that serves both S^T = K Q^T
-//      (row-wise fragments) and O^T += V^T P^T (transposed reads). Waves w
-//      and w + 4 share 32 heads: each holds half of q_lat's latent dims in
-//      registers, takes half of the score products, and the two partial
-//      scores are added through LDS; each then accumulates half of the
-//      output dims. The next block's loads are in flight while the current
-//      block is used;
+//      32-key block is copied raw by LDS DMA two blocks ahead, then
+//      converted bf16 -> fp16 into one swizzled LDS tile that serves both
+//      S^T = K Q^T (row-wise fragments) and O^T += V^T P^T (transposed
+//      reads). Waves w and w + 4 share 32 heads: each holds half of q_lat's
+//      latent dims in registers, takes half of the score products, and the
+//      two partial scores are added through LDS; each then accumulates half
+//      of the output dims;
 //   3. decode_combine_kernel: merges the chunks (max, rescaled sums), writes
 //      o_lat in fp16 and lse;
 //   4. head_gemm_kernel: per-head out = o_lat W_UV_h (fp16 in, fp32 out).
@@ -84,8 +83,8 @@ head_gemm_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t hx, const TIn* 
   }
 }
 
-// Split-KV attention: one workgroup of 8 waves owns a chunk of one sequence's keys
-// for up to 128 heads and all 512 output dims. Waves w and w + 4 form a pair
+// Split-KV attention: one workgroup of 8 waves owns a chunk of one
+// sequence's keys for up to 128 heads and all 512 output dims. Waves w and w + 4 form a pair
 // for heads 32 w' .. (w' = w % 4). Wave half kh = w / 4 holds q_lat dims
 // 256 kh .. 256 kh + 255 and computes the scores over those dims and rope
 // dims 32 kh .. 32 kh + 31 (18 products per 32-key block); the two partial
