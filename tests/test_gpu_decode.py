@@ -97,3 +97,36 @@ def test_decode_matches_explicit_library_path():
     torch.cuda.synchronize()
     check("out", out, eo.cpu().numpy())
     check("lse", lse, el.cpu().numpy())
+
+
+def test_decode_graph_replays_match_eager():
+    """Decode captured into a HIP graph (through torch) and replayed three
+    times, with eager fills and host synchronisations between replays: every
+    replay gives the eager call's bits."""
+    cfg = workloads.decode_config("dec_graph", 64, [5000, 1, 700, 257], seed=6)
+    announce("decode graph capture and replay")
+    x = workloads.make_inputs(cfg, with_dout=False)
+    dev = to_device(x, cfg, names=("q", "c_kv", "k_rope", "W_UK", "W_UV"))
+    args = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+    call = hla.MLADecodeCall(*args, cfg.cu_seqlens())
+    out, lse = call(*args)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.cpu().numpy(), lse.cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                  # warm-up off the default stream
+        call(*args, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(*args, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref_out)
+        assert np.array_equal(lse.cpu().numpy(), ref_lse)
