@@ -95,9 +95,12 @@ mla_status side_stream(SideStream* out) {
     if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess)
       return fail(MLA_ERR_HIP, "hipStreamCreateWithFlags failed");
     if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      if (n.fork != nullptr) (void)hipEventDestroy(n.fork);
+      (void)hipStreamDestroy(n.st);
       return fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed");
-    s = n;
+    }
+    s = n;   // kept until the process ends
   }
   *out = s;
   return MLA_OK;
