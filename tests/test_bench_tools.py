@@ -80,3 +80,72 @@ def test_utilisation_formulas(tmp_path):
     # 1000 TFLOP/s against the dense peak scaled to 2.0 GHz
     assert frac == f"{100 * 1000.0 / (bench.PEAK_TFLOPS * 2.0 / 2.4):.1f}%"
     assert (valu, ldsi, wait) == ("20.0%", "5.0%", "40.0%")
+
+
+# ---------------------------------------------------------------- FLOP counts
+def _golden_counts():
+    rows = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "config_counts.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, P, kn, lo, ff, fb = line.split()
+        rows[name] = tuple(int(v) for v in (P, kn, lo, ff, fb))
+    return rows
+
+
+def test_bench_flops_match_the_oracle_count_on_every_configuration():
+    """bench.flops (the numerator of the headline value) equals the oracle's
+    count, forward and backward, on all five configurations, and both equal
+    the stored counts."""
+    import oracle
+    import workloads
+    golden = _golden_counts()
+    for name in workloads.CONFIG_ORDER:
+        c = workloads.config(name)
+        cu = c.cu_seqlens()
+        P = oracle.visible_pairs(c.S_loc, c.q_offset, cu)
+        kn = oracle.keys_needed(c.S_loc, c.q_offset, cu)
+        args = (c.n_h, c.d_c, c.d_rope, c.d_nope, c.d_v, c.S_loc, c.q_offset, cu)
+        for bwd, col in ((False, 3), (True, 4)):
+            f = bench.flops(c, P, kn, bwd)
+            assert f == oracle.attention_flops(*args, backward=bwd) == golden[name][col], (name, bwd)
+        assert golden[name][:2] == (P, kn)
+
+
+def test_flops_of_the_full_head_configurations_by_hand():
+    """Hand counts at DeepSeek-V3 head dims (d_qk = 192, d_v = 128, d_c =
+    512, 128 heads). Per visible pair and head: forward 192 + 128
+    multiply-adds (scores, weights x V), backward 3 x 192 + 2 x 128 (scores
+    again, dq, dK; dP, dV). Per needed key and head: forward 512 x 256
+    (rebuilding K_nope and V), backward twice that (dc_kv, dW).
+    Full causal 8192: 8192 x 8193 / 2 = 33,558,528 pairs, 8192 keys.
+    The 2048-row shard at 14336 of 16384: 2048 x 14336 + 2048 x 2049 / 2 =
+    31,458,304 pairs, 16384 keys."""
+    import workloads
+    pair_f, pair_b = 2 * 128 * 320, 2 * 128 * 832
+    key_f, key_b = 2 * 128 * 512 * 256, 4 * 128 * 512 * 256
+    for name, P, kn in (("h128_s8k_bwd", 33_558_528, 8192),
+                        ("h128_s16k_shard", 31_458_304, 16384)):
+        c = workloads.config(name)
+        assert bench.flops(c, P, kn, False) == pair_f * P + key_f * kn
+        assert bench.flops(c, P, kn, True) == pair_b * P + key_b * kn
+    c = workloads.config("h128_s8k_bwd")
+    assert round(bench.flops(c, 33_558_528, 8192, True) / 1e12, 3) == 7.697
+    assert round(bench.flops(c, 33_558_528, 8192, False) / 1e12, 3) == 3.024
+    c = workloads.config("h128_varlen64k")
+    assert round(bench.flops(c, 15_619_141, 8638, True) / 1e12, 3) == 3.906
+
+
+def test_kernel_flops_split_the_step_count():
+    """The per-kernel algorithmic counts of bench.kernel_flops add up to the
+    step's count: forward = 2 up-projection launches + attention; backward =
+    dK/dV (S, dP, dV, dK) + dQ (dq) + the latent-gradient GEMM + 2 weight
+    GEMMs; the backward's K/V rebuild launches are not credited."""
+    import workloads
+    c = workloads.config("h128_s16k_shard")
+    P, kn = 31_458_304, 16384
+    kf = lambda n: bench.kernel_flops(n, c, P, kn)[0]  # noqa: E731
+    assert 2 * kf("upproj") + kf("attn_fwd") == bench.flops(c, P, kn, False)
+    for dq in ("attn_bwd_dq", "attn_bwd_dq_ds"):
+        assert kf("attn_bwd_dkdv") + kf(dq) + kf("grad_latent") + 2 * kf("grad_w") == \
+            bench.flops(c, P, kn, True)

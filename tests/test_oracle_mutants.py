@@ -127,3 +127,50 @@ def test_ranges_unmutated_passes():
 @pytest.mark.parametrize("old,new", RANGE_MUTANTS)
 def test_ranges_mutant_caught_by_brute_force(old, new):
     assert ranges_error(mutant(old, new)) > 1e-6
+
+
+def flop_error(mod):
+    """Largest difference between the module's FLOP counts and twice the
+    multiply-adds that the brute-force loops perform (forward products; the
+    backward's products less the K/V rebuild and the row sums D)."""
+    from tests.oracle_brute import MacCounter, brute_backward
+    from tests.test_oracle_pins import BWD_PRODUCTS, FWD_PRODUCTS
+    worst = 0
+    for S, S_loc, q_offset, cu in ((9, 5, 4, None), (12, 7, 5, [0, 3, 3, 4, 9, 12])):
+        x = rand_inputs(n_h=2, d_c=5, d_rope=2, d_nope=3, d_v=4, S=S, S_loc=S_loc, seed=9)
+        L = {k: v.tolist() for k, v in x.items()}
+        dout = np.ones((S_loc, 2, 4)).tolist()
+        fc, bc = MacCounter(), MacCounter()
+        bo, _ = brute_forward(L["q"], L["c_kv"], L["k_rope"], L["W_UK"], L["W_UV"], q_offset, cu,
+                              counter=fc)
+        brute_backward(dout, L["q"], L["c_kv"], L["k_rope"], L["W_UK"], L["W_UV"], bo, q_offset,
+                       cu, counter=bc)
+        cu_a = None if cu is None else np.array(cu, np.int32)
+        args = (2, 5, 2, 3, 4, S_loc, q_offset, cu_a)
+        worst = max(worst, abs(mod.attention_flops(*args) - 2 * sum(fc[k] for k in FWD_PRODUCTS)),
+                    abs(mod.attention_flops(*args, backward=True) - 2 * sum(bc[k] for k in BWD_PRODUCTS)))
+    return worst
+
+
+FLOP_MUTANTS = [
+    # the backward's score recomputation not counted
+    ("return 2 * n_h * (3 * d_qk + 2 * d_v) * P", "return 2 * n_h * (2 * d_qk + 2 * d_v) * P"),
+    # dP or dV dropped
+    ("return 2 * n_h * (3 * d_qk + 2 * d_v) * P", "return 2 * n_h * (3 * d_qk + d_v) * P"),
+    # the backward's up-projection gradients counted once
+    ("+ 4 * n_h * d_c * (d_nope + d_v) * Kn", "+ 2 * n_h * d_c * (d_nope + d_v) * Kn"),
+    # the forward without the up-projection
+    ("return 2 * n_h * (d_qk + d_v) * P + 2 * n_h * d_c * (d_nope + d_v) * Kn",
+     "return 2 * n_h * (d_qk + d_v) * P"),
+    # the forward's value width taken as d_qk
+    ("return 2 * n_h * (d_qk + d_v) * P + 2", "return 2 * n_h * (2 * d_qk) * P + 2"),
+]
+
+
+def test_flops_unmutated_passes():
+    assert flop_error(M) == 0
+
+
+@pytest.mark.parametrize("old,new", FLOP_MUTANTS)
+def test_flop_mutant_caught_by_counted_loops(old, new):
+    assert flop_error(mutant(old, new)) > 0

@@ -26,7 +26,7 @@ import torch
 
 import oracle
 from oracle import mla_oracle as M
-from tests.oracle_brute import brute_forward, brute_visible_pairs
+from tests.oracle_brute import MacCounter, brute_backward, brute_forward, brute_visible_pairs
 
 
 def rand_inputs(n_h=2, d_c=6, d_rope=2, d_nope=3, d_v=4, S=9, S_loc=None, seed=1,
@@ -379,6 +379,52 @@ def test_visible_pairs_shard_closed_form(S_loc, q_off):
                                             (20, 10, [0, 1, 2, 15, 15, 30])])
 def test_visible_pairs_varlen_brute(S_loc, q_off, cu):
     assert oracle.visible_pairs(S_loc, q_off, np.array(cu)) == brute_visible_pairs(S_loc, q_off, cu)
+
+
+# The FLOP count of the block (what the throughput figures divide by) is the
+# multiply-adds of the method's products, two FLOPs each, counted on visible
+# (row, key) pairs only, plus the up-projection of the keys the shard needs.
+# Forward: rebuild K_nope and V, scores, weights times V. Backward: the
+# scores again (counted, as flash attention counts its recomputation), dP,
+# dV, dq, dK, then dc_kv and dW, each over the needed keys; rebuilding K and
+# V for the backward and the row sums D are not counted. The per-product
+# multiply-adds come from running the element-by-element loops of
+# tests/oracle_brute.py, whose values are pinned to the oracle first.
+FLOP_CASES = [
+    (6, 6, 0, None), (9, 5, 4, None), (12, 7, 5, [0, 3, 3, 4, 9, 12]),
+    (10, 4, 6, [0, 1, 7, 10]), (7, 1, 6, None),
+]
+FWD_PRODUCTS = ("rebuild_K", "rebuild_V", "score", "PV")
+BWD_PRODUCTS = ("score", "dP", "dV", "dq", "dK", "dc_kv", "dW")
+
+
+@pytest.mark.parametrize("S,S_loc,q_offset,cu", FLOP_CASES)
+def test_flops_count_the_products_of_brute_force_loops(S, S_loc, q_offset, cu):
+    n_h, d_c, d_rope, d_nope, d_v = 2, 5, 2, 3, 4
+    x = rand_inputs(n_h=n_h, d_c=d_c, d_rope=d_rope, d_nope=d_nope, d_v=d_v, S=S,
+                    S_loc=S_loc, seed=S + S_loc)
+    cu_a = None if cu is None else np.array(cu, np.int32)
+    rng = np.random.default_rng(5)
+    dout = rng.standard_normal((S_loc, n_h, d_v))
+    L = {k: v.tolist() for k, v in x.items()}
+    fc = MacCounter()
+    bo, bl = brute_forward(L["q"], L["c_kv"], L["k_rope"], L["W_UK"], L["W_UV"],
+                           q_offset=q_offset, cu=cu, counter=fc)
+    bc = MacCounter()
+    bg = brute_backward(dout.tolist(), L["q"], L["c_kv"], L["k_rope"], L["W_UK"], L["W_UV"], bo,
+                        q_offset=q_offset, cu=cu, counter=bc)
+    # the loops compute the oracle's values ...
+    o, lse = oracle.mla_forward(**x, q_offset=q_offset, cu_seqlens=cu_a)
+    np.testing.assert_allclose(np.array(bo), o, rtol=1e-11, atol=1e-12)
+    g = oracle.mla_backward(dout, **x, q_offset=q_offset, cu_seqlens=cu_a)
+    for got, ref in zip(bg, g):
+        np.testing.assert_allclose(np.array(got), ref, rtol=1e-10, atol=1e-11)
+    # ... and the FLOP counts are twice their multiply-adds
+    args = (n_h, d_c, d_rope, d_nope, d_v, S_loc, q_offset, cu_a)
+    assert oracle.attention_flops(*args) == 2 * sum(fc[k] for k in FWD_PRODUCTS)
+    assert oracle.attention_flops(*args, backward=True) == 2 * sum(bc[k] for k in BWD_PRODUCTS)
+    assert set(fc) == set(FWD_PRODUCTS)
+    assert set(bc) == set(BWD_PRODUCTS) | {"rebuild_K", "rebuild_V", "D"}
 
 
 def test_flops_headline_shard():
