@@ -72,6 +72,12 @@ def kernel_flops(name, cfg, pairs, kn):
     return table.get(name)
 
 
+# Kernels the fast backward runs on its side stream, next to the main
+# stream's kernels: their event times are wall times while sharing the CUs,
+# not the time they take alone.
+SIDE_STREAM_KERNELS = ("prep_w16", "prep_ckvT", "dout_scale", "bwd_prep", "attn_bwd_dq",
+                       "attn_bwd_dq_ds", "reduce_rope")
+
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")
 # kernel symbol fragment -> (timer name, sources whose text decides its code)
@@ -228,16 +234,63 @@ def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
     return "\n".join(rows)
 
 
-def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
-    """The fp64 oracle, as it stands, on whole heads of the workload (all rows,
-    forward and backward) until about `budget_s` seconds have been spent."""
-    import oracle
+def host_cpu():
+    """Model name of the host CPU (lscpu), and the BLAS library numpy uses
+    with its thread count (threadpoolctl)."""
+    import subprocess
+    info = {"model": None, "logical_cpus": os.cpu_count(), "blas": None, "blas_threads": None}
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            if line.startswith("Model name:"):
+                info["model"] = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = max(p.get("num_threads", 1) for p in blas)
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+        pass
+    return info
+
+
+def cpu_one_core_forward(budget_heads=2):
+    """The oracle's forward on one core for the two small configurations:
+    the tiny fp32 one whole, and `budget_heads` of the 16 heads of the
+    16-head 4096-token one (its rate on those heads)."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+    res = {}
+    with threadpool_limits(limits=1):
+        for name, heads in (("tiny_f32", None), ("h16_s4k", list(range(budget_heads)))):
+            cfg = workloads.config(name)
+            xx = workloads.make_inputs(cfg)
+            args = [xx[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
+            oracle.mla_forward(*args, heads=[0])   # import and first-call costs
+            t0 = time.perf_counter()
+            oracle.mla_forward(*args, heads=heads)
+            dt = time.perf_counter() - t0
+            nh = cfg.n_h if heads is None else len(heads)
+            pairs = oracle.visible_pairs(cfg.S_loc, cfg.q_offset)
+            F = oracle.attention_flops(cfg.n_h, cfg.d_c, cfg.d_rope, cfg.d_nope, cfg.d_v,
+                                       cfg.S_loc, cfg.q_offset) * nh / cfg.n_h
+            res[name] = {"forward_s": round(dt, 4), "heads": nh, "of_heads": cfg.n_h,
+                         "gflops": round(F / dt / 1e9, 3), "visible_pairs_per_head": pairs}
+    return res
+
+
+def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
+    """The fp64 oracle, as it stands, on whole heads of the workload (all rows,
+    forward and backward) until about `budget_s` seconds have been spent; the
+    host's CPU model and BLAS; and one-core forward runs of the two small
+    configurations."""
+    import oracle
+    host = host_cpu()
+    threads = host["blas_threads"] or os.cpu_count() or 1
     args = [x[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
     heads = 0
     t0 = time.perf_counter()
@@ -250,10 +303,16 @@ def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
         heads += 1
     dt = time.perf_counter() - t0
     F = (flops(cfg, pairs, kn, False) + flops(cfg, pairs, kn, True)) * heads / cfg.n_h
-    return {"value": round(F / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle, forward+backward of heads 0..{heads - 1} of {cfg.n_h} "
-                      f"(all {cfg.S_loc} rows), {dt:.1f} s"}
+    res = {"value": round(F / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"fp64 numpy oracle, forward+backward of heads 0..{heads - 1} of {cfg.n_h} "
+                     f"(all {cfg.S_loc} rows), {dt:.1f} s",
+           "host": host}
+    try:
+        res["one_core_forward"] = cpu_one_core_forward()
+    except Exception as e:  # noqa: BLE001
+        res["one_core_forward"] = {"error": str(e)}
+    return res
 
 
 def memory_report(name):
@@ -307,7 +366,7 @@ def memory_report(name):
     for recompute in (False, True):
         def bwd_call():
             c = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, q_ranges=cfg.q_ranges,
-                            backward=True, recompute_dq=recompute)
+                            backward=True, stored_ds=not recompute)
             g = c.bwd(dev["dout"], *a, out, lse)
             return c, g
         (c, g), peak = peak_of(bwd_call)
@@ -561,7 +620,7 @@ def main():
             dev[k] = torch.from_numpy(x[k]).cuda()
     a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
     call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True,
-                       q_ranges=cfg.q_ranges)
+                       q_ranges=cfg.q_ranges)   # the default backward (dQ recomputes)
     pairs, k_lo, k_hi = hla.mla_laga_count(call.desc, call.cu)
     kn = k_hi - k_lo
     F_fwd, F_bwd = flops(cfg, pairs, kn, False), flops(cfg, pairs, kn, True)
@@ -665,6 +724,61 @@ def main():
         del flush
 
     med = lambda v: float(np.median(v))  # noqa: E731
+    for name, k in kern.items():
+        if name in SIDE_STREAM_KERNELS:
+            k["stream"] = "side (wall time while sharing the CUs)"
+
+    # The two backward forms. The default recomputes the scores and dP for
+    # dQ; the stored-dS form (opt-in) keeps dS in the workspace, which grows
+    # with rows x keys. Each form's backward is timed on its own call, and its
+    # allocator peak (workspace and gradients of a fresh call) is measured.
+    def bwd_peak(stored):
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        c = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True,
+                        q_ranges=cfg.q_ranges, stored_ds=stored)
+        g = c.bwd(dev["dout"], *a, out, lse)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - before
+        ws = c.ws_bwd.numel()
+        del c, g
+        torch.cuda.empty_cache()
+        return peak, ws
+
+    forms = {}
+    for stored in (False, True):
+        peak, ws = bwd_peak(stored)
+        entry = {"workspace_bytes": ws, "backward_peak_bytes": peak}
+        if not stored:
+            entry.update({"default": True, "bwd_ms_median": round(med(bwd_ms), 4),
+                          "step_ms": round(step_ms, 4)})
+        else:
+            cs = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True,
+                             q_ranges=cfg.q_ranges, stored_ds=True)
+            gs = cs.bwd(dev["dout"], *a, out, lse)
+            for _ in range(2):
+                cs.bwd(dev["dout"], *a, out, lse, grads=gs)
+            n_s = max(3, min(10, args.steps))
+            sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True)) for _ in range(n_s)]
+            torch.cuda.synchronize()
+            for e0, e1, e2 in sev:
+                e0.record(stream)
+                cs.fwd(*a, out=out, lse=lse)
+                e1.record(stream)
+                cs.bwd(dev["dout"], *a, out, lse, grads=gs)
+                e2.record(stream)
+            torch.cuda.synchronize()
+            sb = [e1.elapsed_time(e2) for _, e1, e2 in sev]
+            ss = [e0.elapsed_time(e2) for e0, _, e2 in sev]
+            entry.update({"default": False, "bwd_ms_median": round(med(sb), 4),
+                          "step_ms": round(med(ss), 4), "steps": n_s,
+                          "step_tflops": round((F_fwd + F_bwd) / (med(ss) / 1e3) / 1e12, 2)})
+            del cs, gs
+            torch.cuda.empty_cache()
+        forms["stored_ds" if stored else "recompute_dq"] = entry
+
     value = (F_fwd + F_bwd) / (step_ms / 1e3) / 1e12
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -684,6 +798,7 @@ def main():
         "bwd": {**spread(bwd_ms), "tflops": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12, 2),
                 "frac_peak": round(F_bwd / (med(bwd_ms) / 1e3) / 1e12 / PEAK_TFLOPS, 4)},
         "step_events": spread([f + b for f, b in zip(fwd_ms, bwd_ms)]),
+        "bwd_forms": forms,
         "step_cold_caches": cold,
         "device": device_info(torch),
         "roofline": roofline,

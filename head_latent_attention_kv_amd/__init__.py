@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MLAError", "MLADesc", "load_library", "library_path", "mla_laga_fwd", "mla_laga_bwd",
     "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
-    "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC", "MLA_FLAG_RECOMPUTE_DQ",
+    "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC", "MLA_FLAG_STORED_DS",
     "MLA_MAX_RANGES", "MLADecodeDesc", "MLADecodeCall", "mla_laga_decode",
     "mla_laga_decode_workspace_size",
 ]
@@ -27,7 +27,7 @@ __all__ = [
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC = 1
-MLA_FLAG_RECOMPUTE_DQ = 2
+MLA_FLAG_STORED_DS = 4
 MLA_MAX_RANGES = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -154,11 +154,12 @@ def _host_ranges(q_ranges) -> Optional[np.ndarray]:
 
 def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: torch.Tensor,
               q_offset: int = 0, cu_seqlens=None, softmax_scale: Optional[float] = None,
-              generic: bool = False, q_ranges=None, recompute_dq: bool = False
+              generic: bool = False, q_ranges=None, stored_ds: bool = False
               ) -> Tuple[MLADesc, Optional[np.ndarray], Optional[np.ndarray]]:
     """Descriptor plus the host arrays it points at (cu_seqlens, ranges):
-    keep those alive as long as the descriptor is used. recompute_dq sets
-    MLA_FLAG_RECOMPUTE_DQ (dQ without the stored-dS workspace)."""
+    keep those alive as long as the descriptor is used. stored_ds sets
+    MLA_FLAG_STORED_DS (the backward keeps dS in a workspace that grows with
+    rows x keys, and dQ reads it instead of recomputing the scores)."""
     S_loc, n_h, d_qk = q.shape
     S, d_c = c_kv.shape
     d_rope = k_rope.shape[1]
@@ -169,7 +170,7 @@ def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: t
     d.n_seqs = 0 if cu is None else len(cu) - 1
     d.S, d.S_loc, d.q_offset = S, S_loc, int(q_offset)
     d.in_dtype = _in_dtype(q)
-    d.flags = (MLA_FLAG_GENERIC if generic else 0) | (MLA_FLAG_RECOMPUTE_DQ if recompute_dq else 0)
+    d.flags = (MLA_FLAG_GENERIC if generic else 0) | (MLA_FLAG_STORED_DS if stored_ds else 0)
     d.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
     rng = _host_ranges(q_ranges)
     d.n_ranges = 0 if rng is None else len(rng)
@@ -177,11 +178,16 @@ def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: t
     return d, cu, rng
 
 
-def _check_inputs(d: MLADesc, tensors):
-    dt = None
+def _check_inputs(d: MLADesc, tensors, dtype=None):
+    """Every tensor must exist on the device, be contiguous, have its shape
+    and share one dtype (`dtype` when given). The library reads and writes
+    raw pointers, so a wrong shape or dtype here would run off a buffer."""
+    dt = dtype
     for name, t, shape in tensors:
         if t is None:
             raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
@@ -190,7 +196,23 @@ def _check_inputs(d: MLADesc, tensors):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         dt = t.dtype if dt is None else dt
         if t.dtype != dt:
-            raise ValueError(f"{name} is {t.dtype}; all inputs must share one dtype ({dt})")
+            raise ValueError(f"{name} is {t.dtype}, expected {dt}")
+
+
+def _in_torch_dtype(d: MLADesc):
+    return torch.bfloat16 if d.in_dtype == MLA_BF16 else torch.float32
+
+
+def _output_specs(d: MLADesc, out, lse):
+    return [("out", out, (d.S_loc, d.n_h, d.d_v)), ("lse", lse, (d.S_loc, d.n_h))]
+
+
+def _grad_specs(d: MLADesc, grads):
+    if len(grads) != 5:
+        raise ValueError("grads must be (dq, dc_kv, dk_rope, dW_UK, dW_UV)")
+    shapes = [(d.S_loc, d.n_h, d.d_nope + d.d_rope), (d.S, d.d_c), (d.S, d.d_rope),
+              (d.d_c, d.n_h * d.d_nope), (d.d_c, d.n_h * d.d_v)]
+    return list(zip(("dq", "dc_kv", "dk_rope", "dW_UK", "dW_UV"), grads, shapes))
 
 
 def _input_specs(d: MLADesc, q, c_kv, k_rope, W_UK, W_UV):
@@ -258,9 +280,9 @@ class MLACall:
 
     def __init__(self, q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None,
                  softmax_scale: Optional[float] = None, generic: bool = False,
-                 backward: bool = False, q_ranges=None, recompute_dq: bool = False):
+                 backward: bool = False, q_ranges=None, stored_ds: bool = False):
         self.desc, self.cu, self.ranges = make_desc(q, c_kv, k_rope, W_UV, q_offset, cu_seqlens,
-                                                    softmax_scale, generic, q_ranges, recompute_dq)
+                                                    softmax_scale, generic, q_ranges, stored_ds)
         _check_inputs(self.desc, _input_specs(self.desc, q, c_kv, k_rope, W_UK, W_UV))
         self.device = q.device
         self.cu_dev = None if self.cu is None else torch.from_numpy(self.cu).to(self.device)
@@ -272,12 +294,21 @@ class MLACall:
     def fast(self) -> bool:
         return mla_laga_uses_fast_path(self.desc)
 
+    def _check_call(self, q, c_kv, k_rope, W_UK, W_UV):
+        d = self.desc
+        _check_inputs(d, _input_specs(d, q, c_kv, k_rope, W_UK, W_UV), _in_torch_dtype(d))
+        for name, t in (("q", q), ("c_kv", c_kv), ("k_rope", k_rope), ("W_UK", W_UK), ("W_UV", W_UV)):
+            if t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, the call was prepared on {self.device}")
+
     def fwd(self, q, c_kv, k_rope, W_UK, W_UV, out=None, lse=None):
         d = self.desc
+        self._check_call(q, c_kv, k_rope, W_UK, W_UV)
         if out is None:
             out = torch.empty((d.S_loc, d.n_h, d.d_v), dtype=torch.float32, device=self.device)
         if lse is None:
             lse = torch.empty((d.S_loc, d.n_h), dtype=torch.float32, device=self.device)
+        _check_inputs(d, _output_specs(d, out, lse), torch.float32)
         stream = torch.cuda.current_stream(self.device).cuda_stream
         _check(load_library().mla_laga_fwd(
             ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK), _ptr(W_UV),
@@ -287,6 +318,11 @@ class MLACall:
 
     def bwd(self, dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, grads=None):
         d = self.desc
+        self._check_call(q, c_kv, k_rope, W_UK, W_UV)
+        _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))], _in_torch_dtype(d))
+        _check_inputs(d, _output_specs(d, out, lse), torch.float32)
+        if grads is not None:
+            _check_inputs(d, _grad_specs(d, grads), torch.float32)
         if self.ws_bwd is None:
             self.ws_bwd = _workspace(mla_laga_bwd_workspace_size(d, self.cu), self.device)
         f32 = dict(dtype=torch.float32, device=self.device)
@@ -316,14 +352,12 @@ def mla_laga_fwd(q, c_kv, k_rope, W_UK, W_UV, q_offset: int = 0, cu_seqlens=None
 
 def mla_laga_bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse, q_offset: int = 0,
                  cu_seqlens=None, softmax_scale: Optional[float] = None, generic: bool = False,
-                 q_ranges=None, recompute_dq: bool = False):
+                 q_ranges=None, stored_ds: bool = False):
     """(dq, dc_kv, dk_rope, dW_UK, dW_UV), all fp32, gradients of sum(out*dout).
-    recompute_dq: compute dQ without the stored-dS workspace."""
+    stored_ds: keep dS in the workspace for dQ (faster; memory grows with
+    rows x keys)."""
     call = MLACall(q, c_kv, k_rope, W_UK, W_UV, q_offset, cu_seqlens, softmax_scale, generic,
-                   backward=True, q_ranges=q_ranges, recompute_dq=recompute_dq)
-    d = call.desc
-    _check_inputs(d, [("dout", dout, (d.S_loc, d.n_h, d.d_v))] +
-                  _input_specs(d, q, c_kv, k_rope, W_UK, W_UV)[:1])
+                   backward=True, q_ranges=q_ranges, stored_ds=stored_ds)
     return call.bwd(dout, q, c_kv, k_rope, W_UK, W_UV, out, lse)
 
 
@@ -359,20 +393,26 @@ class MLADecodeCall:
                  softmax_scale: Optional[float] = None):
         self.desc, self.cu = make_decode_desc(q, c_kv, k_rope, W_UV, cu_seqlens, softmax_scale)
         d = self.desc
-        _check_inputs(d, [("q", q, (d.batch, d.n_h, d.d_nope + d.d_rope)),
-                          ("c_kv", c_kv, (d.S, d.d_c)), ("k_rope", k_rope, (d.S, d.d_rope)),
-                          ("W_UK", W_UK, (d.d_c, d.n_h * d.d_nope)),
-                          ("W_UV", W_UV, (d.d_c, d.n_h * d.d_v))])
+        _check_inputs(d, self._specs(q, c_kv, k_rope, W_UK, W_UV))
         self.device = q.device
         self.cu_dev = torch.from_numpy(self.cu).to(self.device)
         self.ws = _workspace(mla_laga_decode_workspace_size(d, self.cu), self.device)
 
+    def _specs(self, q, c_kv, k_rope, W_UK, W_UV):
+        d = self.desc
+        return [("q", q, (d.batch, d.n_h, d.d_nope + d.d_rope)),
+                ("c_kv", c_kv, (d.S, d.d_c)), ("k_rope", k_rope, (d.S, d.d_rope)),
+                ("W_UK", W_UK, (d.d_c, d.n_h * d.d_nope)), ("W_UV", W_UV, (d.d_c, d.n_h * d.d_v))]
+
     def __call__(self, q, c_kv, k_rope, W_UK, W_UV, out=None, lse=None):
         d = self.desc
+        _check_inputs(d, self._specs(q, c_kv, k_rope, W_UK, W_UV), _in_torch_dtype(d))
         if out is None:
             out = torch.empty((d.batch, d.n_h, d.d_v), dtype=torch.float32, device=self.device)
         if lse is None:
             lse = torch.empty((d.batch, d.n_h), dtype=torch.float32, device=self.device)
+        _check_inputs(d, [("out", out, (d.batch, d.n_h, d.d_v)), ("lse", lse, (d.batch, d.n_h))],
+                      torch.float32)
         stream = torch.cuda.current_stream(self.device).cuda_stream
         _check(load_library().mla_laga_decode(
             ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK), _ptr(W_UV),

@@ -150,7 +150,7 @@ BwdLayout bwd_layout(const Plan& p) {
     return o;
   };
   L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = L.order = -1;
-  L.dS = -1;
+  L.dS = L.dscale = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
     const int64_t S_pad = align_up(p.S_loc, 64);
@@ -170,6 +170,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
                             gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
     L.order = take(4 * ((p.S_loc + 255) / 256 + p.Kpad / 128));
+    L.dscale = take(16 + 4 * kScaleBlocks);
     if (p.ds_store) L.dS = take(p.n_h * p.Kpad * S_pad * 2);
     L.f.total = -1;
   } else {
@@ -184,11 +185,7 @@ BwdLayout bwd_layout(const Plan& p) {
   return L;
 }
 
-static constexpr bool kFastBuilt = true;
-static constexpr bool kFastBwdBuilt = true;
-
 static bool fast_shape(const mla_laga_desc* d) {
-  if (!kFastBuilt) return false;
   return d->in_dtype == MLA_BF16 && !(d->flags & MLA_FLAG_GENERIC) && d->d_nope == kFastDNope &&
          d->d_v == kFastDV && d->d_rope == kFastDRope && d->d_c % 64 == 0 && d->d_c >= 64 &&
          d->d_c <= 4096;
@@ -208,6 +205,9 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   if (d->S > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "S above 2^31-1");
   if (d->in_dtype != MLA_F32 && d->in_dtype != MLA_BF16)
     return fail(MLA_ERR_INVALID_ARG, "in_dtype must be MLA_F32 or MLA_BF16");
+  if (d->flags & ~(MLA_FLAG_GENERIC | MLA_FLAG_STORED_DS))
+    return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x",
+                static_cast<unsigned>(d->flags & ~(MLA_FLAG_GENERIC | MLA_FLAG_STORED_DS)));
   if (d->n_seqs < 0) return fail(MLA_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (d->n_seqs > 0) {
     if (!cu) return fail(MLA_ERR_INVALID_ARG, "n_seqs > 0 needs cu_seqlens_host");
@@ -259,7 +259,7 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   P.S = d->S; P.S_loc = d->S_loc; P.q_offset = d->q_offset;
   P.bf16 = d->in_dtype == MLA_BF16;
   P.fast = fast_shape(d);
-  P.fast_bwd = P.fast && kFastBwdBuilt;
+  P.fast_bwd = P.fast;
   if (!P.fast_bwd && (P.d_qk > 256 || P.d_v > 256))
     return fail(MLA_ERR_UNSUPPORTED, "plain path takes d_nope+d_rope <= 256 and d_v <= 256");
   P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf(static_cast<float>(P.d_qk));
@@ -274,7 +274,7 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   }
   P.Kn = P.key_hi - P.key_lo;
   P.Kpad = align_up(P.Kn, kKeyTile);
-  P.ds_store = P.fast_bwd && !(d->flags & MLA_FLAG_RECOMPUTE_DQ) &&
+  P.ds_store = P.fast_bwd && (d->flags & MLA_FLAG_STORED_DS) &&
                P.n_h * P.Kpad * align_up(P.S_loc, 64) * 2 <= kMaxStoredDsBytes;
   int64_t pairs = 0;
   for (int64_t i = 0; i < P.S_loc; ++i) {

@@ -3,7 +3,8 @@
 // rebuilt from the latent, so their gradients flow back into c_kv, k_rope,
 // W_UK and W_UV).
 //
-//   prep      D = rowsum(dout * out); q and dout to fp16, per head,
+//   scale     max|dout| -> a power of two 2^e that brings it into [4, 8)
+//   prep      D = rowsum(2^e dout * out); q and 2^e dout to fp16, per head,
 //             row-major [row][dim]
 //   rebuild   K_nope and V again (fp16), in the layouts the kernels read
 //   dK, dV    key-outer, one launch of paired waves: a pair owns 32 keys
@@ -15,6 +16,14 @@
 //             is deterministic.
 //   GEMMs     dc_kv = [dK_nope | dV] [W_UK | W_UV]^T,  dW = c_kv^T [dK_nope | dV]
 //   reduce    dk_rope = sum over heads of the per-head rope-key gradients
+//
+// Every gradient is linear in dout. dout, dP, dS and the [dK_nope | dV] rows
+// are held in fp16, whose normal range starts at 2^-14, while the output
+// gradients of a training step are often far smaller. So dout enters scaled
+// by 2^e (exact: a power of two), every fp16 intermediate carries that
+// factor, and the fp32 results leave multiplied by 2^-e (exact again). The
+// scaled dout has its largest magnitude in [4, 8), the range of a standard
+// normal sample of this size, for any input scale.
 //
 // Query/key tiles are DMA-filled (global_load_lds) into swizzled LDS rows
 // and double-buffered, as in the forward.
@@ -45,19 +54,80 @@ __device__ __forceinline__ void work_item(int bid, int n_h, int n_t, int* h, int
   }
 }
 
+// ------------------------------------------------------------------ dout scale
+// part[b] = bits of the largest |dout| element that block b reads (bf16 bit
+// patterns without the sign; as unsigned integers they order like the
+// magnitudes, and the non-finite ones sit above 0x7f7f). n8 = elements / 8.
+__global__ void __launch_bounds__(256)
+dout_absmax_kernel(const u32x4* __restrict__ x, int64_t n8, uint32_t* __restrict__ part) {
+  __shared__ uint32_t wmax[4];
+  uint32_t m = 0;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n8;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const u32x4 v = x[e];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(v[k] & 0x7fffu, (v[k] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), s, 64)));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+}
+
+// sc[0] = 2^e, sc[1] = 2^-e with 2^e max|dout| in [4, 8): e = 2 - floor(log2
+// max|dout|), read off the bf16 exponent (or, for a subnormal maximum, off
+// its leading mantissa bit), clamped to [-126, 126] so that both factors
+// are normal floats. e = 0 when dout is all zero or holds a non-finite value.
+__global__ void __launch_bounds__(256)
+dout_scale_kernel(const uint32_t* __restrict__ part, int n, float* __restrict__ sc) {
+  __shared__ uint32_t wmax[4];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, part[i]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), s, 64)));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    int e = 0;
+    if (m != 0 && m < 0x7f80u) {
+      const int ex = static_cast<int>(m >> 7);   // biased exponent (sign bit is clear)
+      const int fl = ex > 0 ? ex - 127 : (31 - __clz(static_cast<int>(m & 0x7fu))) - 133;
+      e = min(126, max(-126, 2 - fl));
+    }
+    sc[0] = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    sc[1] = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+  }
+}
+
+// fp16 of 8 bf16 values times s (a power of two: the product is exact)
+__device__ __forceinline__ half8 bf16x8_to_half8_scaled(u32x4 v, float s) {
+  half8 h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = v[k];
+    h[2 * k] = static_cast<_Float16>(__uint_as_float(w << 16) * s);
+    h[2 * k + 1] = static_cast<_Float16>(__uint_as_float(w & 0xffff0000u) * s);
+  }
+  return h;
+}
+
 // ------------------------------------------------------------------ prep
-// grid (ceil(S_loc/64), n_h). D[h][i] = dout[i,h,:] . out[i,h,:]; fp16 copies
-// Qn[h][i][192] and dOn[h][i][128] (rows past S_loc are zero); and per
+// grid (ceil(S_loc/64), n_h), dout scaled by sc[0] = 2^e throughout.
+// D[h][i] = 2^e dout[i,h,:] . out[i,h,:]; fp16 copies Qn[h][i][192] and
+// dOn[h][i][128] (2^e dout; rows past S_loc are zero); and per
 // 32-row block the row info the dK/dV kernels read:
 // info[h][i/32] = {lse*log2(e) [32], D [32], sample start [32], position [32]}
 // (rows past S_loc: start INT32_MAX, position -1, so they see no key).
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                 const float* __restrict__ out, const float* __restrict__ lse,
-                const int32_t* __restrict__ cu, float* __restrict__ D, _Float16* __restrict__ Qn,
-                _Float16* __restrict__ dOn, uint32_t* __restrict__ info, int n_h, int n_seqs,
-                int64_t S_loc, int64_t S_pad, RowMap rm) {
+                const int32_t* __restrict__ cu, const float* __restrict__ sc, float* __restrict__ D,
+                _Float16* __restrict__ Qn, _Float16* __restrict__ dOn, uint32_t* __restrict__ info,
+                int n_h, int n_seqs, int64_t S_loc, int64_t S_pad, RowMap rm) {
   const int h = blockIdx.y;
+  const float dsc = sc[0];
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -67,7 +137,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
     float v = 0.f;
     if (i < S_loc) {
       const int64_t base = (i * n_h + h) * DV + 2 * lane;
-      v = bf16_to_f32(dout[base]) * out[base] + bf16_to_f32(dout[base + 1]) * out[base + 1];
+      v = (bf16_to_f32(dout[base]) * dsc) * out[base] + (bf16_to_f32(dout[base + 1]) * dsc) * out[base + 1];
     }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
@@ -94,8 +164,9 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
       const int64_t i = i0 + row;
       half8 v;
       if (i < S_loc) {
-        v = bf16x8_to_half8(
-            *reinterpret_cast<const u32x4*>(src + (i * n_h + h) * width + ch * 8));
+        v = bf16x8_to_half8_scaled(
+            *reinterpret_cast<const u32x4*>(src + (i * n_h + h) * width + ch * 8),
+            pass == 0 ? 1.f : dsc);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
@@ -510,8 +581,8 @@ __global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                    const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                    const _Float16* __restrict__ Vkm, const int* __restrict__ qorder,
-                   float* __restrict__ dq, int n_h, int S_loc, int S_pad, int key_lo, int Kpad,
-                   int n_qt, float scale, float scale_log2) {
+                   const float* __restrict__ sc, float* __restrict__ dq, int n_h, int S_loc,
+                   int S_pad, int key_lo, int Kpad, int n_qt, float scale, float scale_log2) {
   constexpr int NP = (D_PIECES + 7) / 8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * D_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -555,8 +626,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     if (valid) {
-      df[kk] = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(
-          dout + (static_cast<int64_t>(i) * n_h + h) * DV + 16 * kk + 8 * lh));
+      df[kk] = bf16x8_to_half8_scaled(*reinterpret_cast<const u32x4*>(
+          dout + (static_cast<int64_t>(i) * n_h + h) * DV + 16 * kk + 8 * lh), sc[0]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) df[kk][e] = static_cast<_Float16>(0.f);
@@ -683,13 +754,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __syncthreads();
   }
   if (valid) {
+    // the scores' scale, and 2^-e for the scaled dout (exact)
+    const float osc = scale * sc[1];
     float* dst = dq + (static_cast<int64_t>(i) * n_h + h) * DQK;
 #pragma unroll
     for (int dm = 0; dm < 6; ++dm)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {acc[dm][4 * g] * scale, acc[dm][4 * g + 1] * scale,
-                         acc[dm][4 * g + 2] * scale, acc[dm][4 * g + 3] * scale};
+        const f32x4 v = {acc[dm][4 * g] * osc, acc[dm][4 * g + 1] * osc,
+                         acc[dm][4 * g + 2] * osc, acc[dm][4 * g + 3] * osc};
         *reinterpret_cast<f32x4*>(dst + 32 * dm + 8 * g + 4 * lh) = v;
       }
   }
@@ -723,8 +796,8 @@ __device__ __forceinline__ void wait_vm_lgkm(bool four) {
 __global__ void __launch_bounds__(512)
 attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                       const _Float16* __restrict__ dS, const int* __restrict__ qorder,
-                      float* __restrict__ dq, int n_h, int S_loc, int S_pad, int key_lo, int Kpad,
-                      int n_qt, float scale) {
+                      const float* __restrict__ sc, float* __restrict__ dq, int n_h, int S_loc,
+                      int S_pad, int key_lo, int Kpad, int n_qt, float scale) {
   __shared__ __attribute__((aligned(1024))) char smem[E_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -871,22 +944,27 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
     dst_ = dst_ == 2 ? 0 : dst_ + 1;
   }
   if (valid) {
+    // the scores' scale, and 2^-e for the scaled dout (exact)
+    const float osc = scale * sc[1];
     float* dst = dq + (static_cast<int64_t>(i) * n_h + h) * DQK;
 #pragma unroll
     for (int dm = 0; dm < 6; ++dm)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {acc[dm][4 * g] * scale, acc[dm][4 * g + 1] * scale,
-                         acc[dm][4 * g + 2] * scale, acc[dm][4 * g + 3] * scale};
+        const f32x4 v = {acc[dm][4 * g] * osc, acc[dm][4 * g + 1] * osc,
+                         acc[dm][4 * g + 2] * osc, acc[dm][4 * g + 3] * osc};
         *reinterpret_cast<f32x4*>(dst + 32 * dm + 8 * g + 4 * lh) = v;
       }
   }
 }
 
-// dk_rope[key_lo + t][r] = sum_h dKr[h][t][r] for t < Kn; other rows 0.
+// dk_rope[key_lo + t][r] = sc[1] sum_h dKr[h][t][r] for t < Kn (sc[1] = 2^-e
+// undoes the dout scale); other rows 0.
 __global__ void __launch_bounds__(256)
-reduce_rope_kernel(const float* __restrict__ dKr, float* __restrict__ dk_rope, int n_h,
-                   int64_t S, int64_t key_lo, int64_t Kn, int64_t Kpad) {
+reduce_rope_kernel(const float* __restrict__ dKr, const float* __restrict__ sc,
+                   float* __restrict__ dk_rope, int n_h, int64_t S, int64_t key_lo, int64_t Kn,
+                   int64_t Kpad) {
+  const float inv = sc[1];
   const int64_t n = S * 64;
   for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -894,7 +972,7 @@ reduce_rope_kernel(const float* __restrict__ dKr, float* __restrict__ dk_rope, i
     float acc = 0.f;
     if (t >= 0 && t < Kn)
       for (int h = 0; h < n_h; ++h) acc += dKr[(static_cast<int64_t>(h) * Kpad + t) * 64 + r];
-    dk_rope[e] = acc;
+    dk_rope[e] = acc * inv;
   }
 }
 
@@ -904,6 +982,34 @@ zero_rows_kernel(float* __restrict__ p, int64_t n) {
        e += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[e] = 0.f;
 }
+
+// The side stream's fork, joined back into the caller's stream on every way
+// out of the launcher once it has happened: an error return after the fork
+// must not leave work on the side stream unordered with the caller's later
+// work (or leave a graph capture with a stream that never rejoins it).
+class SideFork {
+ public:
+  SideFork(const SideStream& s, hipStream_t main) : s_(s), main_(main) {}
+  ~SideFork() {
+    if (forked_) (void)side_join(s_, main_);
+  }
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+  mla_status fork() {
+    const mla_status r = side_fork(s_, main_);
+    forked_ = r == MLA_OK;
+    return r;
+  }
+  mla_status join() {
+    forked_ = false;
+    return side_join(s_, main_);
+  }
+
+ private:
+  SideStream s_;
+  hipStream_t main_;
+  bool forked_ = false;
+};
 
 unsigned grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
@@ -921,6 +1027,10 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   if (p.Kpad * 256 >= (int64_t(1) << 31) || p.S_loc * DQK >= (int64_t(1) << 31) ||
       p.S + 256 >= (int64_t(1) << 31))
     return fail(MLA_ERR_UNSUPPORTED, "fast backward takes fewer than 2^23 rows per call");
+  // the GEMMs' operand rows (2 n_h 128 and Kpad elements) stay below 2^22
+  // elements: checked here, so that no launcher fails after work is enqueued
+  if (static_cast<int64_t>(p.n_h) * 256 >= (int64_t(1) << 22) || p.Kpad >= (int64_t(1) << 22))
+    return fail(MLA_ERR_UNSUPPORTED, "fast backward takes n_h < 16384 and fewer than 2^22 keys");
   const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
   const int64_t S_pad = align_up(p.S_loc, 64);
   auto at = [&](int64_t off) { return ws + off; };
@@ -938,6 +1048,9 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   uint32_t* info = reinterpret_cast<uint32_t*>(at(L.info));
   // stored dS: the dK/dV kernel writes it, the dQ kernel reads it
   _Float16* dS = p.ds_store ? reinterpret_cast<_Float16*>(at(L.dS)) : nullptr;
+  // {2^e, 2^-e}: the dout scale and its inverse; then the per-block maxima
+  float* dsc = reinterpret_cast<float*>(at(L.dscale));
+  uint32_t* dmax = reinterpret_cast<uint32_t*>(at(L.dscale) + 16);
   const int S_loc = static_cast<int>(p.S_loc), Sp = static_cast<int>(S_pad),
             key_lo = static_cast<int>(p.key_lo),
             Kpad = static_cast<int>(p.Kpad);
@@ -949,7 +1062,8 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   SideStream side;
   if ((s = side_stream(&side)) != MLA_OK) return s;
   const hipStream_t st2 = side.st;
-  if ((s = side_fork(side, st)) != MLA_OK) return s;
+  SideFork fork(side, st);
+  if ((s = fork.fork()) != MLA_OK) return s;
 
   // [W_UK | W_UV] rows in fp16 and c_kv^T in fp16 for the gradient GEMMs
   if ((s = launch_convert(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, W16, 2 * nk,
@@ -962,17 +1076,27 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                             p.Kpad, p.d_c, ckvT, p.Kpad, 0, Elem::F16, 1, st2, "prep_ckvT")) != MLA_OK)
     return s;
   {
+    // the dout scale (every kernel that reads dout or its products waits for it)
+    KernelTimer kt("dout_scale", st2);
+    const int64_t n8 = p.S_loc * p.n_h * DV / 8;
+    const unsigned nb = static_cast<unsigned>(std::min<int64_t>(kScaleBlocks, (n8 + 255) / 256));
+    hipLaunchKernelGGL(dout_absmax_kernel, dim3(nb), dim3(256), 0, st2,
+                       static_cast<const u32x4*>(dout), n8, dmax);
+    hipLaunchKernelGGL(dout_scale_kernel, dim3(1), dim3(256), 0, st2, dmax, static_cast<int>(nb), dsc);
+  }
+  if ((s = check_launch("dout scale")) != MLA_OK) return s;
+  {
     KernelTimer kt("bwd_prep", st2);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(S_pad / 64), p.n_h), dim3(256),
                        0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       out, lse, cu_dev, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
+                       out, lse, cu_dev, dsc, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
                        S_pad, p.rm);
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   // keys (row-major, with the rope key) and V key-major
   if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, nullptr, Vkm, st)) != MLA_OK)
     return s;
-  if ((s = side_join(side, st)) != MLA_OK) return s;
+  if ((s = fork.join()) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;
   // packed calls: query and key tiles in longest-processing-time order
   int *qorder = nullptr, *korder = nullptr;
@@ -994,25 +1118,25 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                        p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
-  if ((s = side_fork(side, st)) != MLA_OK) return s;
+  if ((s = fork.fork()) != MLA_OK) return s;
   {
     const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
     KernelTimer kt(dS != nullptr ? "attn_bwd_dq_ds" : "attn_bwd_dq", st2);
     if (dS != nullptr)
       hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
-                         0, st2, info, Kfull, dS, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
-                         p.scale);
+                         0, st2, info, Kfull, dS, qorder, dsc, dq, p.n_h, S_loc, Sp, key_lo, Kpad,
+                         n_qt, p.scale);
     else
       hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                          0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                         info, Kfull, Vkm, qorder, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt, p.scale,
-                         scale_log2);
+                         info, Kfull, Vkm, qorder, dsc, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
+                         p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
   {
     KernelTimer kt("reduce_rope", st2);
     hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st2, dKr,
-                       dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
+                       dsc, dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
   }
   if ((s = check_launch("rope-key gradient reduce")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0
@@ -1021,7 +1145,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                                        gemm_splitk_bytes(p.d_c, nk, p.Kpad));
   if ((s = launch_gemm_nt(dKV, 2 * nk, p.Kn, W16, 2 * nk, p.d_c, 2 * nk, dc_kv + p.key_lo * p.d_c,
                           p.d_c, 128 * p.d_c, 128, p.Kn, p.d_c, Elem::F16, Elem::F32, st,
-                          "grad_latent", gpart, gpart_bytes)) != MLA_OK)
+                          "grad_latent", gpart, gpart_bytes, dsc + 1)) != MLA_OK)
     return s;
   {
     KernelTimer kt("zero_rows", st);
@@ -1035,14 +1159,14 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   if ((s = check_launch("zero rows")) != MLA_OK) return s;
   // dW_UK = c_kv^T dK_nope, dW_UV = c_kv^T dV (contract over the shard's keys)
   if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT, p.Kpad, nk, p.Kpad, dW_UK, nk, 128 * nk, 128,
-                          p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart, gpart_bytes)) != MLA_OK)
+                          p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart, gpart_bytes,
+                          dsc + 1)) != MLA_OK)
     return s;
   if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT + nk * p.Kpad, p.Kpad, nk, p.Kpad, dW_UV, nk,
                           128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart,
-                          gpart_bytes)) != MLA_OK)
+                          gpart_bytes, dsc + 1)) != MLA_OK)
     return s;
-  if ((s = side_join(side, st)) != MLA_OK) return s;
-  return MLA_OK;
+  return fork.join();
 }
 
 }  // namespace mla

@@ -7,8 +7,8 @@
 //      converted to fp16;
 //   2. K_nope = c_kv W_UK_h is written key-major [h][key][128] and V
 //      d-major [h][128][key], both fp16, for the keys this shard needs;
-//   3. attention: each workgroup owns 256 query rows of one head (4 waves x
-//      64 rows); 64-key K and V^T tiles go straight from memory into LDS
+//   3. attention: each workgroup owns 256 query rows of one head (8 waves x
+//      32 rows, two waves per SIMD); 64-key K and V^T tiles go straight from memory into LDS
 //      (global_load_lds, double-buffered, the next tile in flight while the
 //      current one is used). Each wave computes S^T = K Q^T so
 //      a lane owns one query column: the row max and sum stay in the lane,
@@ -350,6 +350,10 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   const FwdLayout L = fwd_layout(p);
   if (p.Kpad * 192 >= (int64_t(1) << 31) || p.S + 256 >= (int64_t(1) << 31))
     return fail(MLA_ERR_UNSUPPORTED, "fast path takes fewer than 2^23 latent rows per call");
+  // the up-projection GEMM's operand rows (n_h 128 and Kpad elements) stay
+  // below 2^22 elements: checked before anything is enqueued
+  if (static_cast<int64_t>(p.n_h) * 128 >= (int64_t(1) << 22) || p.Kpad >= (int64_t(1) << 22))
+    return fail(MLA_ERR_UNSUPPORTED, "fast forward takes n_h < 32768 and fewer than 2^22 keys");
   uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.WT);
   _Float16* Kfull = reinterpret_cast<_Float16*>(ws + L.Kfull);
   _Float16* Vt = reinterpret_cast<_Float16*>(ws + L.Vt);

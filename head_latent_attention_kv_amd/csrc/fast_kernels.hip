@@ -4,9 +4,9 @@
 // gathered latent) and the backward's latent and weight gradients are all
 // plain GEMMs with K = d_c, n_h*(d_nope+d_v) or the key count. One kernel
 // covers them: both operands are read k-contiguous (so a lane's 8 k-values
-// are one 16-byte LDS read), 256x256 output tiles over four waves of
-// 128x128, and the result is staged through LDS so every global store is a
-// full 16-byte row piece. Thin outputs (the gradients of c_kv and of the
+// are one 16-byte LDS read), 256x256 output tiles over eight waves of
+// 128x64, and an fp16 result is staged through LDS so every global store is
+// a full 16-byte row piece. Thin outputs (the gradients of c_kv and of the
 // weights) split K over more workgroups and sum the fp32 partials in a fixed
 // order afterwards.
 #include <stdlib.h>
@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kW * 64)
 gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __restrict__ Y,
                int64_t ldy, int64_t C, int64_t k_len, OutT* __restrict__ out, int64_t ldo,
                int64_t rt_stride, int64_t ct_stride, int64_t R_store, int64_t C_store,
-               float* __restrict__ part, int n_tr, int n_tc) {
+               float* __restrict__ part, const float* __restrict__ alpha, int n_tr, int n_tc) {
   typedef typename MfmaOp<InT>::vec vec;
   // kW = 4 (four waves of 128x128) also indexes correctly but measured slower;
   // only the eight-wave form is built.
@@ -219,6 +219,8 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   };
   if constexpr (sizeof(OutT) == 4 || kPart) {
     const int64_t PR = static_cast<int64_t>(n_tr) * GT, PC = static_cast<int64_t>(n_tc) * GT;
+    // fp32 results times *alpha when given (split-K: in the reduction)
+    const float am = !kPart && alpha != nullptr ? alpha[0] : 1.f;
     auto put = [&](bool masked) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
@@ -227,7 +229,7 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int rt = wr * 128 + 32 * j + lr, ct = wc * 32 * NI + 32 * i + 8 * g + 4 * lh;
-            const f32x4 v = tile_val(i, j, g, rt, ct, masked);
+            const f32x4 v = tile_val(i, j, g, rt, ct, masked) * am;
             const int64_t r = r0 + rt, c = c0 + ct;
             if constexpr (kPart) {
               __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(part + (blockIdx.y * PR + r) * PC + c));
@@ -319,19 +321,23 @@ tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, RowMap 
     }
 }
 
-// out(r, c) = sum_z part[z][r][c] for r < R_store, c < C_store (0 past R or
-// C), in the tiled layout of launch_gemm_nt; four columns per thread, the
-// splits summed in order (deterministic).
+// out(r, c) = alpha sum_z part[z][r][c] for r < R_store, c < C_store (0 past
+// R or C), in the tiled layout of launch_gemm_nt; four columns per thread,
+// the splits summed in order (deterministic). alpha = *alpha_p, or 1 when
+// alpha_p is null.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t PR, int64_t PC,
                      float* __restrict__ out, int64_t ldo, int64_t rt_stride, int64_t ct_stride,
-                     int64_t R, int64_t C, int64_t R_store, int64_t C_store) {
+                     int64_t R, int64_t C, int64_t R_store, int64_t C_store,
+                     const float* __restrict__ alpha_p) {
+  const float alpha = alpha_p != nullptr ? alpha_p[0] : 1.f;
   const int64_t cq = C_store / 4, n = R_store * cq;
   for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t r = e / cq, c = (e % cq) * 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(part + (z * PR + r) * PC + c);
+    acc *= alpha;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (r >= R || c + q >= C) acc[q] = 0.f;
@@ -492,7 +498,7 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
                           int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
                           int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
                           Elem out_t, hipStream_t st, const char* name, float* part,
-                          int64_t part_bytes) {
+                          int64_t part_bytes, const float* alpha) {
   if (K % GK != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: K=%lld not a multiple of 32", name, (long long)K);
   if (C_store % 8 != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: C_store not a multiple of 8", name);
   const int64_t n_tr = (R_store + GT - 1) / GT, n_tc = (C_store + GT - 1) / GT;
@@ -513,22 +519,22 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
     hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
                        C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
-                       C_store, nullptr, ntr, ntc);
+                       C_store, nullptr, nullptr, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F32 && sp == 1)
     hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store,
-                       C_store, nullptr, ntr, ntc);
+                       C_store, nullptr, alpha, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F32)
     hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<float*>(nullptr), ldo, rt_stride, ct_stride,
-                       R_store, C_store, pp, ntr, ntc);
+                       R_store, C_store, pp, nullptr, ntr, ntc);
   else if (in_t == Elem::F16 && out_t == Elem::F16 && sp == 1)
     hipLaunchKernelGGL((gemm_nt_kernel<_Float16, _Float16, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
                        ldy, C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,
-                       C_store, nullptr, ntr, ntc);
+                       C_store, nullptr, nullptr, ntr, ntc);
   else
     return fail(MLA_ERR_UNSUPPORTED, "%s: GEMM type combination not built", name);
   if (sp > 1) {
@@ -536,7 +542,7 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
     const unsigned g = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 16384));
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(g), dim3(256), 0, st, part, sp, n_tr * GT,
                        n_tc * GT, static_cast<float*>(out), ldo, rt_stride, ct_stride, R, C,
-                       R_store, C_store);
+                       R_store, C_store, alpha);
   }
   return check_launch(name);
 }

@@ -61,11 +61,16 @@ struct BwdLayout {
   // fast path with stored dS: fp16 [n_h][Kpad / 128][S_pad / 32] blocks of 8 KiB
   // ([4 pairs of 32 keys][2 row halves][64 lanes] x 16 bytes, written by dK/dV)
   int64_t dS;
+  // fast path: dout scale {2^e, 2^-e} (fp32), then the per-block maxima of
+  // |dout| it is chosen from (kScaleBlocks uint32)
+  int64_t dscale;
   int64_t total;
 };
 
 // Largest stored-dS buffer the fast backward uses (bytes).
 constexpr int64_t kMaxStoredDsBytes = int64_t(32) << 30;
+// Workgroups of the fast backward's max|dout| reduction.
+constexpr int kScaleBlocks = 1024;
 
 // Decode (absorbed form over the latent cache): one query per sequence.
 struct DecodePlan {

@@ -52,6 +52,20 @@
  *     64 (512 in DeepSeek-V3), any n_h; it keeps the rebuilt K/V and the
  *     softmax weights in fp16 with fp32 accumulation. Every other shape (and
  *     MLA_F32) runs a plain fp32 path of simple kernels.
+ *   - fp16 ranges of the fast path (normal range 2^-14 .. 65504; below it
+ *     values keep an absolute precision of 2^-24, above it they overflow):
+ *       forward: q (both parts), k_rope and the rebuilt K_nope = c_kv W_UK
+ *       and V = c_kv W_UV are taken in fp16 as they are, so their magnitudes
+ *       must stay below 65504, and elements below 2^-14 lose relative
+ *       precision (they matter only against larger elements of the same dot
+ *       product). Softmax weights are at most 256 by construction.
+ *       backward: dout is first multiplied by a power of two 2^e that brings
+ *       max|dout| into [4, 8) (exact), so the gradients do not depend on the
+ *       scale of dout: dout scaled by any power of two gives gradients
+ *       scaled by the same power, bit for bit. dP, dS and the per-key rows
+ *       [dK_nope | dV] carry the factor in fp16, so |dV[key]| <= 8 * (the
+ *       key's total softmax weight over the shard's rows) must stay below
+ *       65504; the fp32 gradients are multiplied back by 2^-e.
  */
 #ifndef MLA_LAGA_H
 #define MLA_LAGA_H
@@ -75,13 +89,18 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 /* Force the plain fp32 path even where the fast path applies. */
 #define MLA_FLAG_GENERIC 1
-/* Fast backward: compute dQ by recomputing the scores and dP per query tile
- * instead of reading dS back from the workspace. The stored-dS form needs
- * n_h * Kpad * S_pad * 2 bytes more workspace (Kpad = needed keys rounded up
- * to 256, S_pad = S_loc rounded up to 64; 8.6 GB at n_h = 128, 16384 keys,
- * 2048 rows) and is used unless this flag is set or that buffer would pass
- * 32 GiB. Both give the same gradients up to fp16 rounding order. */
-#define MLA_FLAG_RECOMPUTE_DQ 2
+/* Fast backward, opt-in: the dK/dV kernel keeps dS = P (dP - D) (fp16) in the
+ * workspace and dQ is computed from it, instead of recomputing the scores
+ * and dP per query tile (the default). Faster, but the workspace then holds
+ * one fp16 value per (local row, needed key, head): n_h * Kpad * S_pad * 2
+ * bytes more (Kpad = needed keys rounded up to 256, S_pad = S_loc rounded up
+ * to 64; 8.6 GB at n_h = 128, 16384 keys, 2048 rows), which grows with the
+ * product of the shard's rows and keys. Ignored (dQ recomputes) when that
+ * buffer would pass 32 GiB. Both forms give the same gradients up to fp16
+ * rounding order. */
+#define MLA_FLAG_STORED_DS 4
+/* The flag value 2 is not used; any flag bit other than these two is
+ * rejected with MLA_ERR_INVALID_ARG. */
 
 /* Most position blocks one shard may hold (mla_laga_desc.n_ranges). */
 #define MLA_MAX_RANGES 16

@@ -160,22 +160,44 @@ def test_workspace_linear_in_rows_and_heads():
     assert h2 - h1 == h3 - h2 and h2 > h1
 
 
-def test_stored_ds_workspace():
-    """The fast backward keeps dS (fp16, n_h x Kpad x S_pad) unless
-    MLA_FLAG_RECOMPUTE_DQ is set or that buffer would pass 32 GiB."""
+def test_default_backward_workspace_has_no_rows_times_keys_term():
+    """The default backward recomputes the scores for dQ, so its workspace is
+    a sum of per-row and per-key terms: the mixed second difference over
+    (rows, keys) vanishes. With MLA_FLAG_STORED_DS it holds dS (fp16,
+    n_h x Kpad x S_pad) as well, exactly the rows x keys term, unless that
+    buffer would pass 32 GiB."""
     base = workloads.config("h128_s16k_shard")
+
+    def ws(S_loc, S, flags=0):
+        d, cu = desc_for(base.with_(S=S, S_loc=S_loc, q_offset=S - S_loc))
+        d.flags = flags
+        return hla.mla_laga_bwd_workspace_size(d, cu)
+
+    for flags, term in ((0, 0), (hla.MLA_FLAG_STORED_DS, 128 * 8192 * 1024 * 2)):
+        mixed = ws(2048, 16384, flags) - ws(1024, 16384, flags) - ws(2048, 8192, flags) \
+            + ws(1024, 8192, flags)
+        assert mixed == term, (flags, mixed)
     d, cu = desc_for(base)
-    with_ds = hla.mla_laga_bwd_workspace_size(d, cu)
-    d.flags = hla.MLA_FLAG_RECOMPUTE_DQ
-    without = hla.mla_laga_bwd_workspace_size(d, cu)
+    default = hla.mla_laga_bwd_workspace_size(d, cu)
+    d.flags = hla.MLA_FLAG_STORED_DS
     # Kpad = 16384 keys, S_pad = 2048 rows
-    assert with_ds - without == 128 * 16384 * 2048 * 2
-    # a shape whose dS would need more than 32 GiB falls back by itself
+    assert hla.mla_laga_bwd_workspace_size(d, cu) - default == 128 * 16384 * 2048 * 2
+    # a shape whose dS would need more than 32 GiB recomputes dQ by itself
     big = base.with_(S=131072, S_loc=8192, q_offset=131072 - 8192)
     d, cu = desc_for(big)
     auto = hla.mla_laga_bwd_workspace_size(d, cu)
-    d.flags = hla.MLA_FLAG_RECOMPUTE_DQ
+    d.flags = hla.MLA_FLAG_STORED_DS
     assert hla.mla_laga_bwd_workspace_size(d, cu) == auto
+
+
+def test_unknown_flags_rejected():
+    d, cu = desc_for(workloads.config("h16_s4k"))
+    for f in (2, 8, 1 << 30):
+        d.flags = f
+        with pytest.raises(hla.MLAError) as e:
+            hla.mla_laga_fwd_workspace_size(d, cu)
+        assert e.value.status == hla.MLA_ERR_INVALID_ARG
+        assert "flag" in str(e.value)
 
 
 def bad(status, fn, *args):

@@ -74,13 +74,13 @@ SMALL = [
 ]
 
 
-def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None, recompute_dq=False):
+def run(cfg, x, cu=None, generic=False, backward=False, dout_override=None, stored_ds=False):
     dev = to_device(x, cfg)
     if dout_override is not None:
         dev["dout"] = dout_override
     call = hla.MLACall(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"],
                        q_offset=cfg.q_offset, cu_seqlens=cu, generic=generic, backward=backward,
-                       q_ranges=cfg.q_ranges, recompute_dq=recompute_dq)
+                       q_ranges=cfg.q_ranges, stored_ds=stored_ds)
     out, lse = call.fwd(dev["q"], dev["c_kv"], dev["k_rope"], dev["W_UK"], dev["W_UV"])
     res = {"out": out, "lse": lse, "fast": call.fast}
     if backward:
@@ -95,14 +95,15 @@ def oracle_args(x):
     return [x[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
 
 
-# default: the fast path with dQ read from the stored dS; recompute_dq: the
-# fast path with dQ recomputing S and dP; plain: the fp32 path
-@pytest.mark.parametrize("path", ["default", "recompute_dq", "plain"])
+# default: the fast path with dQ recomputing S and dP; stored_ds: the fast
+# path with dQ read from the stored dS; plain: the fp32 path
+@pytest.mark.parametrize("path", ["default", "stored_ds", "plain"])
 @pytest.mark.parametrize("cfg,cu", SMALL, ids=[c.name for c, _ in SMALL])
 def test_small_fwd_bwd_elementwise(cfg, cu, path):
     announce(f"small {cfg.name} path={path} n_h={cfg.n_h} S={cfg.S} S_loc={cfg.S_loc} q_off={cfg.q_offset}")
     x = workloads.make_inputs(cfg, with_dout=True)
-    g = run(cfg, x, cu, generic=path == "plain", backward=True, recompute_dq=path == "recompute_dq")
+    g = run(cfg, x, cu, generic=path == "plain", backward=True, stored_ds=path == "stored_ds")
+    assert g["fast"] == (path != "plain")
     ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, **positions(cfg))
     check("out", g["out"], ro)
     check("lse", g["lse"], rl)
@@ -263,9 +264,9 @@ def test_full_size_dq_paths_agree(name):
     x = workloads.make_inputs(cfg, with_dout=True)
     rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, heads=heads,
                              **positions(cfg))
-    for recompute in (False, True):
-        announce(f"{name} dq, recompute_dq={recompute}, heads {heads}")
-        g = run(cfg, x, cu, backward=True, recompute_dq=recompute)
+    for stored in (False, True):
+        announce(f"{name} dq, stored_ds={stored}, heads {heads}")
+        g = run(cfg, x, cu, backward=True, stored_ds=stored)
         check("dq", g["dq"][:, heads], rg[0][:, heads])
 
 
