@@ -21,7 +21,7 @@ __all__ = [
     "mla_laga_fwd_workspace_size", "mla_laga_bwd_workspace_size", "mla_laga_count",
     "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC", "MLA_FLAG_STORED_DS",
     "MLA_MAX_RANGES", "MLADecodeDesc", "MLADecodeCall", "mla_laga_decode",
-    "mla_laga_decode_workspace_size",
+    "mla_laga_decode_workspace_size", "mla_laga_decode_noalloc", "MLA_DECODE_NOALLOC_MAX_BYTES",
 ]
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
@@ -29,6 +29,7 @@ MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC = 1
 MLA_FLAG_STORED_DS = 4
 MLA_MAX_RANGES = 16
+MLA_DECODE_NOALLOC_MAX_BYTES = 256 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -81,6 +82,7 @@ EXPORTED = {
     "mla_laga_decode_workspace_size": (ctypes.c_int, [_DDESCP, _I32P, ctypes.POINTER(ctypes.c_size_t)]),
     "mla_laga_decode": (ctypes.c_int, [_DDESCP, _P, _P, _P, _P, _P, _I32P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+    "mla_laga_decode_noalloc": (ctypes.c_int, [_DDESCP, _P, _P, _P, _P, _P, _I32P, _P, _P, _P, _P]),
     "mla_laga_uses_fast_path": (ctypes.c_int, [_DESCP]),
     "mla_laga_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "mla_laga_timing_select": (ctypes.c_int, [ctypes.c_char_p]),
@@ -419,6 +421,27 @@ class MLADecodeCall:
             _cu_ptr(self.cu), _ptr(self.cu_dev), _ptr(out), _ptr(lse), _ptr(self.ws),
             self.ws.numel(), ctypes.c_void_p(stream)))
         return out, lse
+
+
+def mla_laga_decode_noalloc(q, c_kv, k_rope, W_UK, W_UV, cu_seqlens, cu_seqlens_dev, out, lse,
+                            softmax_scale: Optional[float] = None):
+    """The decode into the caller's out [batch,n_h,d_v] and lse [batch,n_h]
+    (fp32) with the library's static scratch instead of a workspace: the
+    library allocates nothing. cu_seqlens (host) and cu_seqlens_dev (an int32
+    device tensor) hold the same batch+1 values."""
+    d, cu = make_decode_desc(q, c_kv, k_rope, W_UV, cu_seqlens, softmax_scale)
+    _check_inputs(d, [("q", q, (d.batch, d.n_h, d.d_nope + d.d_rope)),
+                      ("c_kv", c_kv, (d.S, d.d_c)), ("k_rope", k_rope, (d.S, d.d_rope)),
+                      ("W_UK", W_UK, (d.d_c, d.n_h * d.d_nope)),
+                      ("W_UV", W_UV, (d.d_c, d.n_h * d.d_v))], _in_torch_dtype(d))
+    _check_inputs(d, [("out", out, (d.batch, d.n_h, d.d_v)), ("lse", lse, (d.batch, d.n_h))],
+                  torch.float32)
+    _check_inputs(d, [("cu_seqlens_dev", cu_seqlens_dev, (d.batch + 1,))], torch.int32)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().mla_laga_decode_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(c_kv), _ptr(k_rope), _ptr(W_UK), _ptr(W_UV), _cu_ptr(cu),
+        _ptr(cu_seqlens_dev), _ptr(out), _ptr(lse), ctypes.c_void_p(stream)))
+    return out, lse
 
 
 def mla_laga_decode(q, c_kv, k_rope, W_UK, W_UV, cu_seqlens,

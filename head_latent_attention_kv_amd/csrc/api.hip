@@ -475,6 +475,31 @@ mla_status mla_laga_decode(const mla_laga_decode_desc* desc, const void* q, cons
                      static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void* q,
+                                   const void* c_kv, const void* k_rope, const void* W_UK,
+                                   const void* W_UV, const int32_t* cu_host,
+                                   const int32_t* cu_dev, float* out, float* lse, void* stream) {
+  DecodePlan p;
+  if (mla_status s = make_decode_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  const void* ptrs[] = {q, c_kv, k_rope, W_UK, W_UV, out, lse};
+  const char* names[] = {"q", "c_kv", "k_rope", "W_UK", "W_UV", "out", "lse"};
+  for (int k = 0; k < 7; ++k) {
+    if (!ptrs[k]) return fail(MLA_ERR_INVALID_ARG, "%s is NULL", names[k]);
+    if (misaligned(ptrs[k])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[k]);
+  }
+  if (!cu_dev) return fail(MLA_ERR_INVALID_ARG, "decode needs cu_seqlens_dev");
+  const int64_t need = decode_layout(p).total;
+  if (need > kDecodeScratchBytes)
+    return fail(MLA_ERR_WORKSPACE,
+                "decode needs %lld bytes of scratch; the static scratch holds %lld "
+                "(use mla_laga_decode with a workspace)",
+                (long long)need, (long long)kDecodeScratchBytes);
+  char* ws = nullptr;
+  if (mla_status s = decode_scratch(&ws); s != MLA_OK) return s;
+  return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
 const char* mla_laga_status_string(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

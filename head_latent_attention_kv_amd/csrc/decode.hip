@@ -27,6 +27,8 @@
 //   4. head_gemm_kernel: per-head out = o_lat W_UV_h (fp16 in, fp32 out).
 #include <math.h>
 
+#include <mutex>
+
 #include "fast.h"
 #include "fast_common.h"
 
@@ -398,6 +400,38 @@ decode_combine_kernel(const _Float16* __restrict__ opart, const float2* __restri
 }
 
 }  // namespace
+
+// Scratch of mla_laga_decode_noalloc, for callers that cannot allocate
+// device memory: a device array of the library's own, which each GPU holds
+// from the loading of the code object until the process ends. On the host,
+// `scratch` names a host-side stand-in, not the device memory: host code
+// uses only the per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+mla_status decode_scratch(char** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MLA_ERR_HIP, "no current device for the static decode scratch");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    // once per device, with that device current: each GPU holds its own
+    // copy of the array at its own address
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *ptr = g_scratch_dev[dev];
+  return MLA_OK;
+}
 
 DecodeLayout decode_layout(const DecodePlan& p) {
   DecodeLayout L{};

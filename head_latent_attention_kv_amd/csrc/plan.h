@@ -88,6 +88,11 @@ struct DecodeLayout {
   int64_t total;
 };
 DecodeLayout decode_layout(const DecodePlan& p);
+// Bytes of the library's static decode scratch (one array per GPU).
+constexpr int64_t kDecodeScratchBytes = MLA_DECODE_NOALLOC_MAX_BYTES;
+// Device address of that scratch on the current device (looked up once per
+// device).
+mla_status decode_scratch(char** ptr);
 
 FwdLayout fwd_layout(const Plan& p, bool fast);
 inline FwdLayout fwd_layout(const Plan& p) { return fwd_layout(p, p.fast); }

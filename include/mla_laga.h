@@ -231,6 +231,31 @@ mla_status mla_laga_decode(const mla_laga_decode_desc* desc, const void* q, cons
                            void* stream);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same operation, arguments and results as
+ * mla_laga_decode, bit for bit, without the workspace: the kernels use a
+ * static device buffer of the library's own (MLA_DECODE_NOALLOC_MAX_BYTES,
+ * 256 MiB), which each GPU the library runs on holds until the process
+ * ends. The call allocates and frees nothing and enqueues no memset; the
+ * buffer's address on a device is looked up on the first call with that
+ * device current (make that first call outside graph capture).
+ *   - A decode whose mla_laga_decode_workspace_size exceeds the buffer is
+ *     rejected with MLA_ERR_WORKSPACE before anything is enqueued (64 x 8192
+ *     cached rows at n_h = 128 need 64.25 MiB).
+ *   - Every call on one GPU shares that GPU's buffer, and nothing in it is
+ *     assumed from an earlier call. Calls that overlap on one GPU (other
+ *     streams, or other host threads, without ordering between them) race
+ *     on it: order them, e.g. on one stream.
+ */
+#define MLA_DECODE_NOALLOC_MAX_BYTES (256ll << 20)
+mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void* q,
+                                   const void* c_kv, const void* k_rope, const void* W_UK,
+                                   const void* W_UV, const int32_t* cu_seqlens_host,
+                                   const int32_t* cu_seqlens_dev, float* out, float* lse,
+                                   void* stream);
+
+/*
  * Host-side counts used for FLOP accounting: visible (query, key) pairs per
  * head, and the half-open latent row range [key_lo, key_hi) the shard needs.
  * Attention cost grows with the visible pairs, i.e. with the sum of squared
