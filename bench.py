@@ -341,15 +341,20 @@ def memory_report(name):
     a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
     cu = cfg.cu_seqlens()
     torch.cuda.synchronize()
-    inputs = torch.cuda.memory_allocated()
+    inputs = requested()
+
+    def requested():
+        return torch.cuda.memory_stats()["requested_bytes.all.current"]
 
     def peak_of(fn):
+        # bytes requested from the caching allocator (not the cached blocks
+        # that serve them)
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated()
+        before = requested()
         torch.cuda.reset_peak_memory_stats()
         res = fn()
         torch.cuda.synchronize()
-        return res, torch.cuda.max_memory_allocated() - before
+        return res, torch.cuda.memory_stats()["requested_bytes.all.peak"] - before
 
     def fwd_call():
         call = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, q_ranges=cfg.q_ranges)
@@ -359,7 +364,7 @@ def memory_report(name):
     (call, out, lse), fwd_peak = peak_of(fwd_call)
     del call
     torch.cuda.synchronize()
-    held = torch.cuda.memory_allocated() - inputs
+    held = requested() - inputs
     res = {"metric": "attention-block device bytes per query shard", "workload": cfg.name,
            "config": {"n_h": cfg.n_h, "S": cfg.S, "S_loc": cfg.S_loc, "q_offset": cfg.q_offset},
            "laga": {"forward_peak": fwd_peak, "held_forward_to_backward": held}}
@@ -381,10 +386,10 @@ def memory_report(name):
 
     def held_bytes(shapes):
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated()
+        before = requested()
         ts = [torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in shapes]
         torch.cuda.synchronize()
-        b = torch.cuda.memory_allocated() - before
+        b = requested() - before
         del ts
         return b
 
@@ -733,14 +738,16 @@ def main():
     # with rows x keys. Each form's backward is timed on its own call, and its
     # allocator peak (workspace and gradients of a fresh call) is measured.
     def bwd_peak(stored):
+        # bytes requested from the caching allocator by a fresh call's
+        # workspaces and the gradients
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated()
+        before = torch.cuda.memory_stats()["requested_bytes.all.current"]
         torch.cuda.reset_peak_memory_stats()
         c = hla.MLACall(*a, q_offset=cfg.q_offset, cu_seqlens=cu, backward=True,
                         q_ranges=cfg.q_ranges, stored_ds=stored)
         g = c.bwd(dev["dout"], *a, out, lse)
         torch.cuda.synchronize()
-        peak = torch.cuda.max_memory_allocated() - before
+        peak = torch.cuda.memory_stats()["requested_bytes.all.peak"] - before
         ws = c.ws_bwd.numel()
         del c, g
         torch.cuda.empty_cache()

@@ -164,7 +164,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.dOn = take(p.n_h * S_pad * 128 * 2);
     L.D = take(p.n_h * S_pad * 4);
     L.dK = take(p.Kpad * 2 * nk * 2);
-    L.dV = take(p.Kpad * 2 * nk * 2);
+    L.dV = -1;
     L.dKrope = take(p.n_h * p.Kpad * 64 * 4);
     L.info = take(p.n_h * S_pad * 16);
     L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),

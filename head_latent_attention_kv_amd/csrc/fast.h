@@ -49,10 +49,13 @@ mla_status launch_tile_order(const int32_t* cu, int n_seqs, int64_t S_loc, const
 // in_t: BF16 or F16 (both operands); out_t: F16 or F32. An fp32 output with
 // few tiles splits K when `part` holds gemm_splitk_bytes() bytes. An fp32
 // output is multiplied by *alpha (device memory) when alpha is not null.
+// y_kmajor: Y is stored k-major, Y[k][c] at Y + k * ldy + c (fp16 in, fp32
+// out, C a multiple of 8), and read transposed in LDS.
 mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, int64_t ldy,
                           int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
                           int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
                           Elem out_t, hipStream_t st, const char* name, float* part = nullptr,
-                          int64_t part_bytes = 0, const float* alpha = nullptr);
+                          int64_t part_bytes = 0, const float* alpha = nullptr,
+                          bool y_kmajor = false);
 
 }  // namespace mla

@@ -203,21 +203,18 @@ constexpr int P_NPW = (P_PIECES + 3) / 4;      // 13 per B wave (only B waves is
 constexpr int P_XCH = 2 * P_BYTES;             // P slots: [pair][buffer] x 2 KiB
 static_assert(P_DON >= QB * XS_ROW && P_INFO - P_DON >= QB * PD_ROW && P_BYTES - P_INFO >= QB * 16,
               "paired dK/dV stage layout");
-// dKV^T staging tile after the loop: 256 dims x 128 keys, rows padded to 136
-// halves (272 bytes, an odd number of 16-byte slots)
-constexpr int T_PITCH = 136;
-// ... then dKr rows: 128 keys x 64 floats, padded to 68 (272 bytes); then
-// dKV rows: 128 keys x 256 halves, padded to 264 (528 bytes, odd slot count)
+// Staging tiles after the loop: dKr rows, 128 keys x 64 floats padded to 68
+// (272 bytes); then dKV rows, 128 keys x 256 halves padded to 264 (528
+// bytes, an odd number of 16-byte slots)
 constexpr int R_PITCH = 68, K_PITCH = 264;
-static_assert(256 * T_PITCH * 2 + 128 * R_PITCH * 4 <= 2 * P_BYTES + 4 * 2 * 2048 &&
+static_assert(128 * R_PITCH * 4 <= 2 * P_BYTES + 4 * 2 * 2048 &&
               128 * K_PITCH * 2 <= 2 * P_BYTES + 4 * 2 * 2048, "staging tiles fit the LDS");
 
 __global__ void __launch_bounds__(512)
 attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict__ dOn,
                      const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                      const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
-                     const int* __restrict__ korder,
-                     _Float16* __restrict__ dKV, _Float16* __restrict__ dKVT,
+                     const int* __restrict__ korder, _Float16* __restrict__ dKV,
                      float* __restrict__ dKr, _Float16* __restrict__ dS, int n_h, int n_seqs,
                      int S_loc, int S_pad, RowMap rm, int key_lo, int Kpad, int n_kt, float scale,
                      float scale_log2) {
@@ -500,41 +497,27 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     if constexpr (kA) store_ds(1);   // the last sub-block (odd parity)
 
     // write: lane = key t, registers = dims (four consecutive per group).
-    // Every output leaves through LDS in whole rows: first dKV^T (one dim,
-    // the workgroup's 128 keys = 256 bytes per row) together with the fp32
-    // rope part of dK (dKr: 128 keys x 64 floats, one contiguous 32 KiB
-    // block), then dKV row-major (one key, 2 x 256 bytes).
-    const int nacc = kA ? 4 : 6;
+    // Every output leaves through LDS in whole rows: first the fp32 rope
+    // part of dK (dKr: 128 keys x 64 floats, one contiguous 32 KiB block),
+    // then dKV row-major (one key, 2 x 256 bytes), which the latent-gradient
+    // GEMM reads as it is and the weight-gradient GEMMs read k-major.
     const int64_t nk = static_cast<int64_t>(n_h) * 128;
     const int key = 32 * pi + lr;                           // key within the workgroup
     const float sc = kA ? 1.f : scale;
-    _Float16* tile = reinterpret_cast<_Float16*>(smem);     // [256 dims][T_PITCH] (free after the loop)
-    float* rtile = reinterpret_cast<float*>(smem + 256 * T_PITCH * 2);   // [128 keys][R_PITCH]
+    float* rtile = reinterpret_cast<float*>(smem);          // [128 keys][R_PITCH] (free after the loop)
+    if constexpr (!kA) {
   #pragma unroll
-    for (int mt = 0; mt < 6; ++mt) {
-      if (mt >= nacc) break;
+      for (int mt = 4; mt < 6; ++mt) {
   #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3
-        if (d < 128) {
-          const int r = (kA ? 128 : 0) + d;       // tile row of dim d
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) tile[(r + e) * T_PITCH + key] = static_cast<_Float16>(acc[mt][4 * g + e] * sc);
-        } else {
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * mt + 8 * g + 4 * lh;   // dims d..d+3 of dK's rope part
           const f32x4 fv = {acc[mt][4 * g] * sc, acc[mt][4 * g + 1] * sc, acc[mt][4 * g + 2] * sc,
                             acc[mt][4 * g + 3] * sc};
           *reinterpret_cast<f32x4*>(rtile + key * R_PITCH + (d - 128)) = fv;
         }
       }
     }
-    __syncthreads();   // both roles' rows written
-    // dKV^T rows h*128 + d (dK_nope) and nk + h*128 + d (dV), keys t0 .. t0+127
-    for (int e = tid; e < 256 * 16; e += 512) {
-      const int r = e >> 4, c = e & 15;
-      const int64_t col = (r < 128 ? 0 : nk) + static_cast<int64_t>(h) * 128 + (r & 127);
-      *reinterpret_cast<u32x4*>(dKVT + col * Kpad + t0 + 8 * c) =
-          *reinterpret_cast<const u32x4*>(tile + r * T_PITCH + 8 * c);
-    }
+    __syncthreads();   // the B waves' rope rows written
     // dKr[h][t0 .. t0+127][64]: contiguous
     float* kr = dKr + (static_cast<int64_t>(h) * Kpad + t0) * 64;
     for (int e = tid; e < 128 * 16; e += 512) {
@@ -1043,7 +1026,6 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   _Float16* dOn = reinterpret_cast<_Float16*>(at(L.dOn));
   float* D = reinterpret_cast<float*>(at(L.D));
   _Float16* dKV = reinterpret_cast<_Float16*>(at(L.dK));
-  _Float16* dKVT = reinterpret_cast<_Float16*>(at(L.dV));
   float* dKr = reinterpret_cast<float*>(at(L.dKrope));
   uint32_t* info = reinterpret_cast<uint32_t*>(at(L.info));
   // stored dS: the dK/dV kernel writes it, the dQ kernel reads it
@@ -1114,7 +1096,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     const int n_kt = static_cast<int>(p.Kpad / PW);
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
-                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKVT, dKr, dS, p.n_h,
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKr, dS, p.n_h,
                        p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
@@ -1157,14 +1139,15 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                          st, dc_kv + p.key_hi * p.d_c, (p.S - p.key_hi) * p.d_c);
   }
   if ((s = check_launch("zero rows")) != MLA_OK) return s;
-  // dW_UK = c_kv^T dK_nope, dW_UV = c_kv^T dV (contract over the shard's keys)
-  if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT, p.Kpad, nk, p.Kpad, dW_UK, nk, 128 * nk, 128,
+  // dW_UK = c_kv^T dK_nope, dW_UV = c_kv^T dV (contract over the shard's
+  // keys): the dKV rows are read k-major (key rows, 2 n_h 128 columns)
+  if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKV, 2 * nk, nk, p.Kpad, dW_UK, nk, 128 * nk, 128,
                           p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart, gpart_bytes,
-                          dsc + 1)) != MLA_OK)
+                          dsc + 1, true)) != MLA_OK)
     return s;
-  if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKVT + nk * p.Kpad, p.Kpad, nk, p.Kpad, dW_UV, nk,
+  if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKV + nk, 2 * nk, nk, p.Kpad, dW_UV, nk,
                           128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart,
-                          gpart_bytes, dsc + 1)) != MLA_OK)
+                          gpart_bytes, dsc + 1, true)) != MLA_OK)
     return s;
   return fork.join();
 }

@@ -74,7 +74,16 @@ __device__ __forceinline__ void gemm_tile(int bid, int n_tr, int n_tc, int* tr, 
 // written as 0. With kPart, the tile goes unmasked to part[blockIdx.y][r][c]
 // (fp32) for a split-K reduction; otherwise to `out` in the tiled layout of
 // launch_gemm_nt.
-template <typename InT, typename OutT, bool kPart, int kW>
+//
+// kYT: Y is stored k-major instead, Y[k][c] with ldy elements per k row (the
+// row-major gradient rows of the backward, contracted over keys). Its tile
+// is then 32 k rows of 256 columns (512 bytes each), DMA-filled two rows per
+// wave instruction, and each fragment is read transposed (two
+// ds_read_b64_tr_b16). A transposed read's 16 lanes fetch 8 bytes of 4
+// consecutive rows in one 32-byte column span; storing the 16-byte slot s of
+// row k at slot s ^ (2 (k % 4)) puts those 4 spans on 4 different 32-byte
+// groups of banks.
+template <typename InT, typename OutT, bool kPart, int kW, bool kYT = false>
 __global__ void __launch_bounds__(kW * 64)
 gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __restrict__ Y,
                int64_t ldy, int64_t C, int64_t k_len, OutT* __restrict__ out, int64_t ldo,
@@ -101,21 +110,32 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
 
   // the first half of the waves fill the X tile, the second the Y tile
   const bool is_x = w < HW;
+  const bool ykm = kYT && !is_x;   // this wave fills a k-major Y tile
   const int64_t ld = is_x ? ldx : ldy;
-  const InT* src = live ? (is_x ? X + r0 * ldx : Y + c0 * ldy) + kbeg : nullptr;
+  const InT* src = live ? (is_x ? X + r0 * ldx + kbeg : (kYT ? Y + kbeg * ldy + c0 : Y + c0 * ldy + kbeg))
+                        : nullptr;
   const int last = static_cast<int>((is_x ? R - r0 : C - c0) - 1);   // >= 0 for live tiles
   // piece p of an operand tile = rows 16p .. 16p + 15; lane l fills row
-  // 16p + l / 4, physical slot l % 4, which holds k-slot (l % 4) ^ ((row / 4) % 4)
+  // 16p + l / 4, physical slot l % 4, which holds k-slot (l % 4) ^ ((row / 4) % 4).
+  // k-major Y: piece p = k rows 2p, 2p + 1; lane l fills k row 2p + l / 32,
+  // physical slot l % 32, which holds column slot (l % 32) ^ (2 (row % 4))
+  // (columns past C reload the last valid 8 columns; never stored)
   int doff[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    const int row = 16 * ((w % HW) * NPW + j) + (lane >> 2);
-    const int slot = (lane & 3) ^ ((row >> 2) & 3);
-    doff[j] = min(row, last) * static_cast<int>(ld) + slot * 8;
+    if (ykm) {
+      const int row = 2 * ((w % HW) * NPW + j) + (lane >> 5);
+      const int cs = (lane & 31) ^ (2 * (row & 3));
+      doff[j] = row * static_cast<int>(ld) + min(8 * cs, last & ~7);
+    } else {
+      const int row = 16 * ((w % HW) * NPW + j) + (lane >> 2);
+      const int slot = (lane & 3) ^ ((row >> 2) & 3);
+      doff[j] = min(row, last) * static_cast<int>(ld) + slot * 8;
+    }
   }
   auto issue = [&](int c, int st) {
     char* dst = smem + st * G_STAGE + (is_x ? 0 : G_OP) + (w % HW) * NPW * 1024;
-    const char* s0 = reinterpret_cast<const char*>(src + static_cast<int64_t>(c) * GK);
+    const char* s0 = reinterpret_cast<const char*>(src + static_cast<int64_t>(c) * GK * (ykm ? ld : 1));
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
       // wave-uniform base plus an unsigned 32-bit lane offset in bytes (the
@@ -140,12 +160,29 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   const int nk = live ? static_cast<int>(k_len / GK) : 0;
   // fragments: [k16 step of the chunk][tile]
   vec a[2][NI], b[2][4];
+  // k-major Y: lane (g = l / 16, p = l % 16) reads k rows 16 step + 8 (g / 2)
+  // + p / 4 (and 4 further), columns 32 (wc NI + i) + 16 (g % 2) + 4 (p % 4)
+  // .. + 3 (frag_tr2); the column slot moves by the row's swizzle
+  int yt_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int g = lane >> 4, p = lane & 15;
+    const int cs = 4 * (wc * NI + i) + 2 * (g & 1) + ((p & 3) >> 1);
+    yt_off[i] = (8 * (g >> 1) + (p >> 2)) * (GT * 2) + (cs ^ (2 * (p >> 2))) * 16 + 8 * (p & 1);
+  }
   auto frags = [&](int kc, int step) {
     const int st = kc % G_NST, so = step ? so1 : so0;
     const char* xa = smem + st * G_STAGE + (wr * 128 + lr) * (GK * 2) + so;
     const char* ya = smem + st * G_STAGE + G_OP + (wc * 32 * NI + lr) * (GK * 2) + so;
+    if constexpr (kYT) {
+      const char* yt = smem + st * G_STAGE + G_OP + step * 16 * (GT * 2);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) a[step][i] = *reinterpret_cast<const vec*>(ya + i * 32 * GK * 2);
+      for (int i = 0; i < NI; ++i)
+        a[step][i] = frag_tr2(yt + yt_off[i], yt + yt_off[i] + 4 * (GT * 2));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a[step][i] = *reinterpret_cast<const vec*>(ya + i * 32 * GK * 2);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[step][j] = *reinterpret_cast<const vec*>(xa + j * 32 * GK * 2);
   };
@@ -498,7 +535,9 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
                           int64_t C, int64_t K, void* out, int64_t ldo, int64_t rt_stride,
                           int64_t ct_stride, int64_t R_store, int64_t C_store, Elem in_t,
                           Elem out_t, hipStream_t st, const char* name, float* part,
-                          int64_t part_bytes, const float* alpha) {
+                          int64_t part_bytes, const float* alpha, bool y_kmajor) {
+  if (y_kmajor && (in_t != Elem::F16 || out_t != Elem::F32 || C % 8 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: k-major Y takes fp16 in, fp32 out, C a multiple of 8", name);
   if (K % GK != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: K=%lld not a multiple of 32", name, (long long)K);
   if (C_store % 8 != 0) return fail(MLA_ERR_UNSUPPORTED, "%s: C_store not a multiple of 8", name);
   const int64_t n_tr = (R_store + GT - 1) / GT, n_tc = (C_store + GT - 1) / GT;
@@ -515,7 +554,18 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
   const int64_t kl = K / sp;
   const int ntr = static_cast<int>(n_tr), ntc = static_cast<int>(n_tc);
   KernelTimer kt(name, st);
-  if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
+  // k-major Y first: the other branches read Y k-contiguous
+  if (y_kmajor && sp == 1)
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, false, 8, true>), grid, dim3(512), 0, st,
+                       static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                       ldy, C, kl, static_cast<float*>(out), ldo, rt_stride, ct_stride, R_store,
+                       C_store, nullptr, alpha, ntr, ntc);
+  else if (y_kmajor)
+    hipLaunchKernelGGL((gemm_nt_kernel<_Float16, float, true, 8, true>), grid, dim3(512), 0, st,
+                       static_cast<const _Float16*>(X), ldx, R, static_cast<const _Float16*>(Y),
+                       ldy, C, kl, static_cast<float*>(nullptr), ldo, rt_stride, ct_stride,
+                       R_store, C_store, pp, nullptr, ntr, ntc);
+  else if (in_t == Elem::BF16 && out_t == Elem::F16 && sp == 1)
     hipLaunchKernelGGL((gemm_nt_kernel<__bf16, _Float16, false, 8>), grid, dim3(512), 0, st,
                        static_cast<const __bf16*>(X), ldx, R, static_cast<const __bf16*>(Y), ldy,
                        C, kl, static_cast<_Float16*>(out), ldo, rt_stride, ct_stride, R_store,

@@ -45,8 +45,8 @@ struct FwdLayout {
 struct BwdLayout {
   FwdLayout f;  // plain path: K, V; fast path: WT, Kfull (Vt unused)
   // plain path: D [S_loc][n_h], dK/dV fp32 [n_h][Kn][.]
-  // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128],
-  //             dV = its transpose [2*n_h*128][Kpad], dKrope fp32 [n_h][Kpad][64]
+  // fast path:  D [n_h][S_pad], dK = [dK_nope | dV] fp16 [Kpad][2*n_h*128]
+  //             (dV unused), dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
   // fast path only (fp16): V key-major [n_h][Kpad][128], [W_UK | W_UV]
   // [d_c][2*n_h*128], c_kv^T [d_c][Kpad], q and dout per head [n_h][S_pad][.].
