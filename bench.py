@@ -170,6 +170,21 @@ UTIL_PASS_B = ("SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_I
                "GRBM_GUI_ACTIVE")
 
 
+def kernel_key(name):
+    """Short name of a kernel from a profiler's (demangled or mangled) name:
+    the function's identifier plus its template arguments."""
+    import re
+    m = re.search(r"::(\w+)(<[^(]*>)?\(", name)
+    z = re.search(r"_GLOBAL__N_1(\d+)(\w+)", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    if z:   # a mangled name: the length-prefixed identifier, then its template args
+        ln, rest = int(z.group(1)), z.group(2)
+        # template arguments run to the "EE" that closes them
+        return rest[:ln] + (f"<{rest[ln + 1:rest.find('EE', ln)]}>" if rest[ln:ln + 1] == "I" else "")
+    return name.split("(")[0]
+
+
 def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
     """Markdown table of per-kernel unit utilisation from the two passes.
 
@@ -184,7 +199,6 @@ def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
     forward-attention launch on): the first launch of each kernel also
     loads its code object."""
     import csv
-    import re
     from collections import defaultdict
 
     def load(path):
@@ -195,16 +209,7 @@ def utilisation_from_counters(csv_a, csv_b, n_xcd=8, n_cu=256, n_simd=1024):
         for r in rows:
             if int(r["Dispatch_Id"]) < first:
                 continue
-            name = r["Kernel_Name"]
-            m = re.search(r"::(\w+)(<[^(]*>)?\(", name)
-            z = re.search(r"_GLOBAL__N_1(\d+)(\w+)", name)
-            if m:
-                k = m.group(1) + (m.group(2) or "")
-            elif z:   # a mangled name: the length-prefixed identifier, then its template args
-                ln, rest = int(z.group(1)), z.group(2)
-                k = rest[:ln] + (f"<{rest[ln + 1:rest.find('E', ln)]}>" if rest[ln:ln + 1] == "I" else "")
-            else:
-                k = name.split("(")[0]
+            k = kernel_key(r["Kernel_Name"])
             cnt[k][r["Counter_Name"]] += float(r["Counter_Value"])
             dur[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
         return cnt, {k: (sum(v.values()), len(v)) for k, v in dur.items()}
@@ -283,6 +288,31 @@ def cpu_one_core_forward(budget_heads=2):
     return res
 
 
+def kernel_stats_from_trace(trace_csv, skip_first=True):
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace
+    csv. With skip_first, each kernel's first dispatch (which also loads its
+    code object) is left out: the table holds warm launches only."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = defaultdict(list)
+    seen = set()
+    for r in rows:
+        key = kernel_key(r["Kernel_Name"])
+        if skip_first and key not in seen:
+            seen.add(key)
+            continue
+        per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    total = sum(sum(v) for v in per.values())
+    out = ["| kernel | warm launches | total ms | average us | min us | max us | % |",
+           "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {len(v)} | {sum(v) / 1e3:.3f} | {sum(v) / len(v):.1f} | {min(v):.1f} "
+                   f"| {max(v):.1f} | {100 * sum(v) / total:.2f} |")
+    return "\n".join(out)
+
+
 def cpu_baseline(cfg, x, cu, pairs, kn, budget_s=15.0, max_heads=16):
     """The fp64 oracle, as it stands, on whole heads of the workload (all rows,
     forward and backward) until about `budget_s` seconds have been spent; the
@@ -340,11 +370,12 @@ def memory_report(name):
            for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV", "dout")}
     a = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
     cu = cfg.cu_seqlens()
-    torch.cuda.synchronize()
-    inputs = requested()
 
     def requested():
         return torch.cuda.memory_stats()["requested_bytes.all.current"]
+
+    torch.cuda.synchronize()
+    inputs = requested()
 
     def peak_of(fn):
         # bytes requested from the caching allocator (not the cached blocks
@@ -567,6 +598,9 @@ def main():
     ap.add_argument("--workload", default="h128_s16k_shard")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-bwd-forms", action="store_true",
+                    help="skip timing the stored-dS backward and the allocator peaks of both "
+                         "forms (so that a profiled run holds the default form only)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed after a 512 MiB write that evicts the caches")
     ap.add_argument("--counter-step", action="store_true",
@@ -575,6 +609,9 @@ def main():
     ap.add_argument("--utilisation-from", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
                     help="print per-kernel MFMA/LDS/VALU utilisation from two --counter-step "
                          "rocprofv3 --pmc runs (counters: UTIL_PASS_A, then UTIL_PASS_B)")
+    ap.add_argument("--kernel-stats-from", metavar="TRACE_CSV",
+                    help="print warm-launch kernel durations from a rocprofv3 --kernel-trace csv "
+                         "(each kernel's first dispatch left out)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two --counter-step counter csv files")
     ap.add_argument("--decode", metavar="NAME",
@@ -588,6 +625,9 @@ def main():
     args = ap.parse_args()
     if args.utilisation_from:
         print(utilisation_from_counters(*args.utilisation_from))
+        return
+    if args.kernel_stats_from:
+        print(kernel_stats_from_trace(args.kernel_stats_from))
         return
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from, args.workload), indent=1))
@@ -754,7 +794,7 @@ def main():
         return peak, ws
 
     forms = {}
-    for stored in (False, True):
+    for stored in (() if args.no_bwd_forms else (False, True)):
         peak, ws = bwd_peak(stored)
         entry = {"workspace_bytes": ws, "backward_peak_bytes": peak}
         if not stored:
