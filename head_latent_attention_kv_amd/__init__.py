@@ -22,9 +22,11 @@ __all__ = [
     "mla_laga_uses_fast_path", "MLACall", "MLA_F32", "MLA_BF16", "MLA_FLAG_GENERIC", "MLA_FLAG_STORED_DS",
     "MLA_MAX_RANGES", "MLADecodeDesc", "MLADecodeCall", "mla_laga_decode",
     "mla_laga_decode_workspace_size", "mla_laga_decode_noalloc", "MLA_DECODE_NOALLOC_MAX_BYTES",
+    "mla_laga_row_window", "MLA_ERR_DEBUG_CHECK",
 ]
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
+MLA_ERR_DEBUG_CHECK = -5
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC = 1
 MLA_FLAG_STORED_DS = 4
@@ -84,6 +86,7 @@ EXPORTED = {
                                        ctypes.c_size_t, _P]),
     "mla_laga_decode_noalloc": (ctypes.c_int, [_DDESCP, _P, _P, _P, _P, _P, _I32P, _P, _P, _P, _P]),
     "mla_laga_uses_fast_path": (ctypes.c_int, [_DESCP]),
+    "mla_laga_row_window": (ctypes.c_int, [_DESCP, _I32P, _P, _P, _P]),
     "mla_laga_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "mla_laga_timing_select": (ctypes.c_int, [ctypes.c_char_p]),
     "mla_laga_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), _I64P]),
@@ -246,6 +249,23 @@ def mla_laga_count(desc: MLADesc, cu: Optional[np.ndarray] = None) -> Tuple[int,
 
 def mla_laga_uses_fast_path(desc: MLADesc) -> bool:
     return bool(load_library().mla_laga_uses_fast_path(ctypes.byref(desc)))
+
+
+def mla_laga_row_window(desc: MLADesc, cu: Optional[np.ndarray] = None,
+                        cu_dev: Optional[torch.Tensor] = None, device="cuda") -> torch.Tensor:
+    """int64 [S_loc, 2]: the first and last global key position each local
+    row of `desc` sees, as the library's kernels compute them. `cu` and
+    `cu_dev` hold the same cu_seqlens on the host and the device."""
+    if (cu is None) != (cu_dev is None):
+        raise ValueError("cu and cu_dev go together")
+    if cu_dev is not None:
+        _check_inputs(desc, [("cu_dev", cu_dev, (len(cu),))], torch.int32)
+    w = torch.empty((desc.S_loc, 2), dtype=torch.int64, device=device)
+    stream = torch.cuda.current_stream(w.device).cuda_stream
+    _check(load_library().mla_laga_row_window(ctypes.byref(desc), _cu_ptr(cu), _ptr(cu_dev),
+                                              _ptr(w) if desc.S_loc > 0 else None,
+                                              ctypes.c_void_p(stream)))
+    return w
 
 
 def timing_enable(on: bool = True):

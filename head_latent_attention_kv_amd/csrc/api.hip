@@ -330,6 +330,20 @@ static mla_status make_decode_plan(const mla_laga_decode_desc* d, const int32_t*
   return MLA_OK;
 }
 
+// Runs `run` (the call's launches), wrapped in the debug-mode checks when
+// MLA_LAGA_DEBUG is set. `used`: the workspace bytes the call's layout takes
+// (the debug tail follows them).
+template <typename F>
+static mla_status run_checked(bool debug, const int32_t* cu_host, const int32_t* cu_dev, int n_cu,
+                              char* ws, int64_t used, const DebugOutput* outs, int n_out,
+                              hipStream_t st, F&& run) {
+  if (!debug) return run();
+  if (mla_status s = debug_begin(cu_host, cu_dev, n_cu, ws, used, outs, n_out, st); s != MLA_OK)
+    return s;
+  if (mla_status s = run(); s != MLA_OK) return s;
+  return debug_end(ws, used, outs, n_out, st);
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -341,7 +355,7 @@ mla_status mla_laga_fwd_workspace_size(const mla_laga_desc* desc, const int32_t*
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   Plan p;
   if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
-  *bytes = static_cast<size_t>(fwd_layout(p).total);
+  *bytes = static_cast<size_t>(fwd_layout(p).total + debug_tail());
   return MLA_OK;
 }
 
@@ -350,7 +364,7 @@ mla_status mla_laga_bwd_workspace_size(const mla_laga_desc* desc, const int32_t*
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   Plan p;
   if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
-  *bytes = static_cast<size_t>(bwd_layout(p).total);
+  *bytes = static_cast<size_t>(bwd_layout(p).total + debug_tail());
   return MLA_OK;
 }
 
@@ -396,16 +410,21 @@ mla_status mla_laga_fwd(const mla_laga_desc* desc, const void* q, const void* c_
   if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
   if (p.S_loc == 0) return MLA_OK;
   const FwdLayout L = fwd_layout(p);
+  const bool debug = debug_mode();
   if (mla_status s = check_common(p, desc, q, c_kv, k_rope, W_UK, W_UV, cu_dev, workspace,
-                                  workspace_bytes, L.total);
+                                  workspace_bytes, L.total + (debug ? kDebugTailBytes : 0));
       s != MLA_OK)
     return s;
   if (!out || !lse || misaligned(out) || misaligned(lse))
     return fail(MLA_ERR_INVALID_ARG, "out/lse NULL or not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (p.fast) return fast_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
-  return generic_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+  const DebugOutput outs[] = {{out, p.S_loc * p.n_h * p.d_v, "out"}, {lse, p.S_loc * p.n_h, "lse"}};
+  return run_checked(debug, cu_host, cu_dev, p.n_seqs > 0 ? p.n_seqs + 1 : 0, ws, L.total, outs, 2,
+                     st, [&] {
+                       if (p.fast) return fast_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+                       return generic_fwd(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+                     });
 }
 
 mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void* q,
@@ -427,8 +446,9 @@ mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void*
     return s;
   }
   const BwdLayout L = bwd_layout(p);
+  const bool debug = debug_mode();
   if (mla_status s = check_common(p, desc, q, c_kv, k_rope, W_UK, W_UV, cu_dev, workspace,
-                                  workspace_bytes, L.total);
+                                  workspace_bytes, L.total + (debug ? kDebugTailBytes : 0));
       s != MLA_OK)
     return s;
   if (!dout || !out || !lse || !dq) return fail(MLA_ERR_INVALID_ARG, "dout/out/lse/dq is NULL");
@@ -436,11 +456,20 @@ mla_status mla_laga_bwd(const mla_laga_desc* desc, const void* dout, const void*
   for (const void* a : al)
     if (a && misaligned(a)) return fail(MLA_ERR_INVALID_ARG, "a gradient argument is not 16-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  if (p.fast_bwd)
-    return fast_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
-                    dW_UK, dW_UV, ws, st);
-  return generic_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq, dc_kv, dk_rope,
-                     dW_UK, dW_UV, ws, st);
+  const int64_t n_w = static_cast<int64_t>(p.d_c) * p.n_h;
+  const DebugOutput outs[] = {{dq, p.S_loc * p.n_h * p.d_qk, "dq"},
+                              {dc_kv, p.S * p.d_c, "dc_kv"},
+                              {dk_rope, p.S * p.d_rope, "dk_rope"},
+                              {dW_UK, n_w * p.d_nope, "dW_UK"},
+                              {dW_UV, n_w * p.d_v, "dW_UV"}};
+  return run_checked(debug, cu_host, cu_dev, p.n_seqs > 0 ? p.n_seqs + 1 : 0, ws, L.total, outs, 5,
+                     st, [&] {
+                       if (p.fast_bwd)
+                         return fast_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq,
+                                         dc_kv, dk_rope, dW_UK, dW_UV, ws, st);
+                       return generic_bwd(p, dout, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, dq,
+                                          dc_kv, dk_rope, dW_UK, dW_UV, ws, st);
+                     });
 }
 
 mla_status mla_laga_decode_workspace_size(const mla_laga_decode_desc* desc, const int32_t* cu_host,
@@ -448,7 +477,7 @@ mla_status mla_laga_decode_workspace_size(const mla_laga_decode_desc* desc, cons
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   DecodePlan p;
   if (mla_status s = make_decode_plan(desc, cu_host, &p); s != MLA_OK) return s;
-  *bytes = static_cast<size_t>(decode_layout(p).total);
+  *bytes = static_cast<size_t>(decode_layout(p).total + debug_tail());
   return MLA_OK;
 }
 
@@ -465,14 +494,20 @@ mla_status mla_laga_decode(const mla_laga_decode_desc* desc, const void* q, cons
     if (misaligned(ptrs[k])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[k]);
   }
   if (!cu_dev) return fail(MLA_ERR_INVALID_ARG, "decode needs cu_seqlens_dev");
-  const int64_t need = decode_layout(p).total;
+  const bool debug = debug_mode();
+  const int64_t used = decode_layout(p).total, need = used + (debug ? kDebugTailBytes : 0);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
     return fail(MLA_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
   if (static_cast<int64_t>(workspace_bytes) < need)
     return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %lld", workspace_bytes,
                 (long long)need);
-  return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse,
-                     static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const DebugOutput outs[] = {{out, int64_t(p.batch) * p.n_h * kFastDV, "out"},
+                              {lse, int64_t(p.batch) * p.n_h, "lse"}};
+  return run_checked(debug, cu_host, cu_dev, p.batch + 1, ws, used, outs, 2, st, [&] {
+    return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+  });
 }
 
 mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void* q,
@@ -488,7 +523,8 @@ mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void*
     if (misaligned(ptrs[k])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[k]);
   }
   if (!cu_dev) return fail(MLA_ERR_INVALID_ARG, "decode needs cu_seqlens_dev");
-  const int64_t need = decode_layout(p).total;
+  const bool debug = debug_mode();
+  const int64_t used = decode_layout(p).total, need = used + (debug ? kDebugTailBytes : 0);
   if (need > kDecodeScratchBytes)
     return fail(MLA_ERR_WORKSPACE,
                 "decode needs %lld bytes of scratch; the static scratch holds %lld "
@@ -496,8 +532,22 @@ mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void*
                 (long long)need, (long long)kDecodeScratchBytes);
   char* ws = nullptr;
   if (mla_status s = decode_scratch(&ws); s != MLA_OK) return s;
-  return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws,
-                     static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const DebugOutput outs[] = {{out, int64_t(p.batch) * p.n_h * kFastDV, "out"},
+                              {lse, int64_t(p.batch) * p.n_h, "lse"}};
+  return run_checked(debug, cu_host, cu_dev, p.batch + 1, ws, used, outs, 2, st, [&] {
+    return fast_decode(p, q, c_kv, k_rope, W_UK, W_UV, cu_dev, out, lse, ws, st);
+  });
+}
+
+mla_status mla_laga_row_window(const mla_laga_desc* desc, const int32_t* cu_host,
+                               const int32_t* cu_dev, int64_t* window, void* stream) {
+  Plan p;
+  if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (p.S_loc == 0) return MLA_OK;
+  if (!window || misaligned(window)) return fail(MLA_ERR_INVALID_ARG, "window is NULL or not 16-byte aligned");
+  if (p.n_seqs > 0 && !cu_dev) return fail(MLA_ERR_INVALID_ARG, "n_seqs > 0 needs cu_seqlens_dev");
+  return launch_row_window(p, cu_dev, window, static_cast<hipStream_t>(stream));
 }
 
 const char* mla_laga_status_string(mla_status s) {
@@ -507,6 +557,7 @@ const char* mla_laga_status_string(mla_status s) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_DEBUG_CHECK: return "MLA_ERR_DEBUG_CHECK";
   }
   return "unknown mla_status";
 }

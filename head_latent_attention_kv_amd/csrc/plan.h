@@ -98,6 +98,28 @@ FwdLayout fwd_layout(const Plan& p, bool fast);
 inline FwdLayout fwd_layout(const Plan& p) { return fwd_layout(p, p.fast); }
 BwdLayout bwd_layout(const Plan& p);
 
+// ---- debug mode (debug.hip)
+// Bytes after the used workspace that debug mode takes for its canary and
+// check slots; the *_workspace_size results include them in that mode.
+constexpr int64_t kDebugTailBytes = 256;
+struct DebugOutput {
+  void* ptr;
+  int64_t n;         // fp32 elements
+  const char* name;
+};
+// MLA_LAGA_DEBUG is set (and not "0"); read at every call.
+bool debug_mode();
+inline int64_t debug_tail() { return debug_mode() ? kDebugTailBytes : 0; }
+// Compare cu_dev with cu_host (n_cu values; skipped when either is null),
+// fill ws[0, ws_used) and the outputs with all-ones bytes and write the
+// canary and check slots at ws + ws_used. Waits for `st`.
+mla_status debug_begin(const int32_t* cu_host, const int32_t* cu_dev, int n_cu, char* ws,
+                       int64_t ws_used, const DebugOutput* outs, int n_out, hipStream_t st);
+// Scan the outputs for NaN, check the canary; waits for `st`.
+mla_status debug_end(char* ws, int64_t ws_used, const DebugOutput* outs, int n_out, hipStream_t st);
+// Per local row, the inclusive window {lo, hi} of global key positions.
+mla_status launch_row_window(const Plan& p, const int32_t* cu_dev, int64_t* window, hipStream_t st);
+
 // Set the thread's last-error message and return `s`.
 mla_status fail(mla_status s, const char* fmt, ...);
 mla_status check_launch(const char* what);

@@ -67,6 +67,25 @@
  *       key's total softmax weight over the shard's rows) must stay below
  *       65504; the fp32 gradients are multiplied back by 2^-e.
  */
+/*
+ * Debug mode. With the environment variable MLA_LAGA_DEBUG set to anything
+ * but "" or "0" (read at every call), mla_laga_fwd, mla_laga_bwd,
+ * mla_laga_decode and mla_laga_decode_noalloc add checks around their work:
+ *   - cu_seqlens_dev is copied back and must equal cu_seqlens_host;
+ *   - every output and the workspace bytes the call uses are first filled
+ *     with all-ones bytes (NaN as fp32, fp16 and bf16), so that an output
+ *     element the call does not write, or a result computed from workspace
+ *     bytes read before the call wrote them, comes out NaN;
+ *   - a canary is written into the 256 bytes after the used workspace (the
+ *     *_workspace_size results are 256 bytes larger in this mode, and the
+ *     static decode scratch holds 256 bytes less) and must be intact after
+ *     the work;
+ *   - after the work every output is scanned for NaN.
+ * The call then waits for its stream (so it cannot be captured into a
+ * graph), and a failed check returns MLA_ERR_DEBUG_CHECK with the first
+ * offending value named in mla_laga_last_error(). NaN in the inputs is
+ * reported the same way. Results are unchanged when the checks pass.
+ */
 #ifndef MLA_LAGA_H
 #define MLA_LAGA_H
 
@@ -82,7 +101,8 @@ typedef enum {
   MLA_ERR_INVALID_ARG = -1, /* bad shape, offset, pointer or cu_seqlens    */
   MLA_ERR_UNSUPPORTED = -2, /* valid, but outside what any path handles     */
   MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
-  MLA_ERR_HIP = -4          /* a HIP runtime call or a launch failed        */
+  MLA_ERR_HIP = -4,         /* a HIP runtime call or a launch failed        */
+  MLA_ERR_DEBUG_CHECK = -5  /* a debug-mode check failed (MLA_LAGA_DEBUG)   */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
@@ -263,6 +283,19 @@ mla_status mla_laga_decode_noalloc(const mla_laga_decode_desc* desc, const void*
  */
 mla_status mla_laga_count(const mla_laga_desc* desc, const int32_t* cu_seqlens_host,
                           int64_t* visible_pairs, int64_t* key_lo, int64_t* key_hi);
+
+/*
+ * The key window of every local row, as the kernels compute it: window
+ * (device, int64 [S_loc][2], 16-byte aligned) receives for row i the
+ * global positions lo = seg_lo(p) and hi = p of the first and last key it
+ * sees (p the row's position; see the mask at the top of this file), from
+ * the same device code that maps rows to positions and finds sample starts
+ * in the attention kernels. For checking the mask against an independent
+ * implementation. Arguments and validation as for mla_laga_fwd; enqueued
+ * on `stream`.
+ */
+mla_status mla_laga_row_window(const mla_laga_desc* desc, const int32_t* cu_seqlens_host,
+                               const int32_t* cu_seqlens_dev, int64_t* window, void* stream);
 
 /*
  * Kernel timing, for measurement. While enabled, every kernel the library

@@ -245,8 +245,44 @@ def test_null_and_misaligned_pointers_rejected_before_launch(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert lib.mla_laga_status_string(s).startswith(b"MLA_")
+    assert lib.mla_laga_status_string(hla.MLA_ERR_DEBUG_CHECK) == b"MLA_ERR_DEBUG_CHECK"
+
+
+def test_debug_mode_adds_a_256_byte_tail_to_every_workspace(monkeypatch):
+    """MLA_LAGA_DEBUG is read at every call: the workspace sizes grow by the
+    canary tail while it is set (and not "0"), and only then."""
+    cfg = workloads.config("h128_varlen64k")
+    d, cu = desc_for(cfg)
+    dd = decode_desc()
+    dcu = np.array([0, 10, 11, 60, 100], np.int32)
+
+    def sizes():
+        return (hla.mla_laga_fwd_workspace_size(d, cu), hla.mla_laga_bwd_workspace_size(d, cu),
+                hla.mla_laga_decode_workspace_size(dd, dcu))
+
+    monkeypatch.delenv("MLA_LAGA_DEBUG", raising=False)
+    base = sizes()
+    for v, extra in (("1", 256), ("0", 0), ("", 0), ("yes", 256)):
+        monkeypatch.setenv("MLA_LAGA_DEBUG", v)
+        assert sizes() == tuple(b + extra for b in base), v
+
+
+def test_row_window_validated_on_host(lib):
+    cfg = workloads.config("h128_varlen64k")
+    d, cu = desc_for(cfg)
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    cup = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.mla_laga_row_window(ctypes.byref(d), cup, fake, None, None) == hla.MLA_ERR_INVALID_ARG
+    assert b"window" in lib.mla_laga_last_error()
+    assert lib.mla_laga_row_window(ctypes.byref(d), cup, None, fake, None) == hla.MLA_ERR_INVALID_ARG
+    assert b"cu_seqlens_dev" in lib.mla_laga_last_error()
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.mla_laga_row_window(ctypes.byref(d), cup, fake, odd, None) == hla.MLA_ERR_INVALID_ARG
+    d.S_loc = 0
+    d.q_offset = 0
+    assert lib.mla_laga_row_window(ctypes.byref(d), cup, None, None, None) == hla.MLA_OK
 
 
 def decode_desc(n_h=128, batch=4, S=100, d_c=512, d_rope=64, d_nope=128, d_v=128, dtype=None):
