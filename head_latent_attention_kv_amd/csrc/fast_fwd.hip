@@ -14,8 +14,12 @@
 //      a lane owns one query column: the row max and sum stay in the lane,
 //      plus one exchange with the lane 32 away. Scores and the online
 //      softmax are fp32; P goes to fp16 and straight into O^T += V^T P^T.
-//      The running max is only moved when a block's max exceeds it by more
-//      than 2^8 (so P <= 256), which skips almost every rescale of O.
+//      The two 32-key halves of a block are scored as two independent MFMA
+//      chains, the running max is taken once per block, and the second
+//      half's weights are formed on the VALU while the first half's PV
+//      products run. The running max is only moved when a block's max
+//      exceeds it by more than 2^8 (so P <= 256), which skips almost every
+//      rescale of O.
 #include <math.h>
 #include <stdlib.h>
 
@@ -191,70 +195,78 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
       const bool need_mask = !(g0 >= wlo_max && g0 + FK - 1 <= wp_min);
       const char* sk = smem + st * STAGE_B + k_lane;
       const char* sv = smem + st * STAGE_B + K_TILE_B + v_lane;
+      // S^T of both 32-key halves of the block (rows: keys 32 mt +
+      // swap23(lr)) as two independent chains issued alternately, K
+      // fragment reads FPF products ahead of each chain
+      f32x16 s[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // S^T rows: keys 32mt + swap23(lr) of the block
-        f32x16 s[NT];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+      constexpr int FPF = 3;
+      half8 fa[2][FPF + 1];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[nt][e] = 0.f;
-        const char* skm = sk + mt * 32 * K_ROW_B;
-        // K fragment reads run FPF products ahead
-        constexpr int FPF = 4;
-        half8 fa[FPF + 1];
+      for (int i = 0; i < FPF; ++i)
 #pragma unroll
-        for (int i = 0; i < FPF; ++i) fa[i] = *reinterpret_cast<const half8*>(skm + 32 * i);
-        // the score products run at raised wave priority, so that the SIMD's
-        // other wave fills the gaps of this dependent chain with its softmax
-        __builtin_amdgcn_s_setprio(1);
+        for (int mt = 0; mt < 2; ++mt)
+          fa[mt][i] = *reinterpret_cast<const half8*>(sk + mt * 32 * K_ROW_B + 32 * i);
+      // the score products run at raised wave priority, so that the SIMD's
+      // other wave fills the gaps of these chains with its softmax
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kk = 0; kk < 12; ++kk) {
-          if (kk + FPF < 12) fa[(kk + FPF) % (FPF + 1)] = *reinterpret_cast<const half8*>(skm + 32 * (kk + FPF));
+      for (int kk = 0; kk < 12; ++kk) {
+        if (kk + FPF < 12)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma_f16(fa[kk % (FPF + 1)], qf[nt][kk], s[nt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_setprio(0);
-        if (need_mask) {
+          for (int mt = 0; mt < 2; ++mt)
+            fa[mt][(kk + FPF) % (FPF + 1)] =
+                *reinterpret_cast<const half8*>(sk + mt * 32 * K_ROW_B + 32 * (kk + FPF));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s[mt] = mfma_f16(fa[mt][kk % (FPF + 1)], qf[0][kk], s[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = g0 + 32 * mt + swap23(d_row(r, lh));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              if (key < lo[nt] || key > p[nt]) s[nt][r] = -INFINITY;
+            if (key < lo[0] || key > p[0]) s[mt][r] = -INFINITY;
           }
-        }
-        half8 pb[NT][2];
+      }
+      // one running-max update per 64-key block
+      float mx = s[0][0];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float mx = s[nt][0];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
-          mx = wave_max_pair(mx) * scale_log2;
-          const bool grow = mx > m[nt] + kTau;
-          if (__any(grow)) {
-            const float m_new = grow ? mx : m[nt];
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m[nt] - m_new) : 1.f;
-            m[nt] = m_new;
-            l[nt] *= alpha;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = wave_max_pair(mx) * scale_log2;
+      const bool grow = mx > m[0] + kTau;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m[0];
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[0] - m_new) : 1.f;
+        m[0] = m_new;
+        l[0] *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-              for (int e = 0; e < 16; ++e) o[nt][dt][e] *= alpha;
-          }
-          const float mu = m[nt] == -INFINITY ? 0.f : m[nt];
-          float sum = l[nt];
+          for (int e = 0; e < 16; ++e) o[0][dt][e] *= alpha;
+      }
+      const float mu = m[0] == -INFINITY ? 0.f : m[0];
+      float sum = l[0];
+      // the weights of one half, then its PV products; the second half's
+      // weights are formed on the VALU while the first half's products run
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            half2v pr;
-            pr[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[nt][r], scale_log2, -mu)));
-            pr[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[nt][r + 1], scale_log2, -mu)));
-            pb[nt][r >> 3][r & 7] = pr[0];
-            pb[nt][r >> 3][(r & 7) + 1] = pr[1];
-            sum = __builtin_amdgcn_fdot2(pr, ones, sum, false);   // sum of the fp16 weights
-          }
-          l[nt] = sum;
+      for (int mt = 0; mt < 2; ++mt) {
+        half8 pb[2];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          half2v pr;
+          pr[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[mt][r], scale_log2, -mu)));
+          pr[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[mt][r + 1], scale_log2, -mu)));
+          pb[r >> 3][r & 7] = pr[0];
+          pb[r >> 3][(r & 7) + 1] = pr[1];
+          sum = __builtin_amdgcn_fdot2(pr, ones, sum, false);   // sum of the fp16 weights
         }
 #pragma unroll
         for (int ksl = 0; ksl < 2; ++ksl) {
@@ -262,11 +274,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
             const half8 a = *reinterpret_cast<const half8*>(sv + dt * 32 * V_ROW_B + ks * 32);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma_f16(a, pb[nt][ksl], o[nt][dt]);
+            o[0][dt] = mfma_f16(a, pb[ksl], o[0][dt]);
           }
         }
       }
+      l[0] = sum;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
