@@ -246,7 +246,7 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
   const int clim = static_cast<int>(min<int64_t>(C - c0, GT));
   const int rstore = static_cast<int>(min<int64_t>(R_store - r0, GT));
   const int cstore = static_cast<int>(min<int64_t>(C_store - c0, GT));
-  const bool edge = !kPart && (rlim < GT || clim < GT);
+  const bool edge = !kPart && (rlim < GT || clim < GT || rstore < GT || cstore < GT);
   auto tile_val = [&](int i, int j, int g, int rt, int ct, bool masked) {
     f32x4 v;
 #pragma unroll
@@ -298,14 +298,26 @@ gemm_nt_kernel(const InT* __restrict__ X, int64_t ldx, int64_t R, const InT* __r
     if (edge) stage(true);
     else stage(false);
     __syncthreads();
-    for (int pc = tid; pc < GT * (GT / 8); pc += kW * 64) {
-      const int rt = pc / (GT / 8), ct = (pc % (GT / 8)) * 8;
-      const int64_t r = r0 + rt, c = c0 + ct;
-      if (rt < rstore && ct < cstore)
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sth + rt * SH + ct),
-                                    reinterpret_cast<u32x4*>(out + (r / 128) * rt_stride +
-                                                             (r % 128) * ldo +
-                                                             (c / 128) * ct_stride + c % 128));
+    // Thread tid copies the 16-byte piece at column ct = 8 (tid % 32) of
+    // tile rows rt = tid / 32 + 16 s, s = 0 .. 15. Tiles start at multiples
+    // of 256 rows and columns, so in the tiled output layout the column part
+    // of the offset is fixed per thread, and the row part is the thread's
+    // first row plus a wave-uniform step (rows 128 and on are in the next
+    // 128-row block). All pieces are read before the first store.
+    constexpr int NS = GT * (GT / 8) / (kW * 64);   // 16 pieces per thread
+    static_assert(GT == 256 && GT % 128 == 0 && NS * kW * 64 == GT * (GT / 8) && NS == 16,
+                  "copy-out pattern");
+    const int ct = (tid & 31) * 8, rt0 = tid >> 5;
+    OutT* const lane_out = out + (r0 / 128) * rt_stride + (c0 / 128 + ct / 128) * ct_stride +
+                           (ct % 128) + static_cast<int64_t>(rt0) * ldo;
+    u32x4 piece[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) piece[q] = *reinterpret_cast<const u32x4*>(sth + (rt0 + 16 * q) * SH + ct);
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const int64_t step = (q >= 8 ? rt_stride : 0) + static_cast<int64_t>(16 * (q & 7)) * ldo;
+      if (!edge || (rt0 + 16 * q < rstore && ct < cstore))
+        __builtin_nontemporal_store(piece[q], reinterpret_cast<u32x4*>(lane_out + step));
     }
   }
 }
@@ -362,24 +374,26 @@ tile_order_kernel(const int32_t* __restrict__ cu, int n_seqs, int S_loc, RowMap 
 // R or C), in the tiled layout of launch_gemm_nt; four columns per thread,
 // the splits summed in order (deterministic). alpha = *alpha_p, or 1 when
 // alpha_p is null.
+// Grid: x over groups of 1024 columns (256 threads x 4), y over rows with a
+// grid-stride loop; a row's place in the tiled layout is worked out once per
+// row, a column's once per thread.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t PR, int64_t PC,
                      float* __restrict__ out, int64_t ldo, int64_t rt_stride, int64_t ct_stride,
                      int64_t R, int64_t C, int64_t R_store, int64_t C_store,
                      const float* __restrict__ alpha_p) {
   const float alpha = alpha_p != nullptr ? alpha_p[0] : 1.f;
-  const int64_t cq = C_store / 4, n = R_store * cq;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t r = e / cq, c = (e % cq) * 4;
+  const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (c >= C_store) return;
+  const int64_t col_off = (c / 128) * ct_stride + c % 128;
+  for (int64_t r = blockIdx.y; r < R_store; r += gridDim.y) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(part + (z * PR + r) * PC + c);
     acc *= alpha;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (r >= R || c + q >= C) acc[q] = 0.f;
-    *reinterpret_cast<f32x4*>(out + (r / 128) * rt_stride + (r % 128) * ldo + (c / 128) * ct_stride +
-                              c % 128) = acc;
+    *reinterpret_cast<f32x4*>(out + (r / 128) * rt_stride + (r % 128) * ldo + col_off) = acc;
   }
 }
 
@@ -588,9 +602,9 @@ mla_status launch_gemm_nt(const void* X, int64_t ldx, int64_t R, const void* Y, 
   else
     return fail(MLA_ERR_UNSUPPORTED, "%s: GEMM type combination not built", name);
   if (sp > 1) {
-    const int64_t n = R_store * (C_store / 4);
-    const unsigned g = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 16384));
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(g), dim3(256), 0, st, part, sp, n_tr * GT,
+    const unsigned gx = static_cast<unsigned>((C_store / 4 + 255) / 256);
+    const unsigned gy = static_cast<unsigned>(std::min<int64_t>(R_store, 65535));
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(gx, gy), dim3(256), 0, st, part, sp, n_tr * GT,
                        n_tc * GT, static_cast<float*>(out), ldo, rt_stride, ct_stride, R, C,
                        R_store, C_store, alpha);
   }
