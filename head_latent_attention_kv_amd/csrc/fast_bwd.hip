@@ -970,30 +970,6 @@ zero_rows_kernel(float* __restrict__ p, int64_t n) {
 // out of the launcher once it has happened: an error return after the fork
 // must not leave work on the side stream unordered with the caller's later
 // work (or leave a graph capture with a stream that never rejoins it).
-class SideFork {
- public:
-  SideFork(const SideStream& s, hipStream_t main) : s_(s), main_(main) {}
-  ~SideFork() {
-    if (forked_) (void)side_join(s_, main_);
-  }
-  SideFork(const SideFork&) = delete;
-  SideFork& operator=(const SideFork&) = delete;
-  mla_status fork() {
-    const mla_status r = side_fork(s_, main_);
-    forked_ = r == MLA_OK;
-    return r;
-  }
-  mla_status join() {
-    forked_ = false;
-    return side_join(s_, main_);
-  }
-
- private:
-  SideStream s_;
-  hipStream_t main_;
-  bool forked_ = false;
-};
-
 unsigned grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   return static_cast<unsigned>(g < 1 ? 1 : (g > 16384 ? 16384 : g));
@@ -1076,7 +1052,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
   // keys (row-major, with the rope key) and V key-major
-  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, nullptr, Vkm, st)) != MLA_OK)
+  if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, Vkm, st, st2)) != MLA_OK)
     return s;
   if ((s = fork.join()) != MLA_OK) return s;
   const float scale_log2 = p.scale * kLog2e;

@@ -310,18 +310,23 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 // Rebuild per-head keys and values from the latent (MFMA GEMMs), in the
 // layouts the attention kernels read; null outputs are skipped.
 //   Kfull  [n_h][Kpad][192]  key rows: K_nope | k_rope       (forward, backward)
-//   KfullT [n_h][192][Kpad]  its transpose                    (backward dQ)
 //   Vt     [n_h][128][Kpad]  V transposed                     (forward)
 //   Vkm    [n_h][Kpad][128]  V key rows                       (backward)
-// WT receives [W_UK | W_UV] transposed (bf16 [2*n_h*128][d_c]).
+// WT receives [W_UK | W_UV] transposed (bf16 [2*n_h*128][d_c]). The rope
+// key's copy into Kfull (its own 128-byte lines of each key row) goes to
+// `side` when given, beside the GEMMs.
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
-                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* KfullT,
-                           _Float16* Vt, _Float16* Vkm, hipStream_t st) {
+                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* Vt,
+                           _Float16* Vkm, hipStream_t st, hipStream_t side) {
   const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
   const uint16_t* ckv = static_cast<const uint16_t*>(c_kv) + p.key_lo * p.d_c;
   const uint16_t* kr = static_cast<const uint16_t*>(k_rope) + p.key_lo * 64;
   const uint16_t* WTv = WT + nk * p.d_c;
   mla_status s;
+  if (Kfull &&
+      (s = launch_broadcast_rows_f16(kr, 64, p.Kn, p.Kpad, 64, Kfull + 128, 192, p.Kpad * 192, p.n_h,
+                                     side != nullptr ? side : st, "prep_rope")) != MLA_OK)
+    return s;
   if ((s = launch_transpose(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, WT, p.d_c,
                             0, Elem::BF16, 1, st, "prep_w")) != MLA_OK) return s;
   if ((s = launch_transpose(static_cast<const uint16_t*>(W_UV), nk, 0, p.d_c, p.d_c, nk,
@@ -331,18 +336,6 @@ mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, 
     // Out[key][h*128 + d] = c_kv[key] . WT[h*128 + d] -> Kfull[h][key][d]
     if ((s = launch_gemm_nt(ckv, p.d_c, p.Kn, WT, p.d_c, nk, p.d_c, Kfull, 192, 128 * 192,
                             p.Kpad * 192, p.Kpad, nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
-      return s;
-    if ((s = launch_broadcast_rows_f16(kr, 64, p.Kn, p.Kpad, 64, Kfull + 128, 192, p.Kpad * 192,
-                                       p.n_h, st, "prep_rope")) != MLA_OK)
-      return s;
-  }
-  if (KfullT) {
-    // Out[h*128 + d][key] -> KfullT[h][d][key]
-    if ((s = launch_gemm_nt(WT, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, KfullT, p.Kpad, 192 * p.Kpad,
-                            128, nk, p.Kpad, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
-      return s;
-    if ((s = launch_transpose(kr, 64, 0, p.Kn, p.Kpad, 64, KfullT + 128 * p.Kpad, p.Kpad,
-                              192 * p.Kpad, Elem::F16, p.n_h, st, "prep_rope")) != MLA_OK)
       return s;
   }
   if (Vt &&
@@ -369,8 +362,18 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.WT);
   _Float16* Kfull = reinterpret_cast<_Float16*>(ws + L.Kfull);
   _Float16* Vt = reinterpret_cast<_Float16*>(ws + L.Vt);
-  mla_status s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, nullptr, Vt, nullptr, st);
+  // the rope-key copy runs on a side stream beside the GEMMs, joined back
+  // before the attention reads Kfull
+  SideStream side;
+  mla_status s = side_stream(&side);
   if (s != MLA_OK) return s;
+  {
+    SideFork fork(side, st);
+    if ((s = fork.fork()) != MLA_OK) return s;
+    if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, Vt, nullptr, st, side.st)) != MLA_OK)
+      return s;
+    if ((s = fork.join()) != MLA_OK) return s;
+  }
   const int n_qt = static_cast<int>((p.S_loc + FQ - 1) / FQ);
   const int64_t blocks = static_cast<int64_t>(n_qt) * p.n_h;
   if (blocks > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups");

@@ -150,6 +150,31 @@ struct SideStream {
 mla_status side_stream(SideStream* out);
 mla_status side_fork(const SideStream& s, hipStream_t main);
 mla_status side_join(const SideStream& s, hipStream_t main);
+// Joins the side stream back into the caller's on every way out once the
+// fork has succeeded, error returns included.
+class SideFork {
+ public:
+  SideFork(const SideStream& s, hipStream_t main) : s_(s), main_(main) {}
+  ~SideFork() {
+    if (forked_) (void)side_join(s_, main_);
+  }
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+  mla_status fork() {
+    const mla_status r = side_fork(s_, main_);
+    forked_ = r == MLA_OK;
+    return r;
+  }
+  mla_status join() {
+    forked_ = false;
+    return side_join(s_, main_);
+  }
+
+ private:
+  SideStream s_;
+  hipStream_t main_;
+  bool forked_ = false;
+};
 
 // Segment start of global position p (host version; device twin in kernels).
 inline int64_t seg_lo_host(const int32_t* cu, int n_seqs, int64_t p) {
@@ -181,9 +206,11 @@ int64_t gemm_splitk_bytes(int64_t R_store, int64_t C_store, int64_t K);
 mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st);
+// side: a stream forked from st for the rope-key copy into Kfull, which
+// runs beside the GEMMs (st itself when null)
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
-                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* KfullT,
-                           _Float16* Vt, _Float16* Vkm, hipStream_t st);
+                           const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* Vt,
+                           _Float16* Vkm, hipStream_t st, hipStream_t side);
 mla_status fast_decode(const DecodePlan& p, const void* q, const void* c_kv, const void* k_rope,
                        const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                        float* lse, char* ws, hipStream_t st);

@@ -35,12 +35,13 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     with no host synchronisation. Outputs are valid once the stream has
  *     reached the call. Calls that share a workspace must be ordered.
- *   - The fast backward runs some of its kernels on an internal stream of
- *     the current device, forked from `stream` by an event and joined back
- *     into it before the call returns, so ordering on `stream` is as if all
- *     the work were there. That stream and its two events are created on the
- *     first fast backward of each host thread on each device and kept until
- *     the process ends (make that first call outside graph capture).
+ *   - The fast forward and backward run some of their kernels on an internal
+ *     stream of the current device, forked from `stream` by an event and
+ *     joined back into it before the call returns, so ordering on `stream`
+ *     is as if all the work were there. That stream and its two events are
+ *     created on the first fast forward or backward of each host thread on
+ *     each device and kept until the process ends (make that first call
+ *     outside graph capture).
  *   - Validation happens on the host before anything is enqueued. On error
  *     nothing is enqueued, the status is returned and a message is kept for
  *     mla_laga_last_error() (per thread). A failed launch returns MLA_ERR_HIP.
