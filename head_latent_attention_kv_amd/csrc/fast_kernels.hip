@@ -437,6 +437,72 @@ transpose_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batc
   }
 }
 
+// Eight bf16 values as OutT (fp16 converted, raw 16-bit copied).
+template <typename OutT>
+__device__ __forceinline__ u32x4 from_bf16x8(u32x4 v) {
+  if constexpr (__is_same(OutT, uint16_t)) {
+    return v;
+  } else {
+    return __builtin_bit_cast(u32x4, bf16x8_to_half8(v));
+  }
+}
+
+// The same transpose with 16-byte accesses, for 64-column tiles and 8-row
+// pieces: a thread loads 8 consecutive columns of a row, then stores 8
+// consecutive rows of a column, so a wave instruction moves eight full
+// 128-byte row segments each way. cols % 64 == 0, rows % 8 == 0, leading
+// dimensions and batch strides multiples of 8, 16-byte aligned bases; rows
+// from rows_valid on read as zero.
+template <typename OutT>
+__global__ void __launch_bounds__(256)
+transpose_v_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
+                   int64_t rows_valid, int64_t rows, OutT* __restrict__ out, int64_t ld_out,
+                   int64_t out_batch) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][72];   // 144-byte rows
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  in += blockIdx.z * in_batch + c0;
+  out += blockIdx.z * out_batch + r0;
+  const int a = threadIdx.x >> 3, b = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int rr = a + 32 * it;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + rr < rows_valid) v = *reinterpret_cast<const u32x4*>(in + (r0 + rr) * ld_in + b);
+    *reinterpret_cast<u32x4*>(&t[rr][b]) = v;
+  }
+  __syncthreads();
+  if (r0 + b >= rows) return;   // whole 8-row pieces (rows % 8 == 0)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int cc = a + 32 * it;
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = static_cast<uint32_t>(t[b + 2 * k][cc]) | (static_cast<uint32_t>(t[b + 2 * k + 1][cc]) << 16);
+    *reinterpret_cast<u32x4*>(out + (c0 + cc) * ld_out + b) = from_bf16x8<OutT>(v);
+  }
+}
+
+// Row-wise conversion with 16-byte accesses: grid x over groups of 2048
+// columns (256 threads x 8), y over rows with a grid-stride loop. cols,
+// leading dimensions and batch strides multiples of 8, 16-byte aligned bases.
+template <typename OutT>
+__global__ void __launch_bounds__(256)
+convert_v_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
+                 int64_t rows_valid, int64_t rows, int64_t cols, OutT* __restrict__ out,
+                 int64_t ld_out, int64_t out_batch) {
+  const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (c >= cols) return;
+  in += blockIdx.z * in_batch + c;
+  out += blockIdx.z * out_batch + c;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows_valid) v = from_bf16x8<OutT>(*reinterpret_cast<const u32x4*>(in + r * ld_in));
+    *reinterpret_cast<u32x4*>(out + r * ld_out) = v;
+  }
+}
+
 template <typename OutT>
 __global__ void __launch_bounds__(256)
 convert_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
@@ -454,28 +520,28 @@ convert_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
 }
 
 // out[b][r][0..cols) = fp16(in[r][0..cols)) for r < rows_valid, 0 for
-// rows_valid <= r < rows; b < batch (out advanced by out_batch). 16 bytes per
-// thread; cols, ld_in and ld_out multiples of 8.
+// rows_valid <= r < rows; b < batch (out advanced by out_batch). A thread
+// converts one 16-byte piece of a row once and writes it to the batch
+// entries b = blockIdx.y, blockIdx.y + gridDim.y, ...; cols, ld_in and
+// ld_out multiples of 8, rows * cols / 8 below 2^31.
 __global__ void __launch_bounds__(256)
 broadcast_rows_f16_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t rows_valid,
                           int64_t rows, int cols, _Float16* __restrict__ out, int64_t ld_out,
                           int64_t out_batch, int batch) {
   const int cpr = cols / 8;
-  const int64_t n = static_cast<int64_t>(batch) * rows * cpr;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int c = static_cast<int>(e % cpr);
-    const int64_t r = (e / cpr) % rows;
-    const int64_t b = e / (cpr * rows);
-    half8 v;
-    if (r < rows_valid) {
-      v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(in + r * ld_in + c * 8));
-    } else {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * cpr) return;
+  const int r = e / cpr, c = e - r * cpr;
+  half8 v;
+  if (r < rows_valid) {
+    v = bf16x8_to_half8(*reinterpret_cast<const u32x4*>(in + r * ld_in + c * 8));
+  } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
-    }
-    *reinterpret_cast<half8*>(out + b * out_batch + r * ld_out + c * 8) = v;
+    for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
   }
+  _Float16* o = out + r * ld_out + c * 8;
+  for (int b = blockIdx.y; b < batch; b += gridDim.y)
+    *reinterpret_cast<half8*>(o + b * out_batch) = v;
 }
 
 }  // namespace
@@ -486,13 +552,21 @@ mla_status launch_broadcast_rows_f16(const uint16_t* in, int64_t ld_in, int64_t 
                                      const char* name) {
   if (cols % 8 || ld_in % 8 || ld_out % 8 || out_batch % 8)
     return fail(MLA_ERR_UNSUPPORTED, "%s: widths must be multiples of 8", name);
-  int64_t blocks = (static_cast<int64_t>(batch) * rows * (cols / 8) + 255) / 256;
-  blocks = blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks);
+  const int64_t pieces = rows * (cols / 8);
+  if (pieces >= (int64_t(1) << 31)) return fail(MLA_ERR_UNSUPPORTED, "%s: too many rows", name);
+  if (pieces == 0 || batch <= 0) return MLA_OK;
+  const unsigned gx = static_cast<unsigned>((pieces + 255) / 256);
+  // about 16 batch entries per thread, at least 2048 workgroups when there are that many
+  unsigned gy = static_cast<unsigned>((batch + 15) / 16);
+  while (gy < static_cast<unsigned>(batch) && static_cast<int64_t>(gx) * gy < 2048) gy *= 2;
+  gy = std::min<unsigned>(gy, static_cast<unsigned>(batch));
   KernelTimer kt(name, st);
-  hipLaunchKernelGGL(broadcast_rows_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     st, in, ld_in, rows_valid, rows, cols, out, ld_out, out_batch, batch);
+  hipLaunchKernelGGL(broadcast_rows_f16_kernel, dim3(gx, gy), dim3(256), 0, st, in, ld_in,
+                     rows_valid, rows, cols, out, ld_out, out_batch, batch);
   return check_launch(name);
 }
+
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                             int64_t rows, int64_t cols, void* out, int64_t ld_out,
@@ -501,7 +575,15 @@ mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch,
   dim3 grid(static_cast<unsigned>((cols + 63) / 64), static_cast<unsigned>((rows + 63) / 64),
             static_cast<unsigned>(batch));
   KernelTimer kt(name, st);
-  if (out_t == Elem::F16)
+  const bool vec = cols % 64 == 0 && rows % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 &&
+                   in_batch % 8 == 0 && out_batch % 8 == 0 && al16(in) && al16(out);
+  if (vec && out_t == Elem::F16)
+    hipLaunchKernelGGL(transpose_v_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
+                       rows_valid, rows, static_cast<_Float16*>(out), ld_out, out_batch);
+  else if (vec)
+    hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, grid, dim3(256), 0, st, in, ld_in, in_batch,
+                       rows_valid, rows, static_cast<uint16_t*>(out), ld_out, out_batch);
+  else if (out_t == Elem::F16)
     hipLaunchKernelGGL(transpose_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
   else
@@ -513,11 +595,24 @@ mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch,
 mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                           int64_t rows, int64_t cols, void* out, int64_t ld_out, int64_t out_batch,
                           Elem out_t, int batch, hipStream_t st, const char* name) {
+  KernelTimer kt(name, st);
+  if (cols % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && in_batch % 8 == 0 &&
+      out_batch % 8 == 0 && al16(in) && al16(out)) {
+    if (rows <= 0 || cols <= 0) return MLA_OK;
+    const dim3 vgrid(static_cast<unsigned>((cols / 8 + 255) / 256),
+                     static_cast<unsigned>(std::min<int64_t>(rows, 65535)), static_cast<unsigned>(batch));
+    if (out_t == Elem::F16)
+      hipLaunchKernelGGL(convert_v_kernel<_Float16>, vgrid, dim3(256), 0, st, in, ld_in, in_batch,
+                         rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
+    else
+      hipLaunchKernelGGL(convert_v_kernel<uint16_t>, vgrid, dim3(256), 0, st, in, ld_in, in_batch,
+                         rows_valid, rows, cols, static_cast<uint16_t*>(out), ld_out, out_batch);
+    return check_launch(name);
+  }
   int64_t blocks = (rows * cols + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   dim3 grid(static_cast<unsigned>(blocks), 1, static_cast<unsigned>(batch));
-  KernelTimer kt(name, st);
   if (out_t == Elem::F16)
     hipLaunchKernelGGL(convert_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
