@@ -129,49 +129,71 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
   const int h = blockIdx.y;
   const float dsc = sc[0];
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  // D: each wave 16 rows, each lane 2 columns
-  for (int rr = 0; rr < 16; ++rr) {
-    const int64_t i = i0 + w * 16 + rr;
-    float v = 0.f;
-    if (i < S_loc) {
-      const int64_t base = (i * n_h + h) * DV + 2 * lane;
-      v = (bf16_to_f32(dout[base]) * dsc) * out[base] + (bf16_to_f32(dout[base + 1]) * dsc) * out[base + 1];
-    }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-    if (lane == 0) {
-      D[h * S_pad + i] = v;
-      uint32_t* blk = info + (static_cast<int64_t>(h) * (S_pad / 32) + i / 32) * 128;
-      const int r = static_cast<int>(i % 32);
-      const bool ok = i < S_loc;
-      blk[r] = __float_as_uint(ok ? lse[i * n_h + h] * kLog2e : 0.f);
-      blk[32 + r] = __float_as_uint(v);
-      const int pos = rm_pos(rm, static_cast<int>(i));
-      blk[64 + r] = ok ? static_cast<uint32_t>(seg_lo_dev(cu, n_seqs, pos)) : 0x7fffffffu;
-      blk[96 + r] = ok ? static_cast<uint32_t>(pos) : 0xffffffffu;
-    }
+  const int tid = threadIdx.x;
+  // row info except D: one thread per row
+  if (tid < 64) {
+    const int64_t i = i0 + tid;
+    uint32_t* blk = info + (static_cast<int64_t>(h) * (S_pad / 32) + i / 32) * 128;
+    const int r = static_cast<int>(i % 32);
+    const bool ok = i < S_loc;
+    blk[r] = __float_as_uint(ok ? lse[i * n_h + h] * kLog2e : 0.f);
+    const int pos = rm_pos(rm, static_cast<int>(i));
+    blk[64 + r] = ok ? static_cast<uint32_t>(seg_lo_dev(cu, n_seqs, pos)) : 0x7fffffffu;
+    blk[96 + r] = ok ? static_cast<uint32_t>(pos) : 0xffffffffu;
   }
-  // q then dout, 16 bytes per thread
-  for (int pass = 0; pass < 2; ++pass) {
-    const int width = pass == 0 ? DQK : DV;
-    const uint16_t* src = pass == 0 ? q : dout;
-    _Float16* nat = (pass == 0 ? Qn : dOn) + static_cast<int64_t>(h) * S_pad * width;
-    const int chunks = width / 8;
+  // q to fp16, 16 bytes per thread
+  {
+    _Float16* nat = Qn + static_cast<int64_t>(h) * S_pad * DQK;
+    constexpr int chunks = DQK / 8;
     for (int e = tid; e < 64 * chunks; e += 256) {
       const int row = e / chunks, ch = e % chunks;
       const int64_t i = i0 + row;
       half8 v;
       if (i < S_loc) {
-        v = bf16x8_to_half8_scaled(
-            *reinterpret_cast<const u32x4*>(src + (i * n_h + h) * width + ch * 8),
-            pass == 0 ? 1.f : dsc);
+        v = bf16x8_to_half8_scaled(*reinterpret_cast<const u32x4*>(q + (i * n_h + h) * DQK + ch * 8), 1.f);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
       }
-      *reinterpret_cast<half8*>(nat + (i0 + row) * width + ch * 8) = v;
+      *reinterpret_cast<half8*>(nat + (i0 + row) * DQK + ch * 8) = v;
+    }
+  }
+  // 2^e dout to fp16 and D in the same pass: the 16 threads of a row each
+  // take 8 columns of dout and out (16-byte loads) and sum their products
+  // across the 16 lanes
+  {
+    _Float16* nat = dOn + static_cast<int64_t>(h) * S_pad * DV;
+    const int ch = tid & 15;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = (tid >> 4) + 16 * it;
+      const int64_t i = i0 + row;
+      half8 v;
+      float part = 0.f;
+      if (i < S_loc) {
+        const int64_t base = (i * n_h + h) * DV + ch * 8;
+        const u32x4 d = *reinterpret_cast<const u32x4*>(dout + base);
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(out + base);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(out + base + 4);
+        v = bf16x8_to_half8_scaled(d, dsc);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = __uint_as_float(d[k] << 16) * dsc, hi = __uint_as_float(d[k] & 0xffff0000u) * dsc;
+          const float olo = k < 2 ? o0[2 * k] : o1[2 * k - 4], ohi = k < 2 ? o0[2 * k + 1] : o1[2 * k - 3];
+          part = fmaf(lo, olo, part);
+          part = fmaf(hi, ohi, part);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = static_cast<_Float16>(0.f);
+      }
+      *reinterpret_cast<half8*>(nat + (i0 + row) * DV + ch * 8) = v;
+#pragma unroll
+      for (int sft = 8; sft >= 1; sft >>= 1) part += __shfl_xor(part, sft, 16);
+      if (ch == 0) {
+        D[h * S_pad + i] = part;
+        info[(static_cast<int64_t>(h) * (S_pad / 32) + i / 32) * 128 + 32 + i % 32] = __float_as_uint(part);
+      }
     }
   }
 }
@@ -959,11 +981,15 @@ reduce_rope_kernel(const float* __restrict__ dKr, const float* __restrict__ sc,
   }
 }
 
+// p[0, n) = 0: 16-byte stores (p 16-byte aligned), the last n % 4 one by one
 __global__ void __launch_bounds__(256)
 zero_rows_kernel(float* __restrict__ p, int64_t n) {
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
+  const int64_t n4 = n / 4;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n4;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[e] = 0.f;
+    reinterpret_cast<f32x4*>(p)[e] = z;
+  if (blockIdx.x == 0 && threadIdx.x < n - 4 * n4) p[4 * n4 + threadIdx.x] = 0.f;
 }
 
 // The side stream's fork, joined back into the caller's stream on every way
@@ -1023,6 +1049,18 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   SideFork fork(side, st);
   if ((s = fork.fork()) != MLA_OK) return s;
 
+  // rows of dc_kv outside the shard's keys get no gradient; no other kernel
+  // writes them
+  if (p.key_lo > 0 || p.key_hi < p.S) {
+    KernelTimer kt("zero_rows", st2);
+    if (p.key_lo > 0)
+      hipLaunchKernelGGL(zero_rows_kernel, dim3(grid_for(p.key_lo * p.d_c / 4)), dim3(256), 0, st2,
+                         dc_kv, p.key_lo * p.d_c);
+    if (p.key_hi < p.S)
+      hipLaunchKernelGGL(zero_rows_kernel, dim3(grid_for((p.S - p.key_hi) * p.d_c / 4)), dim3(256), 0,
+                         st2, dc_kv + p.key_hi * p.d_c, (p.S - p.key_hi) * p.d_c);
+  }
+  if ((s = check_launch("zero rows")) != MLA_OK) return s;
   // [W_UK | W_UV] rows in fp16 and c_kv^T in fp16 for the gradient GEMMs
   if ((s = launch_convert(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, W16, 2 * nk,
                           0, Elem::F16, 1, st2, "prep_w16")) != MLA_OK)
@@ -1105,16 +1143,6 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                           p.d_c, 128 * p.d_c, 128, p.Kn, p.d_c, Elem::F16, Elem::F32, st,
                           "grad_latent", gpart, gpart_bytes, dsc + 1)) != MLA_OK)
     return s;
-  {
-    KernelTimer kt("zero_rows", st);
-    if (p.key_lo > 0)
-      hipLaunchKernelGGL(zero_rows_kernel, dim3(grid_for(p.key_lo * p.d_c)), dim3(256), 0, st,
-                         dc_kv, p.key_lo * p.d_c);
-    if (p.key_hi < p.S)
-      hipLaunchKernelGGL(zero_rows_kernel, dim3(grid_for((p.S - p.key_hi) * p.d_c)), dim3(256), 0,
-                         st, dc_kv + p.key_hi * p.d_c, (p.S - p.key_hi) * p.d_c);
-  }
-  if ((s = check_launch("zero rows")) != MLA_OK) return s;
   // dW_UK = c_kv^T dK_nope, dW_UV = c_kv^T dV (contract over the shard's
   // keys): the dKV rows are read k-major (key rows, 2 n_h 128 columns)
   if ((s = launch_gemm_nt(ckvT, p.Kpad, p.d_c, dKV, 2 * nk, nk, p.Kpad, dW_UK, nk, 128 * nk, 128,
