@@ -12,13 +12,16 @@ enum class Elem { BF16, F16, F32 };
 
 // out[c][r] = conv(in[r][c]) for r < rows_valid (0 for rows_valid <= r < rows),
 // c < cols; `batch` independent copies, in/out advanced by in_batch/out_batch
-// elements. in is bf16; out is bf16 or fp16.
+// elements. in is bf16; out is bf16 or fp16. cols a multiple of 64, rows of
+// 8, leading dimensions and batch strides of 8, both buffers 16-byte aligned
+// (MLA_ERR_UNSUPPORTED otherwise, before any launch).
 mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                             int64_t rows, int64_t cols, void* out, int64_t ld_out,
                             int64_t out_batch, Elem out_t, int batch, hipStream_t st,
                             const char* name);
 
-// out[r][c] = conv(in[r][c]) with the same conventions (no transpose).
+// out[r][c] = conv(in[r][c]) with the same conventions (no transpose); cols,
+// leading dimensions and batch strides multiples of 8, 16-byte aligned.
 mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                           int64_t rows, int64_t cols, void* out, int64_t ld_out, int64_t out_batch,
                           Elem out_t, int batch, hipStream_t st, const char* name);

@@ -404,39 +404,6 @@ int gemm_splits(int64_t R_store, int64_t C_store, int64_t K) {
   return s;
 }
 
-template <typename OutT>
-__device__ __forceinline__ OutT from_bf16(uint16_t b) {
-  if constexpr (sizeof(OutT) == 2 && __is_same(OutT, uint16_t)) {
-    return b;
-  } else {
-    return static_cast<OutT>(bf16_to_f32(b));
-  }
-}
-
-// 64x64 tile transpose through LDS; grid (cols/64, rows/64, batch).
-template <typename OutT>
-__global__ void __launch_bounds__(256)
-transpose_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
-                 int64_t rows_valid, int64_t rows, int64_t cols, OutT* __restrict__ out,
-                 int64_t ld_out, int64_t out_batch) {
-  __shared__ uint16_t t[64][65];
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  in += blockIdx.z * in_batch;
-  out += blockIdx.z * out_batch;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    t[rr][cc] = (r < rows_valid && c < cols) ? in[r * ld_in + c] : static_cast<uint16_t>(0);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int cc = e >> 6, rr = e & 63;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    if (r < rows && c < cols) out[c * ld_out + r] = from_bf16<OutT>(t[rr][cc]);
-  }
-}
-
 // Eight bf16 values as OutT (fp16 converted, raw 16-bit copied).
 template <typename OutT>
 __device__ __forceinline__ u32x4 from_bf16x8(u32x4 v) {
@@ -447,10 +414,10 @@ __device__ __forceinline__ u32x4 from_bf16x8(u32x4 v) {
   }
 }
 
-// The same transpose with 16-byte accesses, for 64-column tiles and 8-row
-// pieces: a thread loads 8 consecutive columns of a row, then stores 8
-// consecutive rows of a column, so a wave instruction moves eight full
-// 128-byte row segments each way. cols % 64 == 0, rows % 8 == 0, leading
+// Transpose through a 64x64 LDS tile (grid: cols / 64, rows / 64, batch)
+// with 16-byte accesses: a thread loads 8 consecutive columns of a row, then
+// stores 8 consecutive rows of a column, so a wave instruction moves eight
+// full 128-byte row segments each way. cols % 64 == 0, rows % 8 == 0, leading
 // dimensions and batch strides multiples of 8, 16-byte aligned bases; rows
 // from rows_valid on read as zero.
 template <typename OutT>
@@ -500,22 +467,6 @@ convert_v_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batc
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < rows_valid) v = from_bf16x8<OutT>(*reinterpret_cast<const u32x4*>(in + r * ld_in));
     *reinterpret_cast<u32x4*>(out + r * ld_out) = v;
-  }
-}
-
-template <typename OutT>
-__global__ void __launch_bounds__(256)
-convert_kernel(const uint16_t* __restrict__ in, int64_t ld_in, int64_t in_batch,
-               int64_t rows_valid, int64_t rows, int64_t cols, OutT* __restrict__ out,
-               int64_t ld_out, int64_t out_batch) {
-  in += blockIdx.z * in_batch;
-  out += blockIdx.z * out_batch;
-  const int64_t n = rows * cols;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t r = e / cols, c = e % cols;
-    out[r * ld_out + c] =
-        r < rows_valid ? from_bf16<OutT>(in[r * ld_in + c]) : static_cast<OutT>(0);
   }
 }
 
@@ -574,50 +525,36 @@ mla_status launch_transpose(const uint16_t* in, int64_t ld_in, int64_t in_batch,
                             const char* name) {
   dim3 grid(static_cast<unsigned>((cols + 63) / 64), static_cast<unsigned>((rows + 63) / 64),
             static_cast<unsigned>(batch));
+  // every caller passes 64-multiple widths and 16-byte aligned buffers (the
+  // fast path's shape checks guarantee them)
+  if (cols % 64 != 0 || rows % 8 != 0 || ld_in % 8 != 0 || ld_out % 8 != 0 || in_batch % 8 != 0 ||
+      out_batch % 8 != 0 || !al16(in) || !al16(out))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: transpose needs 64-column and 8-row multiples, 16-byte alignment", name);
   KernelTimer kt(name, st);
-  const bool vec = cols % 64 == 0 && rows % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 &&
-                   in_batch % 8 == 0 && out_batch % 8 == 0 && al16(in) && al16(out);
-  if (vec && out_t == Elem::F16)
+  if (out_t == Elem::F16)
     hipLaunchKernelGGL(transpose_v_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, static_cast<_Float16*>(out), ld_out, out_batch);
-  else if (vec)
+  else
     hipLaunchKernelGGL(transpose_v_kernel<uint16_t>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, static_cast<uint16_t*>(out), ld_out, out_batch);
-  else if (out_t == Elem::F16)
-    hipLaunchKernelGGL(transpose_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
-                       rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
-  else
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, st, in, ld_in, in_batch,
-                       rows_valid, rows, cols, static_cast<uint16_t*>(out), ld_out, out_batch);
   return check_launch(name);
 }
 
 mla_status launch_convert(const uint16_t* in, int64_t ld_in, int64_t in_batch, int64_t rows_valid,
                           int64_t rows, int64_t cols, void* out, int64_t ld_out, int64_t out_batch,
                           Elem out_t, int batch, hipStream_t st, const char* name) {
+  if (cols % 8 != 0 || ld_in % 8 != 0 || ld_out % 8 != 0 || in_batch % 8 != 0 || out_batch % 8 != 0 ||
+      !al16(in) || !al16(out))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: conversion needs 8-element multiples, 16-byte alignment", name);
+  if (rows <= 0 || cols <= 0) return MLA_OK;
   KernelTimer kt(name, st);
-  if (cols % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && in_batch % 8 == 0 &&
-      out_batch % 8 == 0 && al16(in) && al16(out)) {
-    if (rows <= 0 || cols <= 0) return MLA_OK;
-    const dim3 vgrid(static_cast<unsigned>((cols / 8 + 255) / 256),
-                     static_cast<unsigned>(std::min<int64_t>(rows, 65535)), static_cast<unsigned>(batch));
-    if (out_t == Elem::F16)
-      hipLaunchKernelGGL(convert_v_kernel<_Float16>, vgrid, dim3(256), 0, st, in, ld_in, in_batch,
-                         rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
-    else
-      hipLaunchKernelGGL(convert_v_kernel<uint16_t>, vgrid, dim3(256), 0, st, in, ld_in, in_batch,
-                         rows_valid, rows, cols, static_cast<uint16_t*>(out), ld_out, out_batch);
-    return check_launch(name);
-  }
-  int64_t blocks = (rows * cols + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  dim3 grid(static_cast<unsigned>(blocks), 1, static_cast<unsigned>(batch));
+  const dim3 grid(static_cast<unsigned>((cols / 8 + 255) / 256),
+                  static_cast<unsigned>(std::min<int64_t>(rows, 65535)), static_cast<unsigned>(batch));
   if (out_t == Elem::F16)
-    hipLaunchKernelGGL(convert_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
+    hipLaunchKernelGGL(convert_v_kernel<_Float16>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, cols, static_cast<_Float16*>(out), ld_out, out_batch);
   else
-    hipLaunchKernelGGL(convert_kernel<uint16_t>, grid, dim3(256), 0, st, in, ld_in, in_batch,
+    hipLaunchKernelGGL(convert_v_kernel<uint16_t>, grid, dim3(256), 0, st, in, ld_in, in_batch,
                        rows_valid, rows, cols, static_cast<uint16_t*>(out), ld_out, out_batch);
   return check_launch(name);
 }
