@@ -149,7 +149,7 @@ BwdLayout bwd_layout(const Plan& p) {
     off += align_up(bytes, kAlign);
     return o;
   };
-  L.KfullT = L.Vkm = L.W16 = L.ckvT = L.Qn = L.Qt = L.dOn = L.dOt = L.info = L.gpart = L.order = -1;
+  L.Vkm = L.W16 = L.ckvT = L.Qn = L.dOn = L.info = L.gpart = L.order = -1;
   L.dS = L.dscale = -1;
   if (p.fast_bwd) {
     const int64_t nk = static_cast<int64_t>(p.n_h) * 128;

@@ -49,10 +49,10 @@ struct BwdLayout {
   //             (dV unused), dKrope fp32 [n_h][Kpad][64]
   int64_t D, dK, dV, dKrope;
   // fast path only (fp16): V key-major [n_h][Kpad][128], [W_UK | W_UV]
-  // [d_c][2*n_h*128], c_kv^T [d_c][Kpad], q and dout per head [n_h][S_pad][.].
-  // KfullT, Qt and dOt stay -1: the kernels read those transposes from the
-  // row-major tiles with transposed LDS reads.
-  int64_t KfullT, Vkm, W16, ckvT, Qn, Qt, dOn, dOt;
+  // [d_c][2*n_h*128], c_kv^T [d_c][Kpad], q and dout per head [n_h][S_pad][.]
+  // (the kernels read the transposes of K, q and dout from these row-major
+  // tiles with transposed LDS reads)
+  int64_t Vkm, W16, ckvT, Qn, dOn;
   int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
   int64_t gpart;  // fast path: split-K partial sums of the gradient GEMMs (fp32)
   // fast path, packed calls: query-tile then key-tile order (int32
