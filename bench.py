@@ -76,7 +76,7 @@ def kernel_flops(name, cfg, pairs, kn):
 # stream's kernels: their event times are wall times while sharing the CUs,
 # not the time they take alone.
 SIDE_STREAM_KERNELS = ("prep_rope", "zero_rows", "prep_w16", "prep_ckvT", "dout_scale", "bwd_prep", "attn_bwd_dq",
-                       "attn_bwd_dq_ds", "reduce_rope")
+                       "attn_bwd_dq_ds")
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "head_latent_attention_kv_amd", "csrc")

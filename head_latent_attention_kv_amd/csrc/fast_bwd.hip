@@ -1129,12 +1129,6 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                          p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
-  {
-    KernelTimer kt("reduce_rope", st2);
-    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st2, dKr,
-                       dsc, dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
-  }
-  if ((s = check_launch("rope-key gradient reduce")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0
   float* gpart = reinterpret_cast<float*>(at(L.gpart));
   const int64_t gpart_bytes = std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
@@ -1153,6 +1147,15 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
                           128 * nk, 128, p.d_c, nk, Elem::F16, Elem::F32, st, "grad_w", gpart,
                           gpart_bytes, dsc + 1, true)) != MLA_OK)
     return s;
+  // dk_rope = sum over heads of the rope-key partials (HBM-bound): after the
+  // gradient GEMMs, where it runs under the tail of the dQ kernel (MFMA-bound)
+  // on the side stream
+  {
+    KernelTimer kt("reduce_rope", st);
+    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st, dKr,
+                       dsc, dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
+  }
+  if ((s = check_launch("rope-key gradient reduce")) != MLA_OK) return s;
   return fork.join();
 }
 
