@@ -355,6 +355,8 @@ mla_status mla_laga_fwd_workspace_size(const mla_laga_desc* desc, const int32_t*
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   Plan p;
   if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (p.fast)
+    if (mla_status s = fast_fwd_limits(p); s != MLA_OK) return s;
   *bytes = static_cast<size_t>(fwd_layout(p).total + debug_tail());
   return MLA_OK;
 }
@@ -364,6 +366,8 @@ mla_status mla_laga_bwd_workspace_size(const mla_laga_desc* desc, const int32_t*
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
   Plan p;
   if (mla_status s = make_plan(desc, cu_host, &p); s != MLA_OK) return s;
+  if (p.fast)
+    if (mla_status s = fast_bwd_limits(p); s != MLA_OK) return s;
   *bytes = static_cast<size_t>(bwd_layout(p).total + debug_tail());
   return MLA_OK;
 }

@@ -1003,19 +1003,25 @@ unsigned grid_for(int64_t n) {
 
 }  // namespace
 
+mla_status fast_bwd_limits(const Plan& p) {
+  // positions (S + 256), key-row offsets (Kpad 256) and query-row offsets
+  // (S_loc 192) in 32 bits; the GEMMs' operand rows (2 n_h 128 and Kpad
+  // elements) below 2^22
+  if (p.S + 256 >= (int64_t(1) << 31) || p.S_loc * DQK >= (int64_t(1) << 31) ||
+      p.Kpad >= (int64_t(1) << 22) || static_cast<int64_t>(p.n_h) * 256 >= (int64_t(1) << 22))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "fast backward takes n_h < 16384, fewer than 2^22 needed keys, S_loc below 2^31 / 192 "
+                "and S below 2^31 - 256");
+  return MLA_OK;
+}
+
 mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* c_kv,
                     const void* k_rope, const void* W_UK, const void* W_UV,
                     const int32_t* cu_dev, const float* out, const float* lse, float* dq,
                     float* dc_kv, float* dk_rope, float* dW_UK, float* dW_UV, char* ws,
                     hipStream_t st) {
   const BwdLayout L = bwd_layout(p);
-  if (p.Kpad * 256 >= (int64_t(1) << 31) || p.S_loc * DQK >= (int64_t(1) << 31) ||
-      p.S + 256 >= (int64_t(1) << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "fast backward takes fewer than 2^23 rows per call");
-  // the GEMMs' operand rows (2 n_h 128 and Kpad elements) stay below 2^22
-  // elements: checked here, so that no launcher fails after work is enqueued
-  if (static_cast<int64_t>(p.n_h) * 256 >= (int64_t(1) << 22) || p.Kpad >= (int64_t(1) << 22))
-    return fail(MLA_ERR_UNSUPPORTED, "fast backward takes n_h < 16384 and fewer than 2^22 keys");
+  if (mla_status s = fast_bwd_limits(p); s != MLA_OK) return s;
   const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
   const int64_t S_pad = align_up(p.S_loc, 64);
   auto at = [&](int64_t off) { return ws + off; };

@@ -349,16 +349,21 @@ mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, 
   return MLA_OK;
 }
 
+mla_status fast_fwd_limits(const Plan& p) {
+  // positions (S + 256) and key-row offsets (Kpad 192) in 32 bits; the
+  // up-projection GEMM's operand rows (n_h 128 and Kpad elements) below 2^22
+  if (p.S + 256 >= (int64_t(1) << 31) || p.Kpad >= (int64_t(1) << 22) ||
+      static_cast<int64_t>(p.n_h) * 128 >= (int64_t(1) << 22))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "fast forward takes n_h < 32768, fewer than 2^22 needed keys and S below 2^31 - 256");
+  return MLA_OK;
+}
+
 mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st) {
   const FwdLayout L = fwd_layout(p);
-  if (p.Kpad * 192 >= (int64_t(1) << 31) || p.S + 256 >= (int64_t(1) << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "fast path takes fewer than 2^23 latent rows per call");
-  // the up-projection GEMM's operand rows (n_h 128 and Kpad elements) stay
-  // below 2^22 elements: checked before anything is enqueued
-  if (static_cast<int64_t>(p.n_h) * 128 >= (int64_t(1) << 22) || p.Kpad >= (int64_t(1) << 22))
-    return fail(MLA_ERR_UNSUPPORTED, "fast forward takes n_h < 32768 and fewer than 2^22 keys");
+  if (mla_status s = fast_fwd_limits(p); s != MLA_OK) return s;
   uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.WT);
   _Float16* Kfull = reinterpret_cast<_Float16*>(ws + L.Kfull);
   _Float16* Vt = reinterpret_cast<_Float16*>(ws + L.Vt);

@@ -203,6 +203,11 @@ mla_status zero_fill(float* p, int64_t n, hipStream_t st);
 // Bytes of fp32 partial sums launch_gemm_nt uses to split K for an fp32
 // output of R_store x C_store (0 when it does not split).
 int64_t gemm_splitk_bytes(int64_t R_store, int64_t C_store, int64_t K);
+// The fast path's size limits (32-bit element offsets inside the kernels and
+// the GEMM operand limits), checked by the workspace queries and again by
+// the launchers before anything is enqueued: MLA_ERR_UNSUPPORTED past them.
+mla_status fast_fwd_limits(const Plan& p);
+mla_status fast_bwd_limits(const Plan& p);
 mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* k_rope,
                     const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                     float* lse, char* ws, hipStream_t st);

@@ -53,6 +53,12 @@
  *     64 (512 in DeepSeek-V3), any n_h; it keeps the rebuilt K/V and the
  *     softmax weights in fp16 with fp32 accumulation. Every other shape (and
  *     MLA_F32) runs a plain fp32 path of simple kernels.
+ *   - Size limits of the fast path (32-bit offsets inside its kernels):
+ *     fewer than 2^22 needed keys (the keys the shard's rows see, padded to
+ *     256), S below 2^31 - 256, n_h below 32768 for the forward and 16384
+ *     for the backward, S_loc below 2^31 / 192 for the backward. Past them
+ *     the workspace queries and the calls return MLA_ERR_UNSUPPORTED before
+ *     anything is enqueued.
  *   - fp16 ranges of the fast path (normal range 2^-14 .. 65504; below it
  *     values keep an absolute precision of 2^-24, above it they overflow):
  *       forward: q (both parts), k_rope and the rebuilt K_nope = c_kv W_UK

@@ -225,6 +225,35 @@ def test_invalid_arguments_rejected_on_host():
     bad(hla.MLA_ERR_UNSUPPORTED, hla.mla_laga_fwd_workspace_size, d, None)
 
 
+def test_fast_path_size_limits_rejected_on_host(lib):
+    """Shapes past the fast kernels' 32-bit offsets and GEMM operand limits
+    are refused by the workspace queries and by the calls, before any
+    launch (no GPU is touched here)."""
+    cfg = workloads.config("h128_s16k_shard")
+    U = hla.MLA_ERR_UNSUPPORTED
+    S = 1 << 22                         # one query at the end: 2^22 needed keys
+    d, _ = desc_for(cfg, S=S, S_loc=1, q_offset=S - 1, n_h=1)
+    assert lib.mla_laga_uses_fast_path(ctypes.byref(d)) == 1
+    assert "2^22" in bad(U, hla.mla_laga_fwd_workspace_size, d, None)
+    assert "2^22" in bad(U, hla.mla_laga_bwd_workspace_size, d, None)
+    good = ctypes.c_void_p(1 << 20)    # never dereferenced: the limits come first
+    huge = ctypes.c_size_t(1 << 44)
+    assert lib.mla_laga_fwd(ctypes.byref(d), good, good, good, good, good, None, None,
+                            good, good, good, huge, None) == U
+    assert lib.mla_laga_bwd(ctypes.byref(d), good, good, good, good, good, good, None, None,
+                            good, good, good, good, good, good, good, good, huge, None) == U
+    # one key fewer fits
+    d, _ = desc_for(cfg, S=S - 256, S_loc=1, q_offset=S - 257, n_h=1)
+    assert hla.mla_laga_fwd_workspace_size(d, None) > 0
+    assert hla.mla_laga_bwd_workspace_size(d, None) > 0
+    # n_h: the backward's GEMMs take fewer heads than the forward's
+    d, _ = desc_for(cfg, S=256, S_loc=256, q_offset=0, n_h=16384)
+    assert hla.mla_laga_fwd_workspace_size(d, None) > 0
+    assert "n_h" in bad(U, hla.mla_laga_bwd_workspace_size, d, None)
+    d, _ = desc_for(cfg, S=256, S_loc=256, q_offset=0, n_h=32768)
+    assert "n_h" in bad(U, hla.mla_laga_fwd_workspace_size, d, None)
+
+
 def test_null_and_misaligned_pointers_rejected_before_launch(lib):
     cfg = workloads.config("h16_s4k")
     d, _ = desc_for(cfg)
