@@ -1046,9 +1046,10 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
             Kpad = static_cast<int>(p.Kpad);
   mla_status s;
   // The layout conversions and the row preparation do not depend on the K/V
-  // rebuild, and the dQ kernel and the rope-key reduction not on the gradient
-  // GEMMs: each such group runs on a side stream next to the other (HBM-bound
-  // work beside MFMA-bound work).
+  // rebuild, and the dQ kernel not on the gradient GEMMs: each such group
+  // runs on a side stream next to the other (HBM-bound work beside
+  // MFMA-bound work in the first pair; in the second the GEMMs and then the
+  // rope-key reduction run under the longer dQ kernel).
   SideStream side;
   if ((s = side_stream(&side)) != MLA_OK) return s;
   const hipStream_t st2 = side.st;
