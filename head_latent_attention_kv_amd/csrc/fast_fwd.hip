@@ -317,7 +317,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const _Float16* __restrict__ Kfu
 // `side` when given, beside the GEMMs.
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
                            const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* Vt,
-                           _Float16* Vkm, hipStream_t st, hipStream_t side) {
+                           _Float16* Vkm, hipStream_t st, hipStream_t side, const SideStream* vside) {
   const int64_t nk = static_cast<int64_t>(p.n_h) * 128;
   const uint16_t* ckv = static_cast<const uint16_t*>(c_kv) + p.key_lo * p.d_c;
   const uint16_t* kr = static_cast<const uint16_t*>(k_rope) + p.key_lo * 64;
@@ -327,17 +327,21 @@ mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, 
       (s = launch_broadcast_rows_f16(kr, 64, p.Kn, p.Kpad, 64, Kfull + 128, 192, p.Kpad * 192, p.n_h,
                                      side != nullptr ? side : st, "prep_rope")) != MLA_OK)
     return s;
+  // with vside, W_UV's transpose runs on that stream beside the K GEMM and is
+  // joined back before the V GEMM
+  if ((s = launch_transpose(static_cast<const uint16_t*>(W_UV), nk, 0, p.d_c, p.d_c, nk,
+                            WT + nk * p.d_c, p.d_c, 0, Elem::BF16, 1, vside ? vside->st : st,
+                            "prep_w")) != MLA_OK)
+    return s;
   if ((s = launch_transpose(static_cast<const uint16_t*>(W_UK), nk, 0, p.d_c, p.d_c, nk, WT, p.d_c,
                             0, Elem::BF16, 1, st, "prep_w")) != MLA_OK) return s;
-  if ((s = launch_transpose(static_cast<const uint16_t*>(W_UV), nk, 0, p.d_c, p.d_c, nk,
-                            WT + nk * p.d_c, p.d_c, 0, Elem::BF16, 1, st, "prep_w")) != MLA_OK)
-    return s;
   if (Kfull) {
     // Out[key][h*128 + d] = c_kv[key] . WT[h*128 + d] -> Kfull[h][key][d]
     if ((s = launch_gemm_nt(ckv, p.d_c, p.Kn, WT, p.d_c, nk, p.d_c, Kfull, 192, 128 * 192,
                             p.Kpad * 192, p.Kpad, nk, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
       return s;
   }
+  if (vside && (s = side_join(*vside, st)) != MLA_OK) return s;
   if (Vt &&
       (s = launch_gemm_nt(WTv, p.d_c, nk, ckv, p.d_c, p.Kn, p.d_c, Vt, p.Kpad, 128 * p.Kpad, 128, nk,
                           p.Kpad, Elem::BF16, Elem::F16, st, "upproj")) != MLA_OK)
@@ -375,7 +379,7 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
   {
     SideFork fork(side, st);
     if ((s = fork.fork()) != MLA_OK) return s;
-    if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, Vt, nullptr, st, side.st)) != MLA_OK)
+    if ((s = fast_rebuild_kv(p, c_kv, k_rope, W_UK, W_UV, WT, Kfull, Vt, nullptr, st, side.st, &side)) != MLA_OK)
       return s;
     if ((s = fork.join()) != MLA_OK) return s;
   }

@@ -215,7 +215,8 @@ mla_status fast_fwd(const Plan& p, const void* q, const void* c_kv, const void* 
 // runs beside the GEMMs (st itself when null)
 mla_status fast_rebuild_kv(const Plan& p, const void* c_kv, const void* k_rope, const void* W_UK,
                            const void* W_UV, uint16_t* WT, _Float16* Kfull, _Float16* Vt,
-                           _Float16* Vkm, hipStream_t st, hipStream_t side);
+                           _Float16* Vkm, hipStream_t st, hipStream_t side,
+                           const SideStream* vside = nullptr);
 mla_status fast_decode(const DecodePlan& p, const void* q, const void* c_kv, const void* k_rope,
                        const void* W_UK, const void* W_UV, const int32_t* cu_dev, float* out,
                        float* lse, char* ws, hipStream_t st);
