@@ -71,6 +71,10 @@ SMALL = [
     # other latent widths on the fast path
     small_dc("d_c_256", 256, 3, 700, 333, 367),
     small_dc("d_c_1024", 1024, 2, 600, 450, 150, cu=[0, 1, 1, 130, 131, 400, 600]),
+    # the narrowest latent the fast path takes, and one that is not a power of
+    # two: the gradient GEMMs' latent-side tiles end mid-tile
+    small_dc("d_c_64", 64, 2, 500, 300, 200),
+    small_dc("d_c_320", 320, 3, 700, 333, 367, cu=[0, 90, 91, 400, 700]),
 ]
 
 
