@@ -170,7 +170,7 @@ BwdLayout bwd_layout(const Plan& p) {
     L.gpart = take(std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),
                             gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
     L.order = take(4 * ((p.S_loc + 255) / 256 + p.Kpad / 128));
-    L.dscale = take(16 + 4 * kScaleBlocks);
+    L.dscale = take(16 + 4 * kScaleBlocks + 8 * static_cast<int64_t>(p.n_h));
     if (p.ds_store) L.dS = take(p.n_h * p.Kpad * S_pad * 2);
     L.f.total = -1;
   } else {

@@ -41,6 +41,11 @@ namespace {
 
 constexpr int DQK = 192, DV = 128;
 constexpr float kLog2e = 1.44269504088896340736f;
+// The row info holds lse log2(e) - kPShift, so that the dK/dV kernel's
+// weights come out as P 2^kPShift <= 2^15 (P <= 1): a key's weights among
+// many keys (about 1 / keys each) then stay in fp16's normal range down to
+// P = 2^-29 in the dV product. The dQ kernel adds the shift back.
+constexpr int kPShift = 15;
 
 __device__ __forceinline__ void work_item(int bid, int n_h, int n_t, int* h, int* t) {
   // as in the forward: all tiles of a head on one XCD when n_h % 8 == 0
@@ -79,9 +84,13 @@ dout_absmax_kernel(const u32x4* __restrict__ x, int64_t n8, uint32_t* __restrict
 // max|dout|), read off the bf16 exponent (or, for a subnormal maximum, off
 // its leading mantissa bit), clamped to [-126, 126] so that both factors
 // are normal floats. e = 0 when dout is all zero or holds a non-finite value.
+// It also clears hm[0 .. n_hm), the per-head maxima that the row preparation
+// (the next kernel on the stream) raises.
 __global__ void __launch_bounds__(256)
-dout_scale_kernel(const uint32_t* __restrict__ part, int n, float* __restrict__ sc) {
+dout_scale_kernel(const uint32_t* __restrict__ part, int n, float* __restrict__ sc,
+                  uint32_t* __restrict__ hm, int n_hm) {
   __shared__ uint32_t wmax[4];
+  for (int i = threadIdx.x; i < n_hm; i += blockDim.x) hm[i] = 0u;
   uint32_t m = 0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, part[i]);
 #pragma unroll
@@ -120,12 +129,17 @@ __device__ __forceinline__ half8 bf16x8_to_half8_scaled(u32x4 v, float s) {
 // 32-row block the row info the dK/dV kernels read:
 // info[h][i/32] = {lse*log2(e) [32], D [32], sample start [32], position [32]}
 // (rows past S_loc: start INT32_MAX, position -1, so they see no key).
+// hm[2 h] and hm[2 h + 1] are raised (as float bits: non-negative floats
+// order like their bit patterns) to the largest |2^e dout[i,h,:]| (2-norm)
+// and |D[h][i]| over the rows: with a key's |V| row norm they bound every
+// |dP - D| of the key, which sets its dS scale in the dK/dV kernel.
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                 const float* __restrict__ out, const float* __restrict__ lse,
                 const int32_t* __restrict__ cu, const float* __restrict__ sc, float* __restrict__ D,
                 _Float16* __restrict__ Qn, _Float16* __restrict__ dOn, uint32_t* __restrict__ info,
-                int n_h, int n_seqs, int64_t S_loc, int64_t S_pad, RowMap rm) {
+                uint32_t* __restrict__ hm, int n_h, int n_seqs, int64_t S_loc, int64_t S_pad,
+                RowMap rm) {
   const int h = blockIdx.y;
   const float dsc = sc[0];
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
@@ -136,7 +150,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
     uint32_t* blk = info + (static_cast<int64_t>(h) * (S_pad / 32) + i / 32) * 128;
     const int r = static_cast<int>(i % 32);
     const bool ok = i < S_loc;
-    blk[r] = __float_as_uint(ok ? lse[i * n_h + h] * kLog2e : 0.f);
+    blk[r] = __float_as_uint(ok ? lse[i * n_h + h] * kLog2e - kPShift : 0.f);
     const int pos = rm_pos(rm, static_cast<int>(i));
     blk[64 + r] = ok ? static_cast<uint32_t>(seg_lo_dev(cu, n_seqs, pos)) : 0x7fffffffu;
     blk[96 + r] = ok ? static_cast<uint32_t>(pos) : 0xffffffffu;
@@ -160,8 +174,10 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
   }
   // 2^e dout to fp16 and D in the same pass: the 16 threads of a row each
   // take 8 columns of dout and out (16-byte loads) and sum their products
-  // across the 16 lanes
+  // (and the squares of dout) across the 16 lanes
   {
+    __shared__ float wred[2][4];
+    float nmax = 0.f, dmax = 0.f;   // largest |dout row|^2 and |D| of the thread's rows
     _Float16* nat = dOn + static_cast<int64_t>(h) * S_pad * DV;
     const int ch = tid & 15;
 #pragma unroll
@@ -169,7 +185,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
       const int row = (tid >> 4) + 16 * it;
       const int64_t i = i0 + row;
       half8 v;
-      float part = 0.f;
+      float part = 0.f, sq = 0.f;
       if (i < S_loc) {
         const int64_t base = (i * n_h + h) * DV + ch * 8;
         const u32x4 d = *reinterpret_cast<const u32x4*>(dout + base);
@@ -182,6 +198,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
           const float olo = k < 2 ? o0[2 * k] : o1[2 * k - 4], ohi = k < 2 ? o0[2 * k + 1] : o1[2 * k - 3];
           part = fmaf(lo, olo, part);
           part = fmaf(hi, ohi, part);
+          sq = fmaf(lo, lo, fmaf(hi, hi, sq));
         }
       } else {
 #pragma unroll
@@ -189,11 +206,32 @@ bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dou
       }
       *reinterpret_cast<half8*>(nat + (i0 + row) * DV + ch * 8) = v;
 #pragma unroll
-      for (int sft = 8; sft >= 1; sft >>= 1) part += __shfl_xor(part, sft, 16);
+      for (int sft = 8; sft >= 1; sft >>= 1) {
+        part += __shfl_xor(part, sft, 16);
+        sq += __shfl_xor(sq, sft, 16);
+      }
+      nmax = fmaxf(nmax, sq);
+      dmax = fmaxf(dmax, fabsf(part));
       if (ch == 0) {
         D[h * S_pad + i] = part;
         info[(static_cast<int64_t>(h) * (S_pad / 32) + i / 32) * 128 + 32 + i % 32] = __float_as_uint(part);
       }
+    }
+    // block maxima (the 16 lanes of a row group agree), one atomic each
+    nmax = fmaxf(nmax, __shfl_xor(nmax, 16));
+    nmax = fmaxf(nmax, __shfl_xor(nmax, 32));
+    dmax = fmaxf(dmax, __shfl_xor(dmax, 16));
+    dmax = fmaxf(dmax, __shfl_xor(dmax, 32));
+    if ((tid & 63) == 0) {
+      wred[0][tid >> 6] = nmax;
+      wred[1][tid >> 6] = dmax;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const float n2 = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+      const float dm = fmaxf(fmaxf(wred[1][0], wred[1][1]), fmaxf(wred[1][2], wred[1][3]));
+      if (n2 > 0.f) atomicMax(hm + 2 * h, __float_as_uint(sqrtf(n2)));
+      if (dm > 0.f) atomicMax(hm + 2 * h + 1, __float_as_uint(dm));
     }
   }
 }
@@ -207,7 +245,15 @@ constexpr int QB = 64;      // query rows per step of the key-outer kernel
 // Wave p ("A") holds the keys' K rows, computes S = Q K^T and P, publishes P
 // (fp16) in a 2 KiB LDS slot and accumulates dV^T += dO^T P. Wave p + 4
 // ("B") holds the keys' V rows, computes dP = dO V^T, takes P from the slot,
-// forms dS = P (dP - D) and accumulates dK^T += Q^T dS. Each role does 20 of
+// forms dS = P (dP - D) and accumulates dK^T += Q^T dS. Both carry
+// power-of-two factors that keep the fp16 operands in fp16's normal range
+// for long sequences (exact, removed at the write-out): P comes as P 2^15
+// (the row info's shift), and B's dS as dS 2^ex with ex per key, the largest
+// power for which a bound on every |dP - D| of the key (from the per-head
+// maxima of the row preparation and the key's |V| row norm) keeps
+// |dS 2^ex| < 2^14. B folds 2^(ex - 15) into its V rows and starts each dP
+// accumulation at -D 2^(ex - 15), so that (dP - D) 2^(ex - 15) leaves the
+// products as one. Each role does 20 of
 // the 40 products of a 32 x 32 sub-block and keeps under 256 registers, so
 // two waves share each SIMD. One barrier per 32-row sub-block separates the
 // publication of P from its use; the slot is double-buffered, so A writes
@@ -218,6 +264,7 @@ constexpr int QB = 64;      // query rows per step of the key-outer kernel
 // by A), double-buffered per 64-row block and DMA-filled.
 constexpr int PW = 128;                        // keys per workgroup
 constexpr int PF = 4;                          // fragment reads in flight ahead of the products
+constexpr int kExCap = 64;                     // largest power-of-two factor on dS
 constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
 constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
 constexpr int P_PIECES = P_BYTES / 1024;       // 49
@@ -237,9 +284,9 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                      const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                      const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
                      const int* __restrict__ korder, _Float16* __restrict__ dKV,
-                     float* __restrict__ dKr, _Float16* __restrict__ dS, int n_h, int n_seqs,
-                     int S_loc, int S_pad, RowMap rm, int key_lo, int Kpad, int n_kt, float scale,
-                     float scale_log2) {
+                     float* __restrict__ dKr, _Float16* __restrict__ dS,
+                     const uint32_t* __restrict__ hm, int n_h, int n_seqs, int S_loc, int S_pad,
+                     RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
   // stages, then P slots [pair][buffer], then dS slots [pair][buffer]
   __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 2 * 4 * 2 * 2048];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,6 +376,36 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
       const _Float16* vr = Vkm + (static_cast<int64_t>(h) * Kpad + tw + lr) * DV + 8 * lh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) vf[kk] = *reinterpret_cast<const half8*>(vr + 16 * kk);
+    }
+    // B: the key's dS factor 2^ex. |dP - D| <= |dO row| |V row| + |D| <=
+    // m1 |V_k| + m2 < 2^fe gives |dS 2^ex| <= 2^15 2^fe 2^(ex - 15) = 2^14
+    // for ex = 14 - fe (m1 is at least 1 so that |V_k 2^(ex - 15)| < 1/2;
+    // a key with a zero bound has dS = 0 and takes the cap). fs = 2^(ex - 15)
+    // scales the V rows (exactly: no result leaves fp16's range) and D.
+    int ex = kExCap;
+    float fs = 1.f;
+    if constexpr (!kA) {
+      float v2 = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = static_cast<float>(vf[kk][j]);
+          v2 = fmaf(v, v, v2);
+        }
+      v2 += __shfl_xor(v2, 32);   // lanes l and l ^ 32 hold the two halves of the row
+      const float m1 = fmaxf(__uint_as_float(hm[2 * h]), 1.f), m2 = __uint_as_float(hm[2 * h + 1]);
+      const float bnd = fmaf(m1, sqrtf(v2), m2);
+      if (bnd > 0.f) {
+        int fe;
+        (void)frexpf(bnd, &fe);   // bnd in [2^(fe-1), 2^fe)
+        ex = min(kExCap, 14 - fe);
+      }
+  #pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) vf[kk][j] = __builtin_amdgcn_ldexph(vf[kk][j], ex - kPShift);
+      fs = ldexpf(1.f, ex - kPShift);
     }
     // A: dV^T tiles (4 x 32 dims); B: dK^T tiles (6 x 32 dims)
     f32x16 acc[6];
@@ -427,8 +504,13 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             *reinterpret_cast<half8*>(xs + lane * 16) = pf[0];
             *reinterpret_cast<half8*>(xs + 1024 + lane * 16) = pf[1];
           } else {
+            // dp <- (dO V^T - D) 2^(ex - 15): the accumulation starts at -D fs
   #pragma unroll
-            for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) dp[4 * g + e] = -Dd[e] * fs;
+            }
             auto frag = [&](int k) {
               return *reinterpret_cast<const half8*>(base + ((k & 1) ? a_r1 : a_r0) + mt * 32 * PD_ROW + 64 * (k >> 1));
             };
@@ -469,16 +551,11 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
           } else {
             pf[0] = *reinterpret_cast<const half8*>(xs + lane * 16);
             pf[1] = *reinterpret_cast<const half8*>(xs + 1024 + lane * 16);
+            // dS 2^ex = (P 2^15) (dP - D) 2^(ex - 15)
             half8 dsf[2];
   #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 Dd = *reinterpret_cast<const f32x4*>(rinfo + 32 + swap23(d_row(4 * g, lh)));
-  #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * (dp[r] - Dd[e]));
-              }
-            }
+            for (int r = 0; r < 16; ++r)
+              dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * dp[r]);
             // dK^T (dims x keys) += Q^T (dims x rows) . dS (rows x keys)
             auto frag = [&](int k) {
               const int ks = k / 6, dm = k % 6;
@@ -494,11 +571,17 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               acc[k % 6] = mfma_f16(fa[k % (PF + 1)], dsf[k / 6], acc[k % 6]);
               __builtin_amdgcn_sched_barrier(0);
             }
-            // dS to the pair's slot for this sub-block parity; wave A stores
-            // it in the next phase 2, where it has slack
+            // dS (without the factor: the dQ kernel reads it as it is) to the
+            // pair's slot for this sub-block parity; wave A stores it in the
+            // next phase 2, where it has slack
             if (dS != nullptr) {
-              *reinterpret_cast<half8*>(dslot + mt * 2048 + lane * 16) = dsf[0];
-              *reinterpret_cast<half8*>(dslot + mt * 2048 + 1024 + lane * 16) = dsf[1];
+              const float fu = ldexpf(1.f, -ex);
+              half8 du[2];
+  #pragma unroll
+              for (int r = 0; r < 16; ++r)
+                du[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * dp[r] * fu);
+              *reinterpret_cast<half8*>(dslot + mt * 2048 + lane * 16) = du[0];
+              *reinterpret_cast<half8*>(dslot + mt * 2048 + 1024 + lane * 16) = du[1];
             }
           }
         }
@@ -525,7 +608,8 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
     // GEMM reads as it is and the weight-gradient GEMMs read k-major.
     const int64_t nk = static_cast<int64_t>(n_h) * 128;
     const int key = 32 * pi + lr;                           // key within the workgroup
-    const float sc = kA ? 1.f : scale;
+    // A: P carried 2^15; B: dS carried 2^ex (exact powers of two)
+    const float sc = kA ? ldexpf(1.f, -kPShift) : scale * ldexpf(1.f, -ex);
     float* rtile = reinterpret_cast<float*>(smem);          // [128 keys][R_PITCH] (free after the loop)
     if constexpr (!kA) {
   #pragma unroll
@@ -608,7 +692,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const bool wave_live = wq0 < S_loc;
   const uint32_t* blk = info_h + (wq0 >> 5) * 128;
   const int n_last = wave_live ? min(S_loc - 1 - wq0, 31) : 0;  // the wave's last valid row
-  const float L2 = valid ? __uint_as_float(blk[lr]) : 0.f;
+  const float L2 = valid ? __uint_as_float(blk[lr]) + kPShift : 0.f;
   const float Di = valid ? __uint_as_float(blk[32 + lr]) : 0.f;
   const int lo = valid ? static_cast<int>(blk[64 + lr]) : 0;
   const int p = valid ? static_cast<int>(blk[96 + lr]) : -1;
@@ -1041,6 +1125,8 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   // {2^e, 2^-e}: the dout scale and its inverse; then the per-block maxima
   float* dsc = reinterpret_cast<float*>(at(L.dscale));
   uint32_t* dmax = reinterpret_cast<uint32_t*>(at(L.dscale) + 16);
+  // per head {largest |2^e dout row|, largest |D|} (float bits)
+  uint32_t* hmax = dmax + kScaleBlocks;
   const int S_loc = static_cast<int>(p.S_loc), Sp = static_cast<int>(S_pad),
             key_lo = static_cast<int>(p.key_lo),
             Kpad = static_cast<int>(p.Kpad);
@@ -1085,14 +1171,15 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     const unsigned nb = static_cast<unsigned>(std::min<int64_t>(kScaleBlocks, (n8 + 255) / 256));
     hipLaunchKernelGGL(dout_absmax_kernel, dim3(nb), dim3(256), 0, st2,
                        static_cast<const u32x4*>(dout), n8, dmax);
-    hipLaunchKernelGGL(dout_scale_kernel, dim3(1), dim3(256), 0, st2, dmax, static_cast<int>(nb), dsc);
+    hipLaunchKernelGGL(dout_scale_kernel, dim3(1), dim3(256), 0, st2, dmax, static_cast<int>(nb), dsc,
+                       hmax, 2 * p.n_h);
   }
   if ((s = check_launch("dout scale")) != MLA_OK) return s;
   {
     KernelTimer kt("bwd_prep", st2);
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(S_pad / 64), p.n_h), dim3(256),
                        0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
-                       out, lse, cu_dev, dsc, D, Qn, dOn, info, p.n_h, p.n_seqs, p.S_loc,
+                       out, lse, cu_dev, dsc, D, Qn, dOn, info, hmax, p.n_h, p.n_seqs, p.S_loc,
                        S_pad, p.rm);
   }
   if ((s = check_launch("backward prep")) != MLA_OK) return s;
@@ -1117,7 +1204,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
     const int n_kt = static_cast<int>(p.Kpad / PW);
     KernelTimer kt("attn_bwd_dkdv", st);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
-                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKr, dS, p.n_h,
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKr, dS, hmax, p.n_h,
                        p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
   }
   if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;

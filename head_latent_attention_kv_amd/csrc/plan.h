@@ -62,7 +62,8 @@ struct BwdLayout {
   // ([4 pairs of 32 keys][2 row halves][64 lanes] x 16 bytes, written by dK/dV)
   int64_t dS;
   // fast path: dout scale {2^e, 2^-e} (fp32), then the per-block maxima of
-  // |dout| it is chosen from (kScaleBlocks uint32)
+  // |dout| it is chosen from (kScaleBlocks uint32), then per head the
+  // largest |2^e dout row| and |D| (2 n_h floats)
   int64_t dscale;
   int64_t total;
 };

@@ -69,10 +69,19 @@
  *       backward: dout is first multiplied by a power of two 2^e that brings
  *       max|dout| into [4, 8) (exact), so the gradients do not depend on the
  *       scale of dout: dout scaled by any power of two gives gradients
- *       scaled by the same power, bit for bit. dP, dS and the per-key rows
- *       [dK_nope | dV] carry the factor in fp16, so |dV[key]| <= 8 * (the
- *       key's total softmax weight over the shard's rows) must stay below
- *       65504; the fp32 gradients are multiplied back by 2^-e.
+ *       scaled by the same power, bit for bit. The dK/dV products take the
+ *       softmax weights as P 2^15 and dS = P (dP - D) as dS 2^ex, ex per
+ *       key the largest power for which a bound on the key's |dP - D| (from
+ *       the largest 2^e dout row norm, the largest |D| and the key's V row
+ *       norm) keeps |dS 2^ex| below 2^14; both factors are exact and leave
+ *       in fp32, so a key's weights among up to 2^22 keys stay in fp16's
+ *       normal range. The per-key rows [dK_nope | dV] are stored in fp16
+ *       with the dout factor only: |dV[key]| <= 8 * (the key's total
+ *       softmax weight over the shard's rows) must stay below 65504, and
+ *       where that total is tiny (a few rows over millions of keys) the rows
+ *       fall below 2^-14 and dc_kv loses relative precision (sum|err| /
+ *       sum|dc_kv| of 3e-3 at 2^22 keys and 64 rows, 5e-4 at 2^19 keys and
+ *       256 rows). The fp32 gradients are multiplied back by 2^-e.
  */
 /*
  * Debug mode. With the environment variable MLA_LAGA_DEBUG set to anything

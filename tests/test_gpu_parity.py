@@ -16,7 +16,7 @@ import torch
 import head_latent_attention_kv_amd as hla
 import oracle
 import workloads
-from tests.gpu_helpers import announce, check, to_device
+from tests.gpu_helpers import MEAN_REL, announce, check, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +142,60 @@ def test_h16_s4k_full_forward():
     ro, rl = oracle.mla_forward(*oracle_args(x))
     check("out", g["out"], ro)
     check("lse", g["lse"], rl)
+
+
+@pytest.mark.parametrize("S,S_loc,stored_ds", [(1 << 17, 1024, False), (1 << 17, 1024, True),
+                                               (1 << 19, 256, False)])
+def test_long_context_bwd(S, S_loc, stored_ds):
+    """Long latents with a short shard of rows at the end: the softmax weights
+    of a key are about 1 / S (2^-17 and 2^-19), below fp16's normal range
+    (2^-14). The dK/dV products take them with power-of-two factors (P 2^15,
+    dS 2^ex per key) that keep them normal; every output at the full bar, also
+    with dQ taken from the stored dS (written without the factor)."""
+    cfg = workloads.MLAConfig(f"long_{S}", n_h=1, d_c=64, d_rope=64, d_nope=128, d_v=128, S=S,
+                              S_loc=S_loc, q_offset=S - S_loc, dtype="bf16", backward=True, seed=7)
+    announce(f"long context fwd+bwd: S={S}, last {S_loc} rows, stored_ds={stored_ds}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    g = run(cfg, x, backward=True, stored_ds=stored_ds)
+    assert g["fast"]
+    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset)
+    check("out", g["out"], ro)
+    check("lse", g["lse"], rl)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset)
+    for name, ref in zip(GRADS, rg):
+        check(name, g[name], ref)
+
+
+def test_max_keys_fwd_bwd():
+    """The fast path at its key limit: one head and the last 64 rows of a
+    latent of 2^22 - 256 rows (the most needed keys the fast path takes), so
+    every offset into the rebuilt K, V^T and key-major V tiles, the gradient
+    rows and every 32-bit DMA offset is at its largest. Every key is visible
+    to these rows. All seven outputs element by element against the oracle
+    (the narrowest latent, d_c = 64, keeps the oracle's fp64 copies small).
+
+    dc_kv alone has a wider mean bound. Each key's [dK_nope | dV] row is
+    stored in fp16 (times the dout factor 2^e, max|2^e dout| in [4, 8)):
+    dV[key] sums 64 rows' weights of about 2^-22 each, so its elements are
+    near 2^-19, inside fp16's subnormal range, where the spacing is a fixed
+    2^-24. Rounding to that spacing costs up to 2^-25 / 2^-19 = 2^-6 of each
+    element, about 2^-8 on average over the row's sizes, i.e. 4e-3. The
+    measured sum|err| / sum|ref| is 3.0e-3; the bound is 5e-3. Its max-abs
+    stays at the full bar, and the other outputs meet the full bar."""
+    S = (1 << 22) - 256
+    cfg = workloads.MLAConfig("max_keys", n_h=1, d_c=64, d_rope=64, d_nope=128, d_v=128, S=S,
+                              S_loc=64, q_offset=S - 64, dtype="bf16", backward=True, seed=5)
+    announce(f"max keys fwd+bwd: S={S}, last {cfg.S_loc} rows")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    g = run(cfg, x, backward=True)
+    assert g["fast"]
+    ro, rl = oracle.mla_forward(*oracle_args(x), q_offset=cfg.q_offset)
+    check("out", g["out"], ro)
+    check("lse", g["lse"], rl)
+    del ro, rl
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset)
+    for name, ref in zip(GRADS, rg):
+        check(name, g[name], ref, mean_rel=5e-3 if name == "dc_kv" else MEAN_REL)
 
 
 @pytest.mark.parametrize("heads", [[0, 37, 64, 127]])
