@@ -116,10 +116,11 @@ static_assert(4 * PDW * 64 == DB * (DC / 8) && PDW * 64 / 2 == DB * (DR / 8) &&
                   DB * (DL / 8) == 4 * PDW * 64 + DB * (DR / 8),
               "conversion: four c_kv pieces per thread and a k_rope piece for half the threads");
 
-// s_waitcnt vmcnt(n) for n = 0, 4, 5, other counters at their maxima (gfx9
+// s_waitcnt vmcnt(n) for n = 0, 4, 5, 9, other counters at their maxima (gfx9
 // encoding: vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8)
 __device__ __forceinline__ void wait_vm_n(int n) {
-  if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
+  if (n == 9) __builtin_amdgcn_s_waitcnt(0x0F79);
+  else if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
   else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
@@ -154,18 +155,22 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
   const int h = hw + lr;
 
   // DMA of block blk into raw slot blk % 2: piece I (< 32) is key I's c_kv
-  // row, piece 32 + r the k_rope rows of keys 8 r .. 8 r + 7. Every wave
-  // always issues its pieces (5 for waves 0..3, 4 for waves 4..7), so that
-  // vmcnt counts stay exact: rows past the chunk read the chunk's last row
-  // instead, and the conversion writes zeros for them.
-  const int n_dma = w < PD_PIECES - 4 * PDW ? 5 : 4;
+  // row, piece 32 + r the k_rope rows of keys 8 r .. 8 r + 7. The waves of
+  // the first contraction halves (0..3) issue all 36 pieces, 9 each, after
+  // their score products, where they would otherwise wait for their partners
+  // (which finish theirs later); the other waves issue none. A wave always
+  // issues its 9 pieces, so that vmcnt counts stay exact: rows past the chunk
+  // read the chunk's last row instead, and the conversion writes zeros for
+  // them.
+  const int n_dma = kh == 0 ? PD_PIECES / 4 : 0;
   auto issue = [&](int blk) {
+    if (kh != 0) return;
     const int kb = k0 + blk * DB;
     const int64_t last = static_cast<int64_t>(s0) + k1 - 1;   // the chunk's last row (>= s0)
     char* raw = smem + (blk & 1) * PD_RAW;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const int I = w + PDW * j;   // wave-uniform
+    for (int j = 0; j < PD_PIECES / 4; ++j) {
+      const int I = w + 4 * j;   // wave-uniform
       if (I < DB) {
         const int64_t row = min(static_cast<int64_t>(s0) + kb + I, last);
         lds_dma16(scalar_ptr(c_kv + row * DC), lane * 16u, raw + I * 1024);
@@ -186,21 +191,30 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
     const int kb = k0 + blk * DB;
     const char* raw = smem + (blk & 1) * PD_RAW;
     char* tile = smem + PD_TILE;
-    half8 zero;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zero[e] = static_cast<_Float16>(0.f);
+    // all reads first, then the conversions and writes; rows past the
+    // chunk are cleared through a mask on the raw bits (no branch, so the
+    // reads overlap)
+    u32x4 v[5];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int key = (tid >> 6) + 8 * p, sl = tid & 63;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + key * 1024 + sl * 16);
-      *reinterpret_cast<half8*>(tile + key * DROW + xs_slot(key, sl) * 16) =
-          kb + key < k1 ? bf16x8_to_half8(v) : zero;
+      v[p] = *reinterpret_cast<const u32x4*>(raw + key * 1024 + sl * 16);
+    }
+    const int rkey = (tid >> 3) & 31, rs = tid & 7;
+    if (tid < 256) v[4] = *reinterpret_cast<const u32x4*>(raw + DB * 1024 + rkey * 128 + rs * 16);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 6) + 8 * p, sl = tid & 63;
+      const uint32_t msk = kb + key < k1 ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[p][k] &= msk;
+      *reinterpret_cast<half8*>(tile + key * DROW + xs_slot(key, sl) * 16) = bf16x8_to_half8(v[p]);
     }
     if (tid < 256) {
-      const int key = tid >> 3, rs = tid & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(raw + DB * 1024 + key * 128 + rs * 16);
-      *reinterpret_cast<half8*>(tile + key * DROW + xs_slot(key, 64 + rs) * 16) =
-          kb + key < k1 ? bf16x8_to_half8(v) : zero;
+      const uint32_t msk = kb + rkey < k1 ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[4][k] &= msk;
+      *reinterpret_cast<half8*>(tile + rkey * DROW + xs_slot(rkey, 64 + rs) * 16) = bf16x8_to_half8(v[4]);
     }
   };
 
@@ -251,16 +265,20 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
   char* const xs_own = smem + PD_XS + w * 4096 + lane * 16;
   const char* const xs_par = smem + PD_XS + (w ^ 4) * 4096 + lane * 16;
 
+  // the q loads above complete here, before any DMA: the compiler's wait
+  // model does not see the DMA instructions, and a q load it still counts
+  // as pending would make it wait inside the loop until the DMA issued
+  // there lands
+  __builtin_amdgcn_s_waitcnt(0);
   if (nblk > 0) issue(0);
   if (nblk > 1) issue(1);
   // block 0 landed (loads complete in issue order, and at most block 1's
-  // pieces and the q loads above may remain), q_rope written
+  // pieces may remain), q_rope written
   wait_vm_n(nblk > 1 ? n_dma : 0);
   __syncthreads();
   for (int bi = 0; bi < nblk; ++bi) {
     convert(bi);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // tile ready, raw slot free
-    if (bi + 2 < nblk) issue(bi + 2);
     const char* base = smem + PD_TILE;
     f32x16 s;
 #pragma unroll
@@ -287,6 +305,8 @@ decode_attn_pair_kernel(const _Float16* __restrict__ qlat, const uint16_t* __res
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4*>(xs_own + g * 1024) = f32x4{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
     }
+    // the next DMA, from the waves that would wait here for their partners
+    if (bi + 2 < nblk) issue(bi + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // partial scores visible
     half8 pb[2];
     if (live) {
