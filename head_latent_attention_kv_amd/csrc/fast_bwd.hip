@@ -459,6 +459,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
         half8 pf[2];
         f32x16 dp;
+        half8 dph[2];   // B: dp in fp16, formed before the barrier
         // ---- phase 1: A computes S and P and publishes P; B computes dP
         if (!skip) {
           if constexpr (kA) {
@@ -523,6 +524,10 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               dp = mfma_f16(fa[k % (PF + 1)], vf[k], dp);
               __builtin_amdgcn_sched_barrier(0);
             }
+            // |dp| < 1/2 by the choice of ex: fp16 keeps it to 2^-11 relative,
+            // and phase 2 then forms dS with packed fp16 products
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) dph[r >> 3][r & 7] = static_cast<_Float16>(dp[r]);
           }
         }
         // P(t) visible to B; every wave, every sub-block. Only LDS is waited
@@ -553,9 +558,8 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             pf[1] = *reinterpret_cast<const half8*>(xs + 1024 + lane * 16);
             // dS 2^ex = (P 2^15) (dP - D) 2^(ex - 15)
             half8 dsf[2];
-  #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              dsf[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * dp[r]);
+            dsf[0] = pf[0] * dph[0];
+            dsf[1] = pf[1] * dph[1];
             // dK^T (dims x keys) += Q^T (dims x rows) . dS (rows x keys)
             auto frag = [&](int k) {
               const int ks = k / 6, dm = k % 6;
@@ -575,11 +579,9 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             // pair's slot for this sub-block parity; wave A stores it in the
             // next phase 2, where it has slack
             if (dS != nullptr) {
-              const float fu = ldexpf(1.f, -ex);
               half8 du[2];
   #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                du[r >> 3][r & 7] = static_cast<_Float16>(static_cast<float>(pf[r >> 3][r & 7]) * dp[r] * fu);
+              for (int r = 0; r < 16; ++r) du[r >> 3][r & 7] = __builtin_amdgcn_ldexph(dsf[r >> 3][r & 7], -ex);
               *reinterpret_cast<half8*>(dslot + mt * 2048 + lane * 16) = du[0];
               *reinterpret_cast<half8*>(dslot + mt * 2048 + 1024 + lane * 16) = du[1];
             }
