@@ -524,10 +524,6 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
               dp = mfma_f16(fa[k % (PF + 1)], vf[k], dp);
               __builtin_amdgcn_sched_barrier(0);
             }
-            // |dp| < 1/2 by the choice of ex: fp16 keeps it to 2^-11 relative,
-            // and phase 2 then forms dS with packed fp16 products
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) dph[r >> 3][r & 7] = static_cast<_Float16>(dp[r]);
           }
         }
         // P(t) visible to B; every wave, every sub-block. Only LDS is waited
@@ -556,6 +552,10 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
           } else {
             pf[0] = *reinterpret_cast<const half8*>(xs + lane * 16);
             pf[1] = *reinterpret_cast<const half8*>(xs + 1024 + lane * 16);
+            // dp in fp16 while P is read (|dp| < 1/2 by the choice of ex:
+            // fp16 keeps it to 2^-11 relative), then dS with packed products
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) dph[r >> 3][r & 7] = static_cast<_Float16>(dp[r]);
             // dS 2^ex = (P 2^15) (dP - D) 2^(ex - 15)
             half8 dsf[2];
             dsf[0] = pf[0] * dph[0];
