@@ -127,7 +127,8 @@ __device__ __forceinline__ half8 bf16x8_to_half8_scaled(u32x4 v, float s) {
 // D[h][i] = 2^e dout[i,h,:] . out[i,h,:]; fp16 copies Qn[h][i][192] and
 // dOn[h][i][128] (2^e dout; rows past S_loc are zero); and per
 // 32-row block the row info the dK/dV kernels read:
-// info[h][i/32] = {lse*log2(e) [32], D [32], sample start [32], position [32]}
+// info[h][i/32] = {lse*log2(e) - kPShift [32], D [32], sample start [32],
+// position [32]}
 // (rows past S_loc: start INT32_MAX, position -1, so they see no key).
 // hm[2 h] and hm[2 h + 1] are raised (as float bits: non-negative floats
 // order like their bit patterns) to the largest |2^e dout[i,h,:]| (2-norm)
@@ -253,7 +254,9 @@ constexpr int QB = 64;      // query rows per step of the key-outer kernel
 // maxima of the row preparation and the key's |V| row norm) keeps
 // |dS 2^ex| < 2^14. B folds 2^(ex - 15) into its V rows and starts each dP
 // accumulation at -D 2^(ex - 15), so that (dP - D) 2^(ex - 15) leaves the
-// products as one. Each role does 20 of
+// products as one; after the barrier it converts that to fp16 and forms
+// dS 2^ex = (P 2^15) (dP - D) 2^(ex - 15) with packed fp16 products. Each
+// role does 20 of
 // the 40 products of a 32 x 32 sub-block and keeps under 256 registers, so
 // two waves share each SIMD. One barrier per 32-row sub-block separates the
 // publication of P from its use; the slot is double-buffered, so A writes
@@ -459,7 +462,6 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
         const bool skip = q0 >= S_loc || p_last < gw_min || iinfo[0] > gw_max;
         half8 pf[2];
         f32x16 dp;
-        half8 dph[2];   // B: dp in fp16, formed before the barrier
         // ---- phase 1: A computes S and P and publishes P; B computes dP
         if (!skip) {
           if constexpr (kA) {
@@ -554,6 +556,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
             pf[1] = *reinterpret_cast<const half8*>(xs + 1024 + lane * 16);
             // dp in fp16 while P is read (|dp| < 1/2 by the choice of ex:
             // fp16 keeps it to 2^-11 relative), then dS with packed products
+            half8 dph[2];
   #pragma unroll
             for (int r = 0; r < 16; ++r) dph[r >> 3][r & 7] = static_cast<_Float16>(dp[r]);
             // dS 2^ex = (P 2^15) (dP - D) 2^(ex - 15)

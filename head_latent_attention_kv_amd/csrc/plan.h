@@ -53,7 +53,7 @@ struct BwdLayout {
   // (the kernels read the transposes of K, q and dout from these row-major
   // tiles with transposed LDS reads)
   int64_t Vkm, W16, ckvT, Qn, dOn;
-  int64_t info;  // fast path: per 32-row block {lse*log2e, D, sample start, position} x 32
+  int64_t info;  // fast path: per 32-row block {lse*log2e - 15, D, sample start, position} x 32
   int64_t gpart;  // fast path: split-K partial sums of the gradient GEMMs (fp32)
   // fast path, packed calls: query-tile then key-tile order (int32
   // [ceil(S_loc / 256) + Kpad / 128])
