@@ -16,7 +16,7 @@ import torch
 import head_latent_attention_kv_amd as hla
 import oracle
 import workloads
-from tests.gpu_helpers import MEAN_REL, announce, check, to_device
+from tests.gpu_helpers import MAX_ABS, MEAN_REL, announce, check, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +142,42 @@ def test_h16_s4k_full_forward():
     ro, rl = oracle.mla_forward(*oracle_args(x))
     check("out", g["out"], ro)
     check("lse", g["lse"], rl)
+
+
+def _set(x, name, values):
+    """x with input `name` replaced by `values` (exact in bf16)."""
+    bits = workloads.f32_to_bf16_bits(np.asarray(values, np.float32))
+    return dict(x, **{name: workloads.bf16_bits_to_f32(bits), name + "_bits": bits})
+
+
+@pytest.mark.parametrize("v_exp", [-10, 8])
+@pytest.mark.parametrize("path", ["default", "stored_ds"])
+def test_value_scale_and_zero_rows_bwd(v_exp, path):
+    """The backward's per-key dS factor comes from a bound on |dP - D| built
+    from the key's V row norm and the per-head maxima of |dout row| and |D|.
+    V scaled by 2^v_exp (W_UV times a power of two, exact in bf16) moves the
+    factor's exponent far from its usual range, and a run of latent rows set
+    to zero (V = K_nope = 0 there) leaves the largest |D| as the whole bound
+    of those keys. Every output against the oracle: the sum ratio at the
+    full bar (it does not depend on the scale of the values); the max-abs bar,
+    set for unit-scale inputs, scaled by the same 2^v_exp when v_exp > 0,
+    since out, dq and the key-side gradients grow with V."""
+    cfg, cu = small("v_scale", 2, 700, 333, 367, cu=[0, 90, 91, 400, 700], seed=9)
+    announce(f"value scale 2^{v_exp}, zero latent rows, path={path}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    x = _set(x, "W_UV", x["W_UV"] * np.float32(2.0 ** v_exp))
+    ckv = x["c_kv"].copy()
+    ckv[380:450] = 0.0
+    x = _set(x, "c_kv", ckv)
+    g = run(cfg, x, cu, backward=True, stored_ds=path == "stored_ds")
+    assert g["fast"]
+    ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, **positions(cfg))
+    bar = MAX_ABS * 2.0 ** max(v_exp, 0)
+    check("out", g["out"], ro, max_abs=bar)
+    check("lse", g["lse"], rl)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, **positions(cfg))
+    for name, ref in zip(GRADS, rg):
+        check(name, g[name], ref, max_abs=bar)
 
 
 @pytest.mark.parametrize("S,S_loc,stored_ds", [(1 << 17, 1024, False), (1 << 17, 1024, True),
