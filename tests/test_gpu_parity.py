@@ -180,6 +180,29 @@ def test_value_scale_and_zero_rows_bwd(v_exp, path):
         check(name, g[name], ref, max_abs=bar)
 
 
+@pytest.mark.parametrize("k_mul", [4])
+def test_sharp_softmax_bwd(k_mul):
+    """Scores k_mul times larger (W_UK times a power of two, exact in bf16):
+    the softmax puts most weight on a few keys per row, so P 2^15 comes close
+    to its ceiling of 2^15 for them while most keys' weights fall far below
+    fp16's range. Every output against the oracle; the max-abs bar scaled by
+    k_mul, since dq and dK grow with K. (At 8 times the gradients reach the
+    1e-3 sum-ratio bar, as they did before the dS factors: the scores come
+    from fp16 q and K, and sharper logits magnify their rounding.)"""
+    cfg, cu = small("sharp", 2, 600, 450, 150, cu=[0, 1, 1, 130, 131, 400, 600], seed=11)
+    announce(f"sharp softmax (W_UK x {k_mul})")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    x = _set(x, "W_UK", x["W_UK"] * np.float32(k_mul))
+    g = run(cfg, x, cu, backward=True)
+    assert g["fast"]
+    ro, rl = oracle.mla_forward(*oracle_args(x), cu_seqlens=cu, **positions(cfg))
+    check("out", g["out"], ro)
+    check("lse", g["lse"], rl)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, **positions(cfg))
+    for name, ref in zip(GRADS, rg):
+        check(name, g[name], ref, max_abs=k_mul * MAX_ABS)
+
+
 @pytest.mark.parametrize("S,S_loc,stored_ds", [(1 << 17, 1024, False), (1 << 17, 1024, True),
                                                (1 << 19, 256, False)])
 def test_long_context_bwd(S, S_loc, stored_ds):
