@@ -94,12 +94,13 @@ mla_status side_stream(SideStream* out) {
     SideStream n;
     if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess)
       return fail(MLA_ERR_HIP, "hipStreamCreateWithFlags failed");
-    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
-      if (n.fork != nullptr) (void)hipEventDestroy(n.fork);
-      (void)hipStreamDestroy(n.st);
-      return fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed");
-    }
+    hipEvent_t* evs[4] = {&n.fork, &n.join, &n.buf_free[0], &n.buf_free[1]};
+    for (int i = 0; i < 4; ++i)
+      if (hipEventCreateWithFlags(evs[i], hipEventDisableTiming) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(*evs[j]);
+        (void)hipStreamDestroy(n.st);
+        return fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed");
+      }
     s = n;   // kept until the process ends
   }
   *out = s;
@@ -171,7 +172,8 @@ BwdLayout bwd_layout(const Plan& p) {
                             gemm_splitk_bytes(p.d_c, nk, p.Kpad)));
     L.order = take(4 * ((p.S_loc + 255) / 256 + p.Kpad / 128));
     L.dscale = take(16 + 4 * kScaleBlocks + 8 * static_cast<int64_t>(p.n_h));
-    if (p.ds_store) L.dS = take(p.n_h * p.Kpad * S_pad * 2);
+    if (p.ds_store)
+      L.dS = take((p.ds_heads < p.n_h ? 2 : 1) * static_cast<int64_t>(p.ds_heads) * p.Kpad * S_pad * 2);
     L.f.total = -1;
   } else {
     L.f = fwd_layout(p, false);
@@ -274,8 +276,24 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   }
   P.Kn = P.key_hi - P.key_lo;
   P.Kpad = align_up(P.Kn, kKeyTile);
-  P.ds_store = P.fast_bwd && (d->flags & MLA_FLAG_STORED_DS) &&
-               P.n_h * P.Kpad * align_up(P.S_loc, 64) * 2 <= kMaxStoredDsBytes;
+  // stored dS: every head in one buffer while it fits kStoredDsOneBufferBytes
+  // (dQ then runs once, beside the gradient GEMMs); else head groups of at
+  // most kStoredDsGroupBytes, as even as their count allows; a single head
+  // past that recomputes
+  P.ds_store = false;
+  P.ds_heads = 0;
+  if (P.fast_bwd && (d->flags & MLA_FLAG_STORED_DS)) {
+    const int64_t per_head = P.Kpad * align_up(P.S_loc, 64) * 2;
+    if (P.n_h * per_head <= kStoredDsOneBufferBytes) {
+      P.ds_store = true;
+      P.ds_heads = P.n_h;
+    } else if (per_head <= kStoredDsGroupBytes) {
+      const int64_t most = kStoredDsGroupBytes / per_head;   // heads per group, at most
+      const int64_t groups = (P.n_h + most - 1) / most;
+      P.ds_store = true;
+      P.ds_heads = static_cast<int>((P.n_h + groups - 1) / groups);
+    }
+  }
   int64_t pairs = 0;
   for (int64_t i = 0; i < P.S_loc; ++i) {
     const int64_t pos = rm_pos(P.rm, static_cast<int>(i));

@@ -288,8 +288,9 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
                      const _Float16* __restrict__ Vkm, const int32_t* __restrict__ cu,
                      const int* __restrict__ korder, _Float16* __restrict__ dKV,
                      float* __restrict__ dKr, _Float16* __restrict__ dS,
-                     const uint32_t* __restrict__ hm, int n_h, int n_seqs, int S_loc, int S_pad,
-                     RowMap rm, int key_lo, int Kpad, int n_kt, float scale, float scale_log2) {
+                     const uint32_t* __restrict__ hm, int n_h, int h0, int n_hg, int n_seqs,
+                     int S_loc, int S_pad, RowMap rm, int key_lo, int Kpad, int n_kt, float scale,
+                     float scale_log2) {
   // stages, then P slots [pair][buffer], then dS slots [pair][buffer]
   __shared__ __attribute__((aligned(1024))) char smem[2 * P_BYTES + 2 * 4 * 2 * 2048];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -297,8 +298,10 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
   const int lr = lane & 31, lh = lane >> 5;
   const bool role_a = w < 4;
   const int pi = w & 3;                       // pair index
-  int h, kt;
-  work_item(blockIdx.x, n_h, n_kt, &h, &kt);
+  // heads h0 .. h0 + n_hg - 1; dS (when stored) holds those heads only
+  int hl, kt;
+  work_item(blockIdx.x, n_hg, n_kt, &hl, &kt);
+  const int h = h0 + hl;
   if (korder != nullptr) kt = korder[kt];     // packed calls: heaviest key tiles first
   const int t0 = kt * PW;                     // workspace key row of the workgroup
   const int tw = t0 + 32 * pi;                // the pair's first key
@@ -436,7 +439,7 @@ attn_bwd_dkdv_kernel(const _Float16* __restrict__ Qn, const _Float16* __restrict
       if (ds_q0 >= 0) {
         const half8 v0 = *reinterpret_cast<const half8*>(dslot + par * 2048 + lane * 16);
         const half8 v1 = *reinterpret_cast<const half8*>(dslot + par * 2048 + 1024 + lane * 16);
-        _Float16* db = dS + (((static_cast<int64_t>(h) * n_kt + kt) * (S_pad / 32) + (ds_q0 >> 5)) * 4096 +
+        _Float16* db = dS + (((static_cast<int64_t>(hl) * n_kt + kt) * (S_pad / 32) + (ds_q0 >> 5)) * 4096 +
                              pi * 1024 + lane * 8);
         // non-temporal: the dS stream then leaves the q/dO tiles in L2
         __builtin_nontemporal_store(v0, reinterpret_cast<half8*>(db));
@@ -890,14 +893,16 @@ __device__ __forceinline__ void wait_vm_lgkm(bool four) {
 __global__ void __launch_bounds__(512)
 attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restrict__ Kfull,
                       const _Float16* __restrict__ dS, const int* __restrict__ qorder,
-                      const float* __restrict__ sc, float* __restrict__ dq, int n_h, int S_loc,
-                      int S_pad, int key_lo, int Kpad, int n_qt, float scale) {
+                      const float* __restrict__ sc, float* __restrict__ dq, int n_h, int h0,
+                      int n_hg, int S_loc, int S_pad, int key_lo, int Kpad, int n_qt, float scale) {
   __shared__ __attribute__((aligned(1024))) char smem[E_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lr = lane & 31, lh = lane >> 5;
-  int h, qt;
-  work_item(blockIdx.x, n_h, n_qt, &h, &qt);
+  // heads h0 .. h0 + n_hg - 1; dS holds those heads only
+  int hl, qt;
+  work_item(blockIdx.x, n_hg, n_qt, &hl, &qt);
+  const int h = h0 + hl;
   qt = qorder != nullptr ? qorder[qt] : n_qt - 1 - qt;
   const int q0 = qt * QW;
   const int wq0 = q0 + 32 * w;
@@ -922,7 +927,7 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
 
   const _Float16* Kh = Kfull + static_cast<int64_t>(h) * Kpad * DQK;
   // this wave's dS^T rows (32-row block, clamped for rows past S_pad)
-  const _Float16* dSw = dS + (static_cast<int64_t>(h) * (Kpad / 128) * n_rb + min((q0 >> 5) + w, n_rb - 1)) * (128 * 32);
+  const _Float16* dSw = dS + (static_cast<int64_t>(hl) * (Kpad / 128) * n_rb + min((q0 >> 5) + w, n_rb - 1)) * (128 * 32);
   // K pieces of this wave: w, w + 8, w + 16, w + 24 (< 28); per-lane offsets
   // (elements) of the swizzled rows, pad slots reloading slot 0
   int kdoff[4];
@@ -1205,29 +1210,51 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
         return s;
     }
   }
-  {
-    const int n_kt = static_cast<int>(p.Kpad / PW);
+  const int n_kt = static_cast<int>(p.Kpad / PW), n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
+  auto dkdv = [&](int h0, int n_hg, _Float16* dSg) {
     KernelTimer kt("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * p.n_h)), dim3(512), 0,
-                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKr, dS, hmax, p.n_h,
-                       p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale, scale_log2);
-  }
-  if ((s = check_launch("attention backward dK/dV")) != MLA_OK) return s;
-  if ((s = fork.fork()) != MLA_OK) return s;
-  {
-    const int n_qt = static_cast<int>((p.S_loc + QW - 1) / QW);
-    KernelTimer kt(dS != nullptr ? "attn_bwd_dq_ds" : "attn_bwd_dq", st2);
-    if (dS != nullptr)
-      hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
-                         0, st2, info, Kfull, dS, qorder, dsc, dq, p.n_h, S_loc, Sp, key_lo, Kpad,
-                         n_qt, p.scale);
-    else
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(static_cast<unsigned>(n_kt * n_hg)), dim3(512), 0,
+                       st, Qn, dOn, info, Kfull, Vkm, cu_dev, korder, dKV, dKr, dSg, hmax, p.n_h,
+                       h0, n_hg, p.n_seqs, S_loc, Sp, p.rm, key_lo, Kpad, n_kt, p.scale,
+                       scale_log2);
+    return check_launch("attention backward dK/dV");
+  };
+  if (dS == nullptr) {
+    if ((s = dkdv(0, p.n_h, nullptr)) != MLA_OK) return s;
+    if ((s = fork.fork()) != MLA_OK) return s;
+    {
+      KernelTimer kt("attn_bwd_dq", st2);
       hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(static_cast<unsigned>(n_qt * p.n_h)), dim3(512),
                          0, st2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(dout),
                          info, Kfull, Vkm, qorder, dsc, dq, p.n_h, S_loc, Sp, key_lo, Kpad, n_qt,
                          p.scale, scale_log2);
+    }
+    if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
+  } else {
+    // Stored dS, ds_heads heads at a time: dK/dV of group g (main stream)
+    // fills buffer g % 2, dQ of group g (side stream) reads it while dK/dV of
+    // group g + 1 fills the other; dK/dV of group g + 2 waits until dQ of
+    // group g has released its buffer.
+    const int G = p.ds_heads;
+    const int64_t group_elems = static_cast<int64_t>(G) * p.Kpad * S_pad;
+    for (int h0 = 0, g = 0; h0 < p.n_h; h0 += G, ++g) {
+      const int n_hg = std::min(G, p.n_h - h0);
+      _Float16* dSg = dS + (g & 1) * group_elems;
+      if (g >= 2 && hipStreamWaitEvent(st, side.buf_free[g & 1], 0) != hipSuccess)
+        return fail(MLA_ERR_HIP, "wait for the stored-dS buffer failed");
+      if ((s = dkdv(h0, n_hg, dSg)) != MLA_OK) return s;
+      if ((s = fork.fork()) != MLA_OK) return s;
+      {
+        KernelTimer kt("attn_bwd_dq_ds", st2);
+        hipLaunchKernelGGL(attn_bwd_dq_ds_kernel, dim3(static_cast<unsigned>(n_qt * n_hg)), dim3(512),
+                           0, st2, info, Kfull, dSg, qorder, dsc, dq, p.n_h, h0, n_hg, S_loc, Sp,
+                           key_lo, Kpad, n_qt, p.scale);
+      }
+      if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
+      if (h0 + G < p.n_h && hipEventRecord(side.buf_free[g & 1], st2) != hipSuccess)
+        return fail(MLA_ERR_HIP, "stored-dS buffer event failed");
+    }
   }
-  if ((s = check_launch("attention backward dQ")) != MLA_OK) return s;
   // dc_kv rows [key_lo, key_hi) = [dK_nope | dV] (fp16) . [W_UK | W_UV] rows; others 0
   float* gpart = reinterpret_cast<float*>(at(L.gpart));
   const int64_t gpart_bytes = std::max(gemm_splitk_bytes(p.Kn, p.d_c, 2 * nk),

@@ -27,6 +27,7 @@ struct Plan {
   bool fast;      // forward runs the MFMA path
   bool fast_bwd;  // backward runs the MFMA path
   bool ds_store;  // fast backward: dK/dV stores dS, dQ reads it (no recompute)
+  int ds_heads;   // stored dS: heads per group (a buffer holds one group)
   float scale;
   // latent rows the shard needs: [key_lo, key_hi), Kn of them
   int64_t key_lo, key_hi, Kn, Kpad;
@@ -58,8 +59,9 @@ struct BwdLayout {
   // fast path, packed calls: query-tile then key-tile order (int32
   // [ceil(S_loc / 256) + Kpad / 128])
   int64_t order;
-  // fast path with stored dS: fp16 [n_h][Kpad / 128][S_pad / 32] blocks of 8 KiB
-  // ([4 pairs of 32 keys][2 row halves][64 lanes] x 16 bytes, written by dK/dV)
+  // fast path with stored dS: one or (more than one group) two buffers, each
+  // fp16 [ds_heads][Kpad / 128][S_pad / 32] blocks of 8 KiB ([4 pairs of 32
+  // keys][2 row halves][64 lanes] x 16 bytes, written by dK/dV)
   int64_t dS;
   // fast path: dout scale {2^e, 2^-e} (fp32), then the per-block maxima of
   // |dout| it is chosen from (kScaleBlocks uint32), then per head the
@@ -68,8 +70,11 @@ struct BwdLayout {
   int64_t total;
 };
 
-// Largest stored-dS buffer the fast backward uses (bytes).
-constexpr int64_t kMaxStoredDsBytes = int64_t(32) << 30;
+// Stored dS of the fast backward: all heads in one buffer while that holds at
+// most kStoredDsOneBufferBytes; past that, head groups of at most
+// kStoredDsGroupBytes each through two buffers (bytes).
+constexpr int64_t kStoredDsOneBufferBytes = int64_t(16) << 30;
+constexpr int64_t kStoredDsGroupBytes = int64_t(1) << 30;
 // Workgroups of the fast backward's max|dout| reduction.
 constexpr int kScaleBlocks = 1024;
 
@@ -147,6 +152,7 @@ class KernelTimer {
 struct SideStream {
   hipStream_t st = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t buf_free[2] = {nullptr, nullptr};  // side-stream marks for double-buffered work
 };
 mla_status side_stream(SideStream* out);
 mla_status side_fork(const SideStream& s, hipStream_t main);

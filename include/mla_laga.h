@@ -131,12 +131,16 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 /* Fast backward, opt-in: the dK/dV kernel keeps dS = P (dP - D) (fp16) in the
  * workspace and dQ is computed from it, instead of recomputing the scores
  * and dP per query tile (the default). Faster, but the workspace then holds
- * one fp16 value per (local row, needed key, head): n_h * Kpad * S_pad * 2
- * bytes more (Kpad = needed keys rounded up to 256, S_pad = S_loc rounded up
- * to 64; 8.6 GB at n_h = 128, 16384 keys, 2048 rows), which grows with the
- * product of the shard's rows and keys. Ignored (dQ recomputes) when that
- * buffer would pass 32 GiB. Both forms give the same gradients up to fp16
- * rounding order. */
+ * dS, one fp16 value per (local row, needed key, head): B = Kpad * S_pad * 2
+ * bytes per head (Kpad = needed keys rounded up to 256, S_pad = S_loc
+ * rounded up to 64). While n_h * B <= 16 GiB that is n_h * B bytes more
+ * (8 GiB at n_h = 128, 16384 keys, 2048 rows). Past that, the heads run in
+ * groups of G through two alternating buffers, 2 * G * B bytes more, with
+ * G = ceil(n_h / ceil(n_h / floor(2^30 / B))) (groups of at most 1 GiB, as
+ * even as their count allows); dQ of one group then shares the GPU with
+ * dK/dV of the next, a little slower than the one-buffer form. When B alone
+ * passes 1 GiB (and n_h * B passes 16 GiB) the flag is ignored and dQ
+ * recomputes. Both forms give the same gradients up to fp16 rounding order. */
 #define MLA_FLAG_STORED_DS 4
 /* The flag value 2 is not used; any flag bit other than these two is
  * rejected with MLA_ERR_INVALID_ARG. */

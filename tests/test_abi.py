@@ -160,16 +160,31 @@ def test_workspace_linear_in_rows_and_heads():
     assert h2 - h1 == h3 - h2 and h2 > h1
 
 
-def test_default_backward_workspace_has_no_rows_times_keys_term():
+def stored_ds_bytes(n_h, keys, rows):
+    """Workspace the stored-dS backward adds: fp16 dS per (row padded to 64,
+    needed key padded to 256, head). All heads in one buffer while that is
+    at most 16 GiB; else head groups of at most 1 GiB each, as even as their
+    count allows, through two group buffers; 0 (dQ recomputes) when neither
+    fits."""
+    per_head = (keys + 255) // 256 * 256 * ((rows + 63) // 64 * 64) * 2
+    if n_h * per_head <= 16 << 30:
+        return n_h * per_head
+    if per_head > 1 << 30:
+        return 0
+    groups = -(-n_h // ((1 << 30) // per_head))
+    return 2 * -(-n_h // groups) * per_head
+
+
+def test_stored_ds_workspace():
     """The default backward recomputes the scores for dQ, so its workspace is
     a sum of per-row and per-key terms: the mixed second difference over
-    (rows, keys) vanishes. With MLA_FLAG_STORED_DS it holds dS (fp16,
-    n_h x Kpad x S_pad) as well, exactly the rows x keys term, unless that
-    buffer would pass 32 GiB."""
+    (rows, keys) vanishes. With MLA_FLAG_STORED_DS it holds dS (fp16) as
+    well: n_h x Kpad x S_pad while that fits 16 GiB, else two buffers of one
+    head group (at most 1 GiB) each."""
     base = workloads.config("h128_s16k_shard")
 
-    def ws(S_loc, S, flags=0):
-        d, cu = desc_for(base.with_(S=S, S_loc=S_loc, q_offset=S - S_loc))
+    def ws(S_loc, S, flags=0, n_h=128):
+        d, cu = desc_for(base.with_(S=S, S_loc=S_loc, q_offset=S - S_loc, n_h=n_h))
         d.flags = flags
         return hla.mla_laga_bwd_workspace_size(d, cu)
 
@@ -177,17 +192,20 @@ def test_default_backward_workspace_has_no_rows_times_keys_term():
         mixed = ws(2048, 16384, flags) - ws(1024, 16384, flags) - ws(2048, 8192, flags) \
             + ws(1024, 8192, flags)
         assert mixed == term, (flags, mixed)
-    d, cu = desc_for(base)
-    default = hla.mla_laga_bwd_workspace_size(d, cu)
-    d.flags = hla.MLA_FLAG_STORED_DS
-    # Kpad = 16384 keys, S_pad = 2048 rows
-    assert hla.mla_laga_bwd_workspace_size(d, cu) - default == 128 * 16384 * 2048 * 2
-    # a shape whose dS would need more than 32 GiB recomputes dQ by itself
-    big = base.with_(S=131072, S_loc=8192, q_offset=131072 - 8192)
-    d, cu = desc_for(big)
-    auto = hla.mla_laga_bwd_workspace_size(d, cu)
-    d.flags = hla.MLA_FLAG_STORED_DS
-    assert hla.mla_laga_bwd_workspace_size(d, cu) == auto
+    S = hla.MLA_FLAG_STORED_DS
+    B = 33024 * 2048 * 2    # 32769 keys padded to 33024, 2048 rows
+    cases = [
+        (128, 16384, 2048, 8 << 30),             # one buffer
+        (128, 32768, 2048, 16 << 30),            # one buffer, at its limit
+        (128, 32769, 2048, 2 * 7 * B),           # past it: 19 groups of at most 7 heads
+        (47, 24576, 8192, 2 * 2 * (384 << 20)),  # 24 groups of 2 (the last of 1)
+        (128, 65536, 8192, 2 << 30),             # one head per group, at its limit
+        (8, 131072, 8192, 16 << 30),             # 2 GiB heads, but one buffer holds them
+        (128, 131072, 8192, 0),                  # neither: dQ recomputes
+    ]
+    for n_h, keys, rows, want in cases:
+        assert stored_ds_bytes(n_h, keys, rows) == want, (n_h, keys, rows)
+        assert ws(rows, keys, S, n_h) - ws(rows, keys, 0, n_h) == want, (n_h, keys, rows)
 
 
 def test_unknown_flags_rejected():

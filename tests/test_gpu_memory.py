@@ -12,7 +12,8 @@ the library reports and the output tensors, exactly:
   backward: workspace + the five gradients, for the default backward
             (dQ recomputes the scores: no rows x keys term) and for the
             stored-dS form (its workspace holds one fp16 dS value per
-            local row, needed key and head more).
+            local row, needed key and head more, or, past 16 GiB of that,
+            two buffers of one head group each).
 """
 
 import pytest
@@ -21,6 +22,7 @@ import torch
 import head_latent_attention_kv_amd as hla
 import workloads
 from tests.gpu_helpers import announce, to_device
+from tests.test_abi import stored_ds_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +52,9 @@ CASES = [
     workloads.MLAConfig("mem_packed", n_h=8, S=3000, S_loc=1000, q_offset=2000, dtype="bf16",
                         backward=True, seq_lens=(700, 1, 1299, 1000), d_c=512, d_rope=64,
                         d_nope=128, d_v=128),
+    # 17.6 GiB of dS: the stored form runs 24 head groups through two buffers
+    workloads.MLAConfig("mem_ds_groups", n_h=47, S=24576, S_loc=8192, q_offset=16384,
+                        dtype="bf16", backward=True, d_c=64, d_rope=64, d_nope=128, d_v=128),
 ]
 
 
@@ -101,10 +106,10 @@ def test_allocator_peaks_equal_the_reported_sizes(cfg):
         del c, g
         torch.cuda.empty_cache()
     # the stored-dS workspace is the default one plus dS: one fp16 value per
-    # (row padded to 64, needed key padded to 256, head)
+    # (row padded to 64, needed key padded to 256, head) of all heads or of
+    # two head groups
     pairs, k_lo, k_hi = hla.mla_laga_count(hla.MLACall(*a, q_offset=cfg.q_offset,
                                                        cu_seqlens=cu).desc, cu)
-    Kpad = (k_hi - k_lo + 255) // 256 * 256
-    S_pad = (cfg.S_loc + 63) // 64 * 64
-    ds = cfg.n_h * Kpad * S_pad * 2
+    ds = stored_ds_bytes(cfg.n_h, k_hi - k_lo, cfg.S_loc)
+    assert ds > 0
     assert sizes[True] - sizes[False] == (ds + 255) // 256 * 256

@@ -387,6 +387,39 @@ def test_full_size_dq_paths_agree(name):
         check("dq", g["dq"][:, heads], rg[0][:, heads])
 
 
+def test_stored_ds_head_groups():
+    """Stored dS past its one-buffer limit (16 GiB): 47 heads of 8192 rows
+    over 24576 keys hold 384 MiB of dS each, 17.6 GiB in all, so the backward
+    runs them in 24 groups of 2 heads (the last of 1) through two alternating
+    1 GiB buffers: group g + 2 writes the buffer of group g once dQ of group
+    g has read it, and heads 0, 4 and 46 use the first slot of a buffer. dout
+    is zero outside those three heads, so every output is checked in full
+    against the oracle over them (the idle heads give exactly zero dq and
+    weight gradients)."""
+    cfg = workloads.MLAConfig("ds_groups", n_h=47, d_c=64, d_rope=64, d_nope=128, d_v=128,
+                              S=24576, S_loc=8192, q_offset=16384, dtype="bf16", backward=True,
+                              seed=11)
+    heads = [0, 4, 46]
+    idle = [h for h in range(cfg.n_h) if h not in heads]
+    announce(f"stored dS in 24 head groups, dout on heads {heads}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    dz = np.zeros_like(x["dout"])
+    dz[:, heads] = x["dout"][:, heads]
+    x = _set(x, "dout", dz)
+    g = run(cfg, x, backward=True, stored_ds=True)
+    assert g["fast"]
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, heads=heads)
+    check("dq", g["dq"][:, heads], rg[0][:, heads])
+    check("dc_kv", g["dc_kv"], rg[1])
+    check("dk_rope", g["dk_rope"], rg[2])
+    cols = np.concatenate([np.arange(h * 128, (h + 1) * 128) for h in heads])
+    cols_idle = np.concatenate([np.arange(h * 128, (h + 1) * 128) for h in idle])
+    check("dW_UK", g["dW_UK"][:, cols], rg[3][:, cols])
+    check("dW_UV", g["dW_UV"][:, cols], rg[4][:, cols])
+    assert not g["dq"][:, idle].any()
+    assert not g["dW_UK"][:, cols_idle].any() and not g["dW_UV"][:, cols_idle].any()
+
+
 def test_forward_backward_deterministic():
     cfg = workloads.MLAConfig("det", n_h=8, S=1500, S_loc=1000, q_offset=500, dtype="bf16",
                               backward=True, **DSV3)
