@@ -458,20 +458,34 @@ def test_backward_ordered_on_caller_streams():
             assert np.array_equal(t.cpu().numpy(), ref[k]), k
 
 
-def test_graph_replays_match_eager():
+GRAPH_CASES = {
+    "default": (workloads.MLAConfig("graph", n_h=8, S=1500, S_loc=1000, q_offset=500,
+                                    dtype="bf16", backward=True, **DSV3), False),
+    "stored_ds": (workloads.MLAConfig("graph", n_h=8, S=1500, S_loc=1000, q_offset=500,
+                                      dtype="bf16", backward=True, **DSV3), True),
+    # 24 head groups through two dS buffers (17.6 GiB of dS in one buffer)
+    "stored_ds_groups": (workloads.MLAConfig("graph_groups", n_h=47, d_c=64, d_rope=64, d_nope=128,
+                                             d_v=128, S=24576, S_loc=8192, q_offset=16384,
+                                             dtype="bf16", backward=True, seed=12), True),
+}
+
+
+@pytest.mark.parametrize("form", list(GRAPH_CASES))
+def test_graph_replays_match_eager(form):
     """Forward and backward captured into one HIP graph (through torch) and
     replayed: every replay, with eager work and a host synchronisation
     between replays, gives the eager call's bits. The library enqueues no
     memset or allocation, and the backward's side stream joins the capture
-    through its fork event and leaves it through its join event."""
-    cfg = workloads.MLAConfig("graph", n_h=8, S=1500, S_loc=1000, q_offset=500, dtype="bf16",
-                              backward=True, **DSV3)
-    announce("graph capture and replay")
+    through its fork event and leaves it through its join event; in the
+    head-grouped stored-dS form the waits for a free dS buffer are captured
+    as well."""
+    cfg, stored = GRAPH_CASES[form]
+    announce(f"graph capture and replay, {form}")
     x = workloads.make_inputs(cfg, with_dout=True)
-    ref = run(cfg, x, backward=True)
+    ref = run(cfg, x, backward=True, stored_ds=stored)
     dev = to_device(x, cfg)
     args = [dev[k] for k in ("q", "c_kv", "k_rope", "W_UK", "W_UV")]
-    call = hla.MLACall(*args, q_offset=cfg.q_offset, backward=True)
+    call = hla.MLACall(*args, q_offset=cfg.q_offset, backward=True, stored_ds=stored)
     out, lse = call.fwd(*args)
     grads = call.bwd(dev["dout"], *args, out, lse)   # eager: also creates the side stream
     torch.cuda.synchronize()
