@@ -266,7 +266,7 @@ constexpr int QB = 64;      // query rows per step of the key-outer kernel
 // B) and dout rows (swizzled 320-byte rows, read row-wise by B and transposed
 // by A), double-buffered per 64-row block and DMA-filled.
 constexpr int PW = 128;                        // keys per workgroup
-constexpr int PF = 4;                          // fragment reads in flight ahead of the products
+constexpr int PF = 3;                          // fragment reads in flight ahead of the products
 constexpr int kExCap = 64;                     // largest power-of-two factor on dS
 constexpr int PD_ROW = 320;                    // dout rows (128 elements), swizzled
 constexpr int P_QN = 0, P_DON = 28 * 1024, P_INFO = 48 * 1024, P_BYTES = 49 * 1024;
