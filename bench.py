@@ -775,8 +775,8 @@ def main():
 
     # The two backward forms. The default recomputes the scores and dP for
     # dQ; the stored-dS form (opt-in) keeps dS in the workspace, which grows
-    # with rows x keys up to 16 GiB (past that it runs head groups through
-    # two buffers of at most 1 GiB). Each form's backward is timed on its own call, and its
+    # with rows x keys up to 16 GiB (past that it runs head groups of at least
+    # 8 heads through two buffers of at most 1 GiB). Each form's backward is timed on its own call, and its
     # allocator peak (workspace and gradients of a fresh call) is measured.
     def bwd_peak(stored):
         # bytes requested from the caching allocator by a fresh call's

@@ -164,8 +164,8 @@ def make_desc(q: torch.Tensor, c_kv: torch.Tensor, k_rope: torch.Tensor, W_UV: t
     """Descriptor plus the host arrays it points at (cu_seqlens, ranges):
     keep those alive as long as the descriptor is used. stored_ds sets
     MLA_FLAG_STORED_DS (the backward keeps dS, all heads at once up to 16 GiB,
-    else in head groups of at most 1 GiB through two buffers, and dQ reads it
-    instead of recomputing the scores)."""
+    else in head groups of 8 or more heads and at most 1 GiB through two
+    buffers, and dQ reads it instead of recomputing the scores)."""
     S_loc, n_h, d_qk = q.shape
     S, d_c = c_kv.shape
     d_rope = k_rope.shape[1]

@@ -278,8 +278,8 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
   P.Kpad = align_up(P.Kn, kKeyTile);
   // stored dS: every head in one buffer while it fits kStoredDsOneBufferBytes
   // (dQ then runs once, beside the gradient GEMMs); else head groups of at
-  // most kStoredDsGroupBytes, as even as their count allows; a single head
-  // past that recomputes
+  // most kStoredDsGroupBytes, as even as their count allows, if a group holds
+  // at least kStoredDsMinGroupHeads heads; else dQ recomputes
   P.ds_store = false;
   P.ds_heads = 0;
   if (P.fast_bwd && (d->flags & MLA_FLAG_STORED_DS)) {
@@ -287,7 +287,7 @@ static mla_status make_plan(const mla_laga_desc* d, const int32_t* cu, Plan* p) 
     if (P.n_h * per_head <= kStoredDsOneBufferBytes) {
       P.ds_store = true;
       P.ds_heads = P.n_h;
-    } else if (per_head <= kStoredDsGroupBytes) {
+    } else if (per_head * kStoredDsMinGroupHeads <= kStoredDsGroupBytes) {
       const int64_t most = kStoredDsGroupBytes / per_head;   // heads per group, at most
       const int64_t groups = (P.n_h + most - 1) / most;
       P.ds_store = true;

@@ -72,9 +72,12 @@ struct BwdLayout {
 
 // Stored dS of the fast backward: all heads in one buffer while that holds at
 // most kStoredDsOneBufferBytes; past that, head groups of at most
-// kStoredDsGroupBytes each through two buffers (bytes).
+// kStoredDsGroupBytes each through two buffers (bytes), when a group holds at
+// least kStoredDsMinGroupHeads heads (fewer, and the groups' launches cost
+// more than recomputing dQ saves).
 constexpr int64_t kStoredDsOneBufferBytes = int64_t(16) << 30;
 constexpr int64_t kStoredDsGroupBytes = int64_t(1) << 30;
+constexpr int kStoredDsMinGroupHeads = 8;
 // Workgroups of the fast backward's max|dout| reduction.
 constexpr int kScaleBlocks = 1024;
 

@@ -138,9 +138,11 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  * groups of G through two alternating buffers, 2 * G * B bytes more, with
  * G = ceil(n_h / ceil(n_h / floor(2^30 / B))) (groups of at most 1 GiB, as
  * even as their count allows); dQ of one group then shares the GPU with
- * dK/dV of the next, a little slower than the one-buffer form. When B alone
- * passes 1 GiB (and n_h * B passes 16 GiB) the flag is ignored and dQ
- * recomputes. Both forms give the same gradients up to fp16 rounding order. */
+ * dK/dV of the next, a little slower than the one-buffer form. When 8 heads
+ * do not fit one group (8 * B > 1 GiB, with n_h * B past 16 GiB) the flag is
+ * ignored and dQ recomputes: so many small groups would cost more than
+ * recomputing. Both forms give the same gradients up to fp16 rounding
+ * order. */
 #define MLA_FLAG_STORED_DS 4
 /* The flag value 2 is not used; any flag bit other than these two is
  * rejected with MLA_ERR_INVALID_ARG. */

@@ -164,12 +164,12 @@ def stored_ds_bytes(n_h, keys, rows):
     """Workspace the stored-dS backward adds: fp16 dS per (row padded to 64,
     needed key padded to 256, head). All heads in one buffer while that is
     at most 16 GiB; else head groups of at most 1 GiB each, as even as their
-    count allows, through two group buffers; 0 (dQ recomputes) when neither
-    fits."""
+    count allows, through two group buffers, if 8 heads fit a group; else 0
+    (dQ recomputes)."""
     per_head = (keys + 255) // 256 * 256 * ((rows + 63) // 64 * 64) * 2
     if n_h * per_head <= 16 << 30:
         return n_h * per_head
-    if per_head > 1 << 30:
+    if 8 * per_head > 1 << 30:   # a group would hold fewer than 8 heads
         return 0
     groups = -(-n_h // ((1 << 30) // per_head))
     return 2 * -(-n_h // groups) * per_head
@@ -180,7 +180,7 @@ def test_stored_ds_workspace():
     a sum of per-row and per-key terms: the mixed second difference over
     (rows, keys) vanishes. With MLA_FLAG_STORED_DS it holds dS (fp16) as
     well: n_h x Kpad x S_pad while that fits 16 GiB, else two buffers of one
-    head group (at most 1 GiB) each."""
+    head group (at most 1 GiB, at least 8 heads) each."""
     base = workloads.config("h128_s16k_shard")
 
     def ws(S_loc, S, flags=0, n_h=128):
@@ -193,13 +193,14 @@ def test_stored_ds_workspace():
             + ws(1024, 8192, flags)
         assert mixed == term, (flags, mixed)
     S = hla.MLA_FLAG_STORED_DS
-    B = 33024 * 2048 * 2    # 32769 keys padded to 33024, 2048 rows
     cases = [
         (128, 16384, 2048, 8 << 30),             # one buffer
         (128, 32768, 2048, 16 << 30),            # one buffer, at its limit
-        (128, 32769, 2048, 2 * 7 * B),           # past it: 19 groups of at most 7 heads
-        (47, 24576, 8192, 2 * 2 * (384 << 20)),  # 24 groups of 2 (the last of 1)
-        (128, 65536, 8192, 2 << 30),             # one head per group, at its limit
+        (129, 32768, 2048, 2 * 8 * (128 << 20)),  # past it: 17 groups of 8 (the last of 1)
+        (130, 16384, 4096, 2 * 8 * (128 << 20)),  # 16 groups of 8 and one of 2
+        (256, 32768, 4096, 0),                   # four heads of 256 MiB per group: recomputes
+        (128, 32769, 2048, 0),                   # 7 heads of 129 MiB per group: recomputes
+        (47, 24576, 8192, 0),                    # 384 MiB heads, 17.6 GiB: recomputes
         (8, 131072, 8192, 16 << 30),             # 2 GiB heads, but one buffer holds them
         (128, 131072, 8192, 0),                  # neither: dQ recomputes
     ]

@@ -52,8 +52,8 @@ CASES = [
     workloads.MLAConfig("mem_packed", n_h=8, S=3000, S_loc=1000, q_offset=2000, dtype="bf16",
                         backward=True, seq_lens=(700, 1, 1299, 1000), d_c=512, d_rope=64,
                         d_nope=128, d_v=128),
-    # 17.6 GiB of dS: the stored form runs 24 head groups through two buffers
-    workloads.MLAConfig("mem_ds_groups", n_h=47, S=24576, S_loc=8192, q_offset=16384,
+    # 16.25 GiB of dS: the stored form runs 17 head groups through two buffers
+    workloads.MLAConfig("mem_ds_groups", n_h=130, S=16384, S_loc=4096, q_offset=12288,
                         dtype="bf16", backward=True, d_c=64, d_rope=64, d_nope=128, d_v=128),
 ]
 

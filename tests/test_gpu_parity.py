@@ -387,21 +387,26 @@ def test_full_size_dq_paths_agree(name):
         check("dq", g["dq"][:, heads], rg[0][:, heads])
 
 
-def test_stored_ds_head_groups():
-    """Stored dS past its one-buffer limit (16 GiB): 47 heads of 8192 rows
-    over 24576 keys hold 384 MiB of dS each, 17.6 GiB in all, so the backward
-    runs them in 24 groups of 2 heads (the last of 1) through two alternating
-    1 GiB buffers: group g + 2 writes the buffer of group g once dQ of group
-    g has read it, and heads 0, 4 and 46 use the first slot of a buffer. dout
-    is zero outside those three heads, so every output is checked in full
-    against the oracle over them (the idle heads give exactly zero dq and
-    weight gradients)."""
-    cfg = workloads.MLAConfig("ds_groups", n_h=47, d_c=64, d_rope=64, d_nope=128, d_v=128,
-                              S=24576, S_loc=8192, q_offset=16384, dtype="bf16", backward=True,
+# 130 heads x 128 MiB of dS: the stored-dS backward in 17 head groups
+GROUPED = workloads.MLAConfig("ds_groups", n_h=130, d_c=64, d_rope=64, d_nope=128, d_v=128,
+                              S=16384, S_loc=4096, q_offset=12288, dtype="bf16", backward=True,
                               seed=11)
-    heads = [0, 4, 46]
+
+
+def test_stored_ds_head_groups():
+    """Stored dS past its one-buffer limit (16 GiB): 130 heads of 4096 rows
+    over 16384 keys hold 128 MiB of dS each, 16.25 GiB in all, so the
+    backward runs them in 16 groups of 8 heads and one of 2 through two
+    alternating 1 GiB buffers: group g + 2 writes the buffer of group g once
+    dQ of group g has read it. Heads 0 and 16 use the first slot of buffer 0
+    in groups 0 and 2; head 129 is in the last group, which also uses buffer
+    0. dout is zero outside those three heads, so every output is checked in
+    full against the oracle over them (the idle heads give exactly zero dq
+    and weight gradients)."""
+    cfg = GROUPED
+    heads = [0, 16, 129]
     idle = [h for h in range(cfg.n_h) if h not in heads]
-    announce(f"stored dS in 24 head groups, dout on heads {heads}")
+    announce(f"stored dS in 17 head groups, dout on heads {heads}")
     x = workloads.make_inputs(cfg, with_dout=True)
     dz = np.zeros_like(x["dout"])
     dz[:, heads] = x["dout"][:, heads]
@@ -463,10 +468,11 @@ GRAPH_CASES = {
                                     dtype="bf16", backward=True, **DSV3), False),
     "stored_ds": (workloads.MLAConfig("graph", n_h=8, S=1500, S_loc=1000, q_offset=500,
                                       dtype="bf16", backward=True, **DSV3), True),
-    # 24 head groups through two dS buffers (17.6 GiB of dS in one buffer)
-    "stored_ds_groups": (workloads.MLAConfig("graph_groups", n_h=47, d_c=64, d_rope=64, d_nope=128,
-                                             d_v=128, S=24576, S_loc=8192, q_offset=16384,
-                                             dtype="bf16", backward=True, seed=12), True),
+    # 17 head groups through two dS buffers (16.25 GiB of dS in one buffer)
+    "stored_ds_groups": (workloads.MLAConfig("graph_groups", n_h=130, d_c=64, d_rope=64,
+                                             d_nope=128, d_v=128, S=16384, S_loc=4096,
+                                             q_offset=12288, dtype="bf16", backward=True,
+                                             seed=12), True),
 }
 
 
