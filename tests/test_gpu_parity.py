@@ -393,7 +393,8 @@ GROUPED = workloads.MLAConfig("ds_groups", n_h=130, d_c=64, d_rope=64, d_nope=12
                               seed=11)
 
 
-def test_stored_ds_head_groups():
+@pytest.mark.parametrize("packed", [False, True], ids=["causal", "packed"])
+def test_stored_ds_head_groups(packed):
     """Stored dS past its one-buffer limit (16 GiB): 130 heads of 4096 rows
     over 16384 keys hold 128 MiB of dS each, 16.25 GiB in all, so the
     backward runs them in 16 groups of 8 heads and one of 2 through two
@@ -402,8 +403,11 @@ def test_stored_ds_head_groups():
     in groups 0 and 2; head 129 is in the last group, which also uses buffer
     0. dout is zero outside those three heads, so every output is checked in
     full against the oracle over them (the idle heads give exactly zero dq
-    and weight gradients)."""
-    cfg = GROUPED
+    and weight gradients). Packed: a second sample starts at 16000, so the
+    dS blocks of its rows against earlier keys are never written and still
+    hold an earlier group's values, which dQ must mask."""
+    cfg = GROUPED.with_(seq_lens=(16000, 384)) if packed else GROUPED
+    cu = cfg.cu_seqlens()
     heads = [0, 16, 129]
     idle = [h for h in range(cfg.n_h) if h not in heads]
     announce(f"stored dS in 17 head groups, dout on heads {heads}")
@@ -411,9 +415,10 @@ def test_stored_ds_head_groups():
     dz = np.zeros_like(x["dout"])
     dz[:, heads] = x["dout"][:, heads]
     x = _set(x, "dout", dz)
-    g = run(cfg, x, backward=True, stored_ds=True)
+    g = run(cfg, x, cu, backward=True, stored_ds=True)
     assert g["fast"]
-    rg = oracle.mla_backward(x["dout"], *oracle_args(x), q_offset=cfg.q_offset, heads=heads)
+    rg = oracle.mla_backward(x["dout"], *oracle_args(x), cu_seqlens=cu, q_offset=cfg.q_offset,
+                             heads=heads)
     check("dq", g["dq"][:, heads], rg[0][:, heads])
     check("dc_kv", g["dc_kv"], rg[1])
     check("dk_rope", g["dk_rope"], rg[2])
