@@ -114,6 +114,29 @@ def test_debug_mode_checks_pass_and_change_nothing(cfg, cu, path, monkeypatch):
         assert np.array_equal(got[k], ref[k]), k
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["causal", "packed"])
+def test_debug_mode_stored_ds_head_groups(packed, monkeypatch):
+    """The head-grouped stored-dS backward (130 heads, 17 groups through two
+    dS buffers) in debug mode. The workspace starts as NaN: with packed
+    samples the dS blocks of the second sample's rows against earlier keys
+    are written by no group, so a dQ that let them through would leave NaN
+    in dq; the canary past the buffers checks the group offsets. Every
+    output equals the plain call's bits."""
+    from tests.test_gpu_parity import GROUPED
+    cfg = GROUPED.with_(seq_lens=(16000, 384)) if packed else GROUPED
+    cu = cfg.cu_seqlens()
+    announce(f"debug mode, stored dS in head groups, packed={packed}")
+    x = workloads.make_inputs(cfg, with_dout=True)
+    dev = to_device(x, cfg)
+    monkeypatch.delenv("MLA_LAGA_DEBUG", raising=False)
+    plain_call, ref = run_all(cfg, cu, dev, generic=False, stored_ds=True)
+    monkeypatch.setenv("MLA_LAGA_DEBUG", "1")
+    dbg_call, got = run_all(cfg, cu, dev, generic=False, stored_ds=True)
+    assert dbg_call.ws_bwd.numel() == plain_call.ws_bwd.numel() + 256
+    for k in ref:
+        assert np.array_equal(got[k], ref[k]), k
+
+
 def test_debug_mode_reports_nan_inputs(monkeypatch):
     cfg, cu = small("nan_input", 300, 200, 100, cu=[0, 50, 180, 300])
     announce("debug mode NaN input")
