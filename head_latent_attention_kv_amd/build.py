@@ -52,6 +52,10 @@ DEVICE_FLAGS = {
     # VGPRs; the AGPR form put the score chain in AGPRs next to the
     # accumulators and spilled to scratch
     "decode.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+    # forward attention: the backend's ILP-first scheduling strategy orders
+    # the two score chains' fragment reads and the softmax work better
+    # around the products (about 1.5% on the attention kernel)
+    "fast_fwd.hip": ["-Xarch_device", "-mllvm=-amdgpu-sched-strategy=max-ilp"],
 }
 
 
