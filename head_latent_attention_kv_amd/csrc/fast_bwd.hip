@@ -1058,20 +1058,34 @@ attn_bwd_dq_ds_kernel(const uint32_t* __restrict__ info, const _Float16* __restr
 }
 
 // dk_rope[key_lo + t][r] = sc[1] sum_h dKr[h][t][r] for t < Kn (sc[1] = 2^-e
-// undoes the dout scale); other rows 0.
+// undoes the dout scale); other rows 0. A thread owns four consecutive r
+// (16-byte loads and store) and keeps eight heads' loads in flight; the sum
+// still runs over h in order, so the result does not depend on the grid.
 __global__ void __launch_bounds__(256)
 reduce_rope_kernel(const float* __restrict__ dKr, const float* __restrict__ sc,
                    float* __restrict__ dk_rope, int n_h, int64_t S, int64_t key_lo, int64_t Kn,
                    int64_t Kpad) {
   const float inv = sc[1];
-  const int64_t n = S * 64;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
+  const int64_t n4 = S * 16;          // 16-byte pieces of dk_rope
+  const int64_t hstride = Kpad * 16;  // pieces per head of dKr
+  const f32x4* src = reinterpret_cast<const f32x4*>(dKr);
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n4;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t j = e >> 6, r = e & 63, t = j - key_lo;
-    float acc = 0.f;
-    if (t >= 0 && t < Kn)
-      for (int h = 0; h < n_h; ++h) acc += dKr[(static_cast<int64_t>(h) * Kpad + t) * 64 + r];
-    dk_rope[e] = acc * inv;
+    const int64_t j = e >> 4, t = j - key_lo;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (t >= 0 && t < Kn) {
+      const f32x4* pt = src + t * 16 + (e & 15);
+      int h = 0;
+      for (; h + 8 <= n_h; h += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pt[(h + u) * hstride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      for (; h < n_h; ++h) acc += pt[h * hstride];
+    }
+    reinterpret_cast<f32x4*>(dk_rope)[e] = acc * inv;
   }
 }
 
@@ -1278,7 +1292,7 @@ mla_status fast_bwd(const Plan& p, const void* dout, const void* q, const void* 
   // on the side stream
   {
     KernelTimer kt("reduce_rope", st);
-    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 64)), dim3(256), 0, st, dKr,
+    hipLaunchKernelGGL(reduce_rope_kernel, dim3(grid_for(p.S * 16)), dim3(256), 0, st, dKr,
                        dsc, dk_rope, p.n_h, p.S, p.key_lo, p.Kn, p.Kpad);
   }
   if ((s = check_launch("rope-key gradient reduce")) != MLA_OK) return s;
